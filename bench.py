@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-rank state-sharding engine on one MI355X.
+
+One step is one pass of the whole hot path over the 7B Llama-style model's
+rank-0 FSDP2 shard (N = 8 logical ranks, grad_acc = 4), all inputs resident
+in HBM before timing starts:
+
+  1. fs_pack    x33 groups  all-gather copy-in of every group (all N shards)
+  2. fs_unpack  x33 groups  all-gather copy-out into per-parameter tensors
+  3. fs_reduce_shard        32 bf16 gradient slices -> fp32 shard (842,301,440)
+  4. fs_adamw_step          fp32 master/m/v update + bf16 parameter copy
+
+The layout plans are built and uploaded once, before timing (a plan is made
+once per group).  Throughput is algorithmic bytes (what the method must read
+and write) per second; per-kernel durations come from HIP events recorded on
+the stream the kernels run on.  The CPU baseline is the plain C oracle on a
+bounded sample of the same workload, single-threaded.
+
+Prints one JSON line.  `--gpus N` with N > 1 is refused: this engine runs all
+logical ranks on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
+KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_state_amd", "csrc", "fs_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard_step.json")
+
+WORKLOADS = {
+    # name: (n_blocks, d, f, kv, vocab, world, grad_acc)
+    "7b": (32, 4096, 11008, None, 32000, 8, 4),
+    "70b": (80, 8192, 28672, 1024, 32000, 8, 2),
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def setup(workload: str, seed: int = 4):
+    import torch
+
+    import fsdp_sharded_state_amd as fs
+    import synth
+
+    n_blocks, d, f, kv, vocab, world, grad_acc = WORKLOADS[workload]
+    groups = synth.llama_model_groups(n_blocks, d, f, vocab=vocab, kv=kv)
+    plans = [fs.fs_plan(g, "bf16", world, False, "fsdp2", grad_acc).upload() for g in groups]
+    S = sum(p.shard_numel for p in plans)
+    P = sum(p.total_numel for p in plans)
+    log(f"workload {workload}: {len(groups)} groups, P={P}, shard S={S}, N={world}, A={grad_acc}")
+
+    t0 = time.time()
+    params, gathered, outs = [], [], []
+    off = 0
+    for g, p in zip(groups, plans):
+        ps = []
+        for s in g:
+            n = math.prod(s)
+            ps.append(synth.normal_bf16(seed, synth.STREAM_PARAMS, n, 0.02, device="cuda", start=off).view(*s))
+            off += n
+        params.append(ps)
+        gathered.append(torch.empty(p.gathered_numel, dtype=torch.bfloat16, device="cuda"))
+        outs.append([torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in g])
+    slices = [synth.normal_bf16(seed, synth.stream_grad(j, k, world), S, 1e-3, device="cuda")
+              for j in range(grad_acc) for k in range(world)]
+    master = synth.normal_f32(seed, synth.STREAM_MASTER, S, 0.02, device="cuda")
+    exp_avg = torch.zeros(S, dtype=torch.float32, device="cuda")
+    exp_avg_sq = torch.zeros(S, dtype=torch.float32, device="cuda")
+    grad32 = torch.empty(S, dtype=torch.float32, device="cuda")
+    p16 = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"inputs generated on the GPU in {time.time() - t0:.1f}s; "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+    return dict(fs=fs, plans=plans, params=params, gathered=gathered, outs=outs, slices=slices,
+                master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, grad32=grad32, p16=p16,
+                S=S, P=P, world=world, grad_acc=grad_acc, groups=len(groups))
+
+
+def algorithmic_bytes(W) -> dict:
+    """Bytes each kernel must move (pads written by pack count; pads are never read)."""
+    P, S, N, A = W["P"], W["S"], W["world"], W["grad_acc"]
+    gathered = sum(p.gathered_numel for p in W["plans"])
+    return {
+        "pack": 2 * P + 2 * gathered,      # read every parameter, write every gathered element
+        "unpack": 2 * P + 2 * P,           # read every parameter element of the gathered buffers, write it out
+        "reduce": (2 * N * A + 4) * S,     # read N*A bf16 slices, write fp32
+        "adamw": 30 * S,                   # read g, theta, m, v (fp32); write theta, m, v (fp32) + bf16 param
+    }
+
+
+def run_step(W, step_t, ev=None):
+    fs = W["fs"]
+    if ev:
+        ev[0].record()
+    for p, ps, g in zip(W["plans"], W["params"], W["gathered"]):
+        fs.fs_pack(p, ps, g)
+    if ev:
+        ev[1].record()
+    for p, g, o in zip(W["plans"], W["gathered"], W["outs"]):
+        fs.fs_unpack(p, g, o)
+    if ev:
+        ev[2].record()
+    fs.fs_reduce_shard(W["slices"], W["grad32"], W["world"], W["grad_acc"])
+    if ev:
+        ev[3].record()
+    fs.fs_adamw_step(W["master"], W["exp_avg"], W["exp_avg_sq"], W["grad32"], W["p16"],
+                     lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=step_t)
+    if ev:
+        ev[4].record()
+
+
+def copy_ceiling(fs, nbytes=1 << 32, reps=5):
+    """Achieved GB/s of a plain dwordx4 copy (read + write) of nbytes."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    fs.fs_copy_bytes(b, a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        s.record()
+        fs.fs_copy_bytes(b, a)
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    del a, b
+    torch.cuda.empty_cache()
+    t = sorted(times)[len(times) // 2]
+    return 2 * nbytes / (t * 1e-3) / 1e9
+
+
+def cpu_baseline(workload: str, target_s: float = 12.0, seed: int = 4) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    reduce + AdamW over the first n_s shard elements and pack + unpack of one
+    transformer block group, single-threaded, timed with a monotonic clock."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    torch.set_num_threads(min(16, os.cpu_count() or 1))
+    n_blocks, d, f, kv, vocab, world, grad_acc = WORKLOADS[workload]
+    n_s = 1 << 22
+    # same generator and streams as the GPU run, evaluated on the GPU for speed
+    sl = [synth.to_numpy_bits(synth.normal_bf16(seed, synth.stream_grad(j, k, world), n_s, 1e-3, device="cuda"))
+          for j in range(grad_acc) for k in range(world)]
+    th = synth.normal_f32(seed, synth.STREAM_MASTER, n_s, 0.02, device="cuda").cpu().numpy()
+    z = np.zeros(n_s, np.float32)
+    block = synth.llama_block_shapes(d, f, kv)
+    L = oracle.fsdp2_layout(block, 2, world)
+    nb = int(L.numel.sum())
+    prm = [np.frombuffer(np.random.default_rng(k).bytes(2 * int(n)), np.uint16) for k, n in enumerate(L.numel)]
+    hp = oracle.AdamWHparams(step=1)
+
+    total_bytes, total_t, reps = 0, 0.0, 0
+    while total_t < target_s and reps < 20:
+        t0 = time.perf_counter()
+        g = oracle.reduce_shard(sl, world, grad_acc)
+        oracle.adamw_step(th, z, z, g, hp)
+        gath = oracle.pack(L, prm)
+        oracle.unpack(L, gath)
+        total_t += time.perf_counter() - t0
+        total_bytes += (2 * world * grad_acc + 4) * n_s + 30 * n_s + (2 * nb + 2 * L.gathered_numel) + 4 * nb
+        reps += 1
+    return {
+        "value": total_bytes / total_t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{reps} passes of: reduce ({world * grad_acc} bf16 slices) + AdamW over {n_s} of the "
+                   f"rank-0 shard's elements, pack + unpack of one block group ({nb} params); "
+                   f"{total_t:.1f}s of single-threaded CPU work"),
+    }
+
+
+def traffic_for(kernel: str, launch_bytes_alg: float):
+    """HBM bytes per launch from the committed PMC summary, or None when the
+    kernel source changed since the counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this engine runs all N logical ranks on one GPU; "
+                                   "--gpus above 1 is not supported", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    W = setup(args.workload)
+    fs = W["fs"]
+    alg = algorithmic_bytes(W)
+    step_bytes = sum(alg.values())
+
+    t = 1
+    for _ in range(args.warmup):
+        run_step(W, t)
+        t += 1
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        run_step(W, t, evs[k])
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    phases = ["pack", "unpack", "reduce", "adamw"]
+    ms = {ph: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, ph in enumerate(phases)}
+    kern = {ph: {"ms": round(ms[ph], 4), "GB": round(alg[ph] / 1e9, 3),
+                 "GBps": round(alg[ph] / (ms[ph] * 1e-3) / 1e9, 1),
+                 "frac_hbm_peak": round(alg[ph] / (ms[ph] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            for ph in phases}
+    ra_ms = ms["reduce"] + ms["adamw"]
+    ra_gbps = (alg["reduce"] + alg["adamw"]) / (ra_ms * 1e-3) / 1e9
+    kern["reduce_adamw"] = {"ms": round(ra_ms, 4), "GBps": round(ra_gbps, 1),
+                            "frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4)}
+    ceiling = copy_ceiling(fs)
+
+    red_gbps = alg["reduce"] / (ms["reduce"] * 1e-3) / 1e9
+    traffic = traffic_for("reduce", alg["reduce"])
+    out = {
+        "metric": "sharded AdamW+reduce step GB/s and % HBM peak; pack/unpack GB/s (7B, N=8)",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "dtype_detail": {"pack/unpack": "bf16 bit copy", "reduce": "fp32 accumulate",
+                         "adamw": "f64 math on fp32 state, bf16 copy"},
+        "data": "synthetic",
+        "config": {"workload": ("7B Llama-style model, rank 0's FSDP2 1/8 shard: pack + unpack of all 33 groups, "
+                                "reduce of 4x8 bf16 gradient slices, AdamW" if args.workload == "7b" else
+                                "70B Llama-style model, rank 0's FSDP2 1/8 shard: pack + unpack of all 81 groups, "
+                                "reduce of 2x8 bf16 gradient slices, AdamW"),
+                   "params": W["P"], "shard_numel": W["S"], "world": W["world"], "grad_acc": W["grad_acc"],
+                   "groups": W["groups"], "step_bytes": step_bytes},
+        "kernels": kern,
+        "reduce_adamw_GBps": round(ra_gbps, 1),
+        "reduce_adamw_frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4),
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "roofline": {"bound": "hbm", "kernel": "reduce_kernel", "achieved": round(red_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(red_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": alg["reduce"]},
+        "cpu_baseline": None,
+    }
+    del W
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

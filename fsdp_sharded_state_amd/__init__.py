@@ -1,0 +1,276 @@
+"""Python binding of the per-rank state-sharding engine (libfsstate.so).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/fs.h.  torch supplies device memory and
+streams.  There is no fallback: if the library is missing, importing its
+functions raises.
+
+    plan = fs_plan(shapes, "bf16", world=8, mode="fsdp2")
+    plan.upload()                         # segment/tile tables -> device
+    fs_pack(plan, params, gathered)       # all-gather copy-in (all N ranks)
+    fs_unpack(plan, gathered, outs)       # all-gather copy-out
+    fs_reduce_shard(slices, grad32, world=8, grad_acc=4)
+    fs_adamw_step(master, m, v, grad32, p16, lr=1e-3, step=1)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsstate.so")
+
+FS_OK = 0
+FS_E_INVAL, FS_E_UNSUPPORTED, FS_E_DTYPE, FS_E_OVERFLOW, FS_E_ALIGN, FS_E_HIP, FS_E_NOMEM = range(-1, -8, -1)
+_CODES = {0: "FS_OK", -1: "FS_E_INVAL", -2: "FS_E_UNSUPPORTED", -3: "FS_E_DTYPE",
+          -4: "FS_E_OVERFLOW", -5: "FS_E_ALIGN", -6: "FS_E_HIP", -7: "FS_E_NOMEM"}
+FS_BF16, FS_FP32 = 0, 1
+FS_FSDP1_FLAT, FS_FSDP2_PER_PARAM = 1, 2
+
+
+class FsError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("dtype", ctypes.c_int32), ("world", ctypes.c_int32),
+                ("use_orig_params", ctypes.c_int32), ("grad_acc", ctypes.c_int32),
+                ("n_params", ctypes.c_int32), ("elem_bytes", ctypes.c_int32), ("bopt", ctypes.c_int32),
+                ("total_numel", ctypes.c_int64), ("flat_numel", ctypes.c_int64),
+                ("shard_numel", ctypes.c_int64), ("gathered_numel", ctypes.c_int64),
+                ("align_pad", ctypes.c_int64), ("tail_pad", ctypes.c_int64),
+                ("n_segments", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("ledger_ideal_bytes", ctypes.c_double), ("ledger_padded_bytes", ctypes.c_double)]
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("dst_off", ctypes.c_int64), ("src_off", ctypes.c_int64), ("len", ctypes.c_int64),
+                ("param", ctypes.c_int32), ("rank", ctypes.c_int32)]
+
+
+class ParamLayout(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("start", ctypes.c_int64), ("chunk_rows", ctypes.c_int64),
+                ("row", ctypes.c_int64), ("pre", ctypes.c_int64)]
+
+
+class AdamWHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("step", ctypes.c_int64)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfsstate.so (built by `python -m fsdp_sharded_state_amd.build`)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m fsdp_sharded_state_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    L.fs_plan.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(vp)]
+    L.fs_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    L.fs_plan_param.argtypes = [vp, i32, ctypes.POINTER(ParamLayout)]
+    L.fs_plan_segments.argtypes = [vp, vp, i64, ctypes.POINTER(i64)]
+    L.fs_plan_upload.argtypes = [vp, vp, sz, vp]
+    L.fs_plan_destroy.argtypes = [vp]
+    L.fs_plan_destroy.restype = None
+    L.fs_pack.argtypes = [vp, vp, vp, i32, vp]
+    L.fs_unpack.argtypes = [vp, vp, vp, vp]
+    L.fs_reduce_shard.argtypes = [i64, i32, i32, vp, vp, vp]
+    L.fs_adamw_step.argtypes = [i64, vp, vp, vp, vp, i32, vp, ctypes.POINTER(AdamWHparams), vp]
+    L.fs_copy_bytes.argtypes = [vp, vp, i64, vp]
+    L.fs_last_error.argtypes = []
+    L.fs_last_error.restype = ctypes.c_char_p
+    for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
+                 "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_copy_bytes"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != FS_OK:
+        raise FsError(rc, lib().fs_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in ("bf16", torch.bfloat16, FS_BF16):
+        return FS_BF16
+    if dtype in ("fp32", torch.float32, FS_FP32):
+        return FS_FP32
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def _mode_code(mode) -> int:
+    if mode in ("fsdp1", FS_FSDP1_FLAT):
+        return FS_FSDP1_FLAT
+    if mode in ("fsdp2", FS_FSDP2_PER_PARAM):
+        return FS_FSDP2_PER_PARAM
+    raise ValueError(f"unsupported mode {mode!r}")
+
+
+def _dev_ptr(t: torch.Tensor, what: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+class Plan:
+    """An uploaded-or-not layout plan (wraps fs_plan_t)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        self._destroy = lib().fs_plan_destroy   # kept for interpreter shutdown
+        info = PlanInfo()
+        _check(lib().fs_plan_info(self._h, ctypes.byref(info)))
+        self.info = info
+        self.workspace: Optional[torch.Tensor] = None
+        self._ptr_cache = {}
+
+    def close(self):
+        """Release the plan's host memory (also done on garbage collection)."""
+        h = self.__dict__.pop("_h", None)
+        if h is not None and h.value:
+            self._destroy(h)
+
+    def __del__(self):
+        self.close()
+
+    # summary
+    def __getattr__(self, name):
+        info = self.__dict__.get("info")
+        if info is not None and name in dict(PlanInfo._fields_):
+            return getattr(info, name)
+        raise AttributeError(name)
+
+    def param(self, i: int) -> ParamLayout:
+        out = ParamLayout()
+        _check(lib().fs_plan_param(self._h, i, ctypes.byref(out)))
+        return out
+
+    def segments(self) -> List[tuple]:
+        n = ctypes.c_int64()
+        _check(lib().fs_plan_segments(self._h, None, 0, ctypes.byref(n)))
+        arr = (Segment * max(1, n.value))()
+        _check(lib().fs_plan_segments(self._h, arr, n.value, ctypes.byref(n)))
+        return [(s.dst_off, s.src_off, s.len, s.param, s.rank) for s in arr[:n.value]]
+
+    def upload(self, device="cuda", stream=None) -> "Plan":
+        ws = torch.empty(max(16, self.info.workspace_bytes), dtype=torch.uint8, device=device)
+        _check(lib().fs_plan_upload(self._h, ws.data_ptr(), ws.numel(), _stream(stream)))
+        self.workspace = ws
+        return self
+
+    def ptr_table(self, tensors: Sequence[torch.Tensor], what: str) -> torch.Tensor:
+        """Device array of the tensors' data pointers (cached per pointer set)."""
+        if len(tensors) != self.info.n_params:
+            raise ValueError(f"{what}: expected {self.info.n_params} tensors, got {len(tensors)}")
+        esz = self.info.elem_bytes
+        ptrs = []
+        for i, t in enumerate(tensors):
+            if t.element_size() != esz:
+                raise ValueError(f"{what}[{i}]: element size {t.element_size()} != plan's {esz}")
+            if t.numel() != self.param(i).numel:
+                raise ValueError(f"{what}[{i}]: numel {t.numel()} != {self.param(i).numel}")
+            ptrs.append(_dev_ptr(t, f"{what}[{i}]") if t.numel() else 0)
+        key = (tuple(ptrs), str(tensors[0].device) if tensors else "")
+        tab = self._ptr_cache.get(key)
+        if tab is None:
+            dev = tensors[0].device if tensors else torch.device("cuda")
+            tab = torch.tensor(ptrs or [0], dtype=torch.int64, device=dev)
+            self._ptr_cache = {key: tab}
+        return tab
+
+
+def fs_plan(shapes: Sequence[Sequence[int]], dtype="bf16", world: int = 1, use_orig_params: bool = False,
+            mode="fsdp1", grad_acc: int = 1) -> Plan:
+    """Plan one FSDP group's shard layout (fs_plan)."""
+    n = len(shapes)
+    ndim = (ctypes.c_int32 * max(1, n))(*[len(s) for s in shapes])
+    flat = [int(d) for s in shapes for d in s]
+    dims = (ctypes.c_int64 * max(1, len(flat)))(*flat)
+    h = ctypes.c_void_p()
+    _check(lib().fs_plan(n, ndim, dims, _dtype_code(dtype), int(world), int(bool(use_orig_params)),
+                         _mode_code(mode), int(grad_acc), ctypes.byref(h)))
+    return Plan(h.value)
+
+
+def fs_pack(plan: Plan, params: Sequence[torch.Tensor], out: torch.Tensor, rank: int = -1, stream=None):
+    """All-gather copy-in: params -> out (whole gathered buffer, or rank's shard)."""
+    want = plan.info.gathered_numel if rank < 0 else plan.info.shard_numel
+    if out.numel() != want or out.element_size() != plan.info.elem_bytes:
+        raise ValueError(f"fs_pack: out must hold {want} elements of {plan.info.elem_bytes} bytes")
+    tab = plan.ptr_table(params, "params")
+    _check(lib().fs_pack(plan._h, tab.data_ptr(), _dev_ptr(out, "out") if want else 0, int(rank), _stream(stream)))
+
+
+def fs_unpack(plan: Plan, gathered: torch.Tensor, params: Sequence[torch.Tensor], stream=None):
+    """All-gather copy-out: gathered -> params."""
+    if gathered.numel() != plan.info.gathered_numel or gathered.element_size() != plan.info.elem_bytes:
+        raise ValueError("fs_unpack: gathered has the wrong size or element size")
+    tab = plan.ptr_table(params, "params")
+    _check(lib().fs_unpack(plan._h, _dev_ptr(gathered, "gathered") if gathered.numel() else 0,
+                           tab.data_ptr(), _stream(stream)))
+
+
+def fs_reduce_shard(slices: Sequence[torch.Tensor], out: torch.Tensor, world: int, grad_acc: int = 1, stream=None):
+    """Average slices[j*world + k] (bf16, n each) into out (fp32, n)."""
+    n = out.numel()
+    if out.dtype != torch.float32:
+        raise ValueError("fs_reduce_shard: out must be float32")
+    if len(slices) != world * grad_acc:
+        raise ValueError(f"fs_reduce_shard: need world*grad_acc = {world * grad_acc} slices")
+    ptrs = []
+    for k, s in enumerate(slices):
+        if s.dtype != torch.bfloat16 or s.numel() != n:
+            raise ValueError(f"fs_reduce_shard: slice {k} must be bf16 with {n} elements")
+        ptrs.append(_dev_ptr(s, f"slices[{k}]") if n else 0)
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    _check(lib().fs_reduce_shard(n, int(world), int(grad_acc), arr, _dev_ptr(out, "out") if n else 0,
+                                 _stream(stream)))
+
+
+def fs_adamw_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, grad: torch.Tensor,
+                  param_bf16: Optional[torch.Tensor] = None, *, lr: float = 1e-3, beta1: float = 0.9,
+                  beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.01, step: int = 1,
+                  stream=None):
+    """One AdamW step over the fp32 shard (in place), writing the bf16 copy."""
+    n = master.numel()
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if t.dtype != torch.float32 or t.numel() != n:
+            raise ValueError(f"fs_adamw_step: {name} must be float32 with {n} elements")
+    if grad.numel() != n or grad.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("fs_adamw_step: grad must be float32 or bfloat16 with n elements")
+    if param_bf16 is not None and (param_bf16.dtype != torch.bfloat16 or param_bf16.numel() != n):
+        raise ValueError("fs_adamw_step: param_bf16 must be bfloat16 with n elements")
+    hp = AdamWHparams(lr, beta1, beta2, eps, weight_decay, 0, int(step))
+    ptr = (lambda t, w: _dev_ptr(t, w) if n else 0)
+    _check(lib().fs_adamw_step(n, ptr(master, "master"), ptr(exp_avg, "exp_avg"), ptr(exp_avg_sq, "exp_avg_sq"),
+                               ptr(grad, "grad"), FS_BF16 if grad.dtype == torch.bfloat16 else FS_FP32,
+                               ptr(param_bf16, "param_bf16") if param_bf16 is not None else None,
+                               ctypes.byref(hp), _stream(stream)))
+
+
+def fs_copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None):
+    """Plain streaming copy (measurement aid): src -> dst, same byte size."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("fs_copy_bytes: size mismatch")
+    _check(lib().fs_copy_bytes(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), nb, _stream(stream)))

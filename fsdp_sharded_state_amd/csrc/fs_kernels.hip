@@ -1,0 +1,768 @@
+// fs_kernels.hip -- gfx950 (CDNA4) kernels and the C-ABI launchers.
+//
+// All four kernels are HBM-bandwidth-bound streams with no reuse: pack and
+// unpack move bytes, the reduce does one fp32 add per input element, AdamW a
+// few dozen flops per 30 bytes.  None is a contraction, so none uses MFMA;
+// the design goals are 16-byte (dwordx4) accesses on every lane, enough loads
+// in flight per wave to cover HBM latency, and no divergent control flow at
+// layout boundaries.
+//
+// Sources (page title, section):
+//   pack / unpack: "FSDP1 vs FSDP2", section 03 (FlatParameter padding and
+//     chunk(N); FSDP2 dim-0 chunks concatenated into one all-gather input).
+//   reduce: "Data parallelism, ZeRO and FSDP", sections 2.1 (sum, then divide
+//     by N), 1 and 9.2 (fp32 accumulation on the own shard), 5 (1/grad_acc in
+//     the loss).
+//   AdamW: "Data parallelism, ZeRO and FSDP", sections 1 (moments, then the
+//     parameter) and 9.1 (update the fp32 shard, then cast it to bf16).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "fs_plan_impl.h"
+
+using fsi::BufInfo;
+using fsi::Segment;
+using fsi::Tile;
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = fsi::kThreads;
+
+__host__ __device__ __forceinline__ int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+__host__ __device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// ---------------------------------------------------------------- memory --
+
+__device__ __forceinline__ u32x4 ld16(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void st16(char *p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
+// Bytes [sh, sh+16) of the 32-byte window lo:hi (sh in 0..15): a two-level
+// word select (by 2 words, then by 1) followed by a byte align.  Written with
+// scalars only, so the words stay in registers.
+__device__ __forceinline__ u32x4 funnel16(u32x4 lo, u32x4 hi, uint32_t sh) {
+    const uint32_t q = sh >> 2, r = sh & 3;
+    const bool s2 = (q & 2) != 0, s1 = (q & 1) != 0;
+    const uint32_t b0 = s2 ? lo.z : lo.x, b1 = s2 ? lo.w : lo.y, b2 = s2 ? hi.x : lo.z;
+    const uint32_t b3 = s2 ? hi.y : lo.w, b4 = s2 ? hi.z : hi.x, b5 = s2 ? hi.w : hi.y;
+    const uint32_t a0 = s1 ? b1 : b0, a1 = s1 ? b2 : b1, a2 = s1 ? b3 : b2;
+    const uint32_t a3 = s1 ? b4 : b3, a4 = s1 ? b5 : b4;
+    u32x4 o;
+    o.x = __builtin_amdgcn_alignbyte(a1, a0, r);
+    o.y = __builtin_amdgcn_alignbyte(a2, a1, r);
+    o.z = __builtin_amdgcn_alignbyte(a3, a2, r);
+    o.w = __builtin_amdgcn_alignbyte(a4, a3, r);
+    return o;
+}
+
+// Select mask of the elements [e_lo, e_hi) of a 16-byte block (W-byte elements).
+template <int W>
+__device__ __forceinline__ u32x4 elem_mask(int e_lo, int e_hi) {
+    uint32_t m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (W == 4) {
+            m[i] = (i >= e_lo && i < e_hi) ? 0xFFFFFFFFu : 0u;
+        } else {
+            uint32_t lo = (2 * i >= e_lo && 2 * i < e_hi) ? 0x0000FFFFu : 0u;
+            uint32_t hi = (2 * i + 1 >= e_lo && 2 * i + 1 < e_hi) ? 0xFFFF0000u : 0u;
+            m[i] = lo | hi;
+        }
+    }
+    return u32x4{m[0], m[1], m[2], m[3]};
+}
+
+template <int W>
+__device__ __forceinline__ void store_elems(char *dst, u32x4 v, int e_lo, int e_hi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 16 / W; ++e) {
+        if (e >= e_lo && e < e_hi) {
+            if (W == 4)
+                *reinterpret_cast<uint32_t *>(dst + 4 * e) = w[e];
+            else
+                *reinterpret_cast<uint16_t *>(dst + 2 * e) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+// --------------------------------------------------------- pack / unpack --
+//
+// One workgroup per tile.  The tile's segments are staged in LDS; every lane
+// builds 16-byte destination blocks.  For a block, each overlapping segment
+// contributes its elements through two aligned 16-byte loads and a byte
+// funnel shift (so a source at any element offset is read with aligned
+// dwordx4 loads), merged under an element mask; elements no segment covers
+// stay zero (pads).  Tiles covered by a single segment -- nearly all of them
+// for large parameters -- take a uniform fast path: straight dwordx4 copies,
+// or, when source and destination differ in 16-byte phase, one aligned load
+// per lane with the next block taken from the neighbouring lane by a
+// wavefront shuffle.
+//
+// Every load is a naturally aligned 16-byte block that overlaps bytes of the
+// source run it serves; such a block never crosses a page, so only mapped
+// memory is read.  Stores are full 16-byte blocks inside the destination, or
+// per-element stores at its edges.
+
+struct TileLds {
+    int64_t vx[fsi::kTileSegs];
+    int64_t end[fsi::kTileSegs];
+    int64_t src[fsi::kTileSegs];
+    int32_t buf[fsi::kTileSegs];
+};
+
+__device__ __forceinline__ int find_first_ending_after(const TileLds &L, int nseg, int64_t x) {
+    int lo = 0, hi = nseg;
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (L.end[mid] <= x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// Source pointer of a segment: pack reads parameter `buf`, unpack reads the
+// gathered buffer.
+struct PackSrc {
+    const void *const *params;
+    __device__ __forceinline__ const char *operator()(int buf) const {
+        return reinterpret_cast<const char *>(params[buf]);
+    }
+};
+struct UnpackSrc {
+    const char *gathered;
+    __device__ __forceinline__ const char *operator()(int) const { return gathered; }
+};
+
+// Assemble the 16-byte block of virtual elements [x0, x0+VEC) from the
+// staged segments; pads are zero.  *first receives the first overlapping
+// segment (nseg if none).
+template <int W, class Src>
+__device__ __forceinline__ u32x4 gather_block(const TileLds &L, int nseg, int64_t x0, Src src, int *first) {
+    constexpr int VEC = 16 / W;
+    u32x4 r = {0u, 0u, 0u, 0u};
+    int s = find_first_ending_after(L, nseg, x0);
+    *first = s;
+    for (; s < nseg && L.vx[s] < x0 + VEC; ++s) {
+        const int e_lo = (int)(imax(x0, L.vx[s]) - x0);
+        const int e_hi = (int)(imin(x0 + VEC, L.end[s]) - x0);
+        // byte address element 0 of this block would have in the source run
+        const intptr_t base = reinterpret_cast<intptr_t>(src(L.buf[s])) + (L.src[s] + (x0 - L.vx[s])) * W;
+        const intptr_t a0 = base & ~(intptr_t)15;
+        const uint32_t sh = (uint32_t)(base & 15);
+        const intptr_t valid_lo = base + e_lo * W, valid_hi = base + e_hi * W;
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (a0 + 16 > valid_lo) lo = ld16(reinterpret_cast<const char *>(a0));
+        if (sh != 0 && a0 + 16 < valid_hi) hi = ld16(reinterpret_cast<const char *>(a0 + 16));
+        const u32x4 v = funnel16(lo, hi, sh);
+        const u32x4 m = elem_mask<W>(e_lo, e_hi);
+        r = (r & ~m) | (v & m);
+    }
+    return r;
+}
+
+template <int W>
+__device__ __forceinline__ void stage_tile(TileLds &L, const Segment *segs, const Tile &t) {
+    for (int k = threadIdx.x; k < t.nseg; k += kThreads) {
+        const Segment sg = segs[t.seg_lo + k];
+        L.vx[k] = sg.vx;
+        L.end[k] = sg.vx + sg.len;
+        L.src[k] = sg.src_off;
+        L.buf[k] = sg.buf;
+    }
+    __syncthreads();
+}
+
+// Uniform fast path: the whole tile is one contiguous run src -> dst with a
+// 16-byte-aligned destination.  `src` is the byte address of the tile's
+// first element in the source.
+__device__ __forceinline__ void copy_run(char *dst, const char *src, int nblk) {
+    constexpr int U = fsi::kBlocksPerThread;
+    const int tid = threadIdx.x;
+    const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(src) & 15);
+    if (sh == 0) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = u * kThreads + tid;
+            if (b < nblk) v[u] = ld16(src + 16 * (int64_t)b);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = u * kThreads + tid;
+            if (b < nblk) st16(dst + 16 * (int64_t)b, v[u]);
+        }
+        return;
+    }
+    // Misaligned source: lane l loads aligned block b (containing the start
+    // of its 16 bytes); the following aligned block is lane l+1's load,
+    // fetched with a wavefront shuffle.  The last lane of each wave (and the
+    // lane holding the tile's last block) loads it itself; that block holds
+    // needed bytes because sh > 0.
+    const char *a = src - sh;
+    const int lane = tid & 63;
+    u32x4 lo[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int b = u * kThreads + tid;
+        lo[u] = b < nblk ? ld16(a + 16 * (int64_t)b) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int b = u * kThreads + tid;
+        u32x4 hi;
+        hi.x = __shfl_down(lo[u].x, 1);
+        hi.y = __shfl_down(lo[u].y, 1);
+        hi.z = __shfl_down(lo[u].z, 1);
+        hi.w = __shfl_down(lo[u].w, 1);
+        if (b < nblk) {
+            if (lane == 63 || b + 1 >= nblk) hi = ld16(a + 16 * (int64_t)(b + 1));
+            st16(dst + 16 * (int64_t)b, funnel16(lo[u], hi, sh));
+        }
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(kThreads) void pack_kernel(const Segment *__restrict__ segs,
+                                                        const Tile *__restrict__ tiles,
+                                                        const void *const *__restrict__ params,
+                                                        char *__restrict__ out, int64_t dst_lo,
+                                                        int64_t dst_hi) {
+    constexpr int VEC = 16 / W;
+    __shared__ TileLds L;
+    const Tile t = tiles[blockIdx.x];
+    stage_tile<W>(L, segs, t);
+    const int64_t x_end = t.x_begin + (int64_t)t.nblk * VEC;
+    char *dst0 = out + (t.x_begin - dst_lo) * W;
+    const bool dst_full = t.x_begin >= dst_lo && x_end <= dst_hi &&
+                          (reinterpret_cast<uintptr_t>(dst0) & 15) == 0;
+    if (dst_full && t.nseg == 1 && L.vx[0] <= t.x_begin && L.end[0] >= x_end) {
+        const char *src = reinterpret_cast<const char *>(params[L.buf[0]]) +
+                          (L.src[0] + (t.x_begin - L.vx[0])) * W;
+        copy_run(dst0, src, t.nblk);
+        return;
+    }
+    const PackSrc S{params};
+#pragma unroll 2
+    for (int u = 0; u < fsi::kBlocksPerThread; ++u) {
+        const int b = u * kThreads + threadIdx.x;
+        if (b >= t.nblk) break;
+        const int64_t x0 = t.x_begin + (int64_t)b * VEC;
+        int first;
+        const u32x4 v = gather_block<W>(L, t.nseg, x0, S, &first);
+        char *dst = dst0 + 16 * (int64_t)b;
+        if (dst_full) {
+            st16(dst, v);
+        } else {
+            const int e_lo = (int)imax(0, dst_lo - x0);
+            const int e_hi = (int)imin(VEC, dst_hi - x0);
+            if (e_lo == 0 && e_hi == VEC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0)
+                st16(dst, v);
+            else
+                store_elems<W>(dst, v, e_lo, e_hi);
+        }
+    }
+}
+
+template <int W>
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const Segment *__restrict__ segs,
+                                                          const Tile *__restrict__ tiles,
+                                                          const BufInfo *__restrict__ bufs,
+                                                          const char *__restrict__ gathered,
+                                                          void *const *__restrict__ params) {
+    constexpr int VEC = 16 / W;
+    __shared__ TileLds L;
+    const Tile t = tiles[blockIdx.x];
+    stage_tile<W>(L, segs, t);
+    const int64_t x_end = t.x_begin + (int64_t)t.nblk * VEC;
+    if (t.nseg == 1 && L.vx[0] <= t.x_begin && L.end[0] >= x_end) {
+        const int j = L.buf[0];
+        char *dst0 = reinterpret_cast<char *>(params[j]) + (t.x_begin - bufs[j].vbase) * W;
+        if ((reinterpret_cast<uintptr_t>(dst0) & 15) == 0) {
+            copy_run(dst0, gathered + (L.src[0] + (t.x_begin - L.vx[0])) * W, t.nblk);
+            return;
+        }
+    }
+    const UnpackSrc S{gathered};
+#pragma unroll 2
+    for (int u = 0; u < fsi::kBlocksPerThread; ++u) {
+        const int b = u * kThreads + threadIdx.x;
+        if (b >= t.nblk) break;
+        const int64_t x0 = t.x_begin + (int64_t)b * VEC;
+        int first;
+        const u32x4 v = gather_block<W>(L, t.nseg, x0, S, &first);
+        if (first >= t.nseg || L.vx[first] >= x0 + VEC) continue;   // no element of any parameter
+        const int j = L.buf[first];
+        const BufInfo bi = bufs[j];
+        char *dst = reinterpret_cast<char *>(params[j]) + (x0 - bi.vbase) * W;
+        const int e_hi = (int)imin(VEC, bi.vbase + bi.numel - x0);
+        if (e_hi == VEC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0)
+            st16(dst, v);
+        else
+            store_elems<W>(dst, v, 0, e_hi);
+    }
+}
+
+// ---------------------------------------------------------------- reduce --
+//
+// Lane i owns 8 consecutive elements of the shard: per term it issues one
+// dwordx4 load (8 bf16) and adds the widened values into 8 fp32
+// accumulators, in slice order, so the summation order is exactly the
+// sequential one with no cross-lane traffic; the last pass divides by N and
+// writes two dwordx4 (8 fp32).  More than kTermsPerPass terms are split into
+// passes that carry the fp32 partial sum through `out`, which is the same
+// arithmetic as one pass.
+
+constexpr int kTermsPerPass = 32;
+
+struct SliceArgs {
+    const uint16_t *p[kTermsPerPass];
+};
+
+__device__ __forceinline__ void add_bf16x8(float acc[8], u32x4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = acc[2 * i] + __uint_as_float(w[i] << 16);
+        acc[2 * i + 1] = acc[2 * i + 1] + __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+__device__ __forceinline__ void set_bf16x8(float acc[8], u32x4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __uint_as_float(w[i] << 16);
+        acc[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+// Load 16 bytes of slice `p` starting at byte offset `off` (even); aligned
+// loads plus a funnel shift when the slice is not 16-byte aligned.  Both
+// loads overlap bytes [p+off, p+off+16), which lie inside the slice.
+template <bool ALIGNED>
+__device__ __forceinline__ u32x4 ld_slice16(const uint16_t *p, int64_t off) {
+    const char *c = reinterpret_cast<const char *>(p) + off;
+    if (ALIGNED) return ld16(c);
+    const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(c) & 15);
+    const char *a = c - sh;
+    const u32x4 lo = ld16(a);
+    const u32x4 hi = sh ? ld16(a + 16) : u32x4{0u, 0u, 0u, 0u};
+    return funnel16(lo, hi, sh);
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nterms, int first_pass,
+                                                          int last_pass, float world,
+                                                          int64_t n, float *__restrict__ out) {
+    const int64_t nvec = n >> 3;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < nvec) {
+        const int64_t off = i * 16;
+        float acc[8];
+        int t = 0;
+        if (first_pass) {
+            set_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[0], off));
+            t = 1;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = out[8 * i + e];
+        }
+        for (; t + 8 <= nterms; t += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = ld_slice16<ALIGNED>(sa.p[t + k], off);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) add_bf16x8(acc, v[k]);
+        }
+        for (; t < nterms; ++t) add_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[t], off));
+        if (last_pass) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = acc[e] / world;
+        }
+        if (ALIGNED) {
+            st16(reinterpret_cast<char *>(out + 8 * i),
+                 u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                       __float_as_uint(acc[3])});
+            st16(reinterpret_cast<char *>(out + 8 * i + 4),
+                 u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
+                       __float_as_uint(acc[7])});
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[8 * i + e] = acc[e];
+        }
+    }
+    // ragged tail: the last n % 8 elements, one per lane of the first wave
+    const int64_t tail = n - nvec * 8;
+    if (blockIdx.x == 0 && (int64_t)threadIdx.x < tail) {
+        const int64_t e = nvec * 8 + threadIdx.x;
+        float acc;
+        int t = 0;
+        if (first_pass) {
+            acc = __uint_as_float((uint32_t)sa.p[0][e] << 16);
+            t = 1;
+        } else {
+            acc = out[e];
+        }
+        for (; t < nterms; ++t) acc = acc + __uint_as_float((uint32_t)sa.p[t][e] << 16);
+        out[e] = last_pass ? acc / world : acc;
+    }
+}
+
+// ----------------------------------------------------------------- AdamW --
+//
+// One fused read-modify-write pass: read g, theta, m, v; write theta, m, v
+// and the bf16 parameter.  Lane i owns 8 consecutive elements (dwordx4
+// accesses).  The update is evaluated in double from the fp32 inputs and
+// rounded to fp32 once per stored value; the bias corrections 1 - beta^t are
+// per-step scalars computed on the host.
+
+struct AdamConsts {
+    double b1, b2, omb1, omb2, bc1, bc2, lr, eps, decay;
+};
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void adam_elem(const AdamConsts &c, float g32, float &th32, float &m32,
+                                          float &v32) {
+    const double g = g32, th = th32, m = m32, v = v32;
+    const double m_new = c.b1 * m + c.omb1 * g;
+    const double v_new = c.b2 * v + c.omb2 * g * g;
+    const double m_hat = m_new / c.bc1;
+    const double v_hat = v_new / c.bc2;
+    const double th_new = th * c.decay - c.lr * m_hat / (sqrt(v_hat) + c.eps);
+    th32 = (float)th_new;
+    m32 = (float)m_new;
+    v32 = (float)v_new;
+}
+
+__device__ __forceinline__ void f4(u32x4 v, float o[4]) {
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ u32x4 u4(const float o[4]) {
+    return u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+}
+
+template <bool GRAD_BF16, bool HAS_P16>
+__global__ __launch_bounds__(kThreads) void adamw_vec_kernel(int64_t nvec, float *__restrict__ th,
+                                                             float *__restrict__ m,
+                                                             float *__restrict__ v,
+                                                             const void *__restrict__ grad,
+                                                             uint16_t *__restrict__ p16,
+                                                             AdamConsts c) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= nvec) return;
+    char *pt = reinterpret_cast<char *>(th + 8 * i);
+    char *pm = reinterpret_cast<char *>(m + 8 * i);
+    char *pv = reinterpret_cast<char *>(v + 8 * i);
+    float G[8], T[8], M[8], V[8];
+    if (GRAD_BF16) {
+        const u32x4 gb = ld16(reinterpret_cast<const char *>(grad) + 16 * i);
+        const uint32_t w[4] = {gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            G[2 * k] = __uint_as_float(w[k] << 16);
+            G[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    } else {
+        const char *pg = reinterpret_cast<const char *>(grad) + 32 * i;
+        f4(ld16(pg), G);
+        f4(ld16(pg + 16), G + 4);
+    }
+    f4(ld16(pt), T);
+    f4(ld16(pt + 16), T + 4);
+    f4(ld16(pm), M);
+    f4(ld16(pm + 16), M + 4);
+    f4(ld16(pv), V);
+    f4(ld16(pv + 16), V + 4);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) adam_elem(c, G[k], T[k], M[k], V[k]);
+    st16(pt, u4(T));
+    st16(pt + 16, u4(T + 4));
+    st16(pm, u4(M));
+    st16(pm + 16, u4(M + 4));
+    st16(pv, u4(V));
+    st16(pv + 16, u4(V + 4));
+    if (HAS_P16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w[k] = (uint32_t)bf16_rne(T[2 * k]) | ((uint32_t)bf16_rne(T[2 * k + 1]) << 16);
+        st16(reinterpret_cast<char *>(p16 + 8 * i), u32x4{w[0], w[1], w[2], w[3]});
+    }
+}
+
+// Element-wise variant for misaligned buffers and the ragged tail.
+__global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t begin, int64_t n, float *th,
+                                                                float *m, float *v,
+                                                                const void *grad, int grad_bf16,
+                                                                uint16_t *p16, AdamConsts c) {
+    const int64_t e = begin + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= n) return;
+    const float g = grad_bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(grad)[e] << 16)
+                              : reinterpret_cast<const float *>(grad)[e];
+    float T = th[e], M = m[e], V = v[e];
+    adam_elem(c, g, T, M, V);
+    th[e] = T;
+    m[e] = M;
+    v[e] = V;
+    if (p16) p16[e] = bf16_rne(T);
+}
+
+// ------------------------------------------------------------------ copy --
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(char *__restrict__ dst,
+                                                        const char *__restrict__ src, int64_t nvec) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < nvec) st16(dst + 16 * i, ld16(src + 16 * i));
+}
+
+// -------------------------------------------------------------- launchers --
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+int check_launch(const char *what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fsi::fail(FS_E_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return FS_OK;
+}
+
+bool ranges_overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return abytes > 0 && bbytes > 0 && x < y + (uintptr_t)bbytes && y < x + (uintptr_t)abytes;
+}
+
+}  // namespace
+
+extern "C" int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hipStream_t stream) {
+    fsi::clear_error();
+    if (!plan || !workspace) return fsi::fail(FS_E_INVAL, "fs_plan_upload: NULL argument");
+    if (misaligned(workspace, 16)) return fsi::fail(FS_E_ALIGN, "fs_plan_upload: workspace must be 16-byte aligned");
+    const fsi::WorkspaceLayout &w = plan->ws;
+    if ((int64_t)bytes < w.total_bytes)
+        return fsi::fail(FS_E_INVAL, "fs_plan_upload: workspace too small (%zu < %lld bytes)", bytes,
+                         (long long)w.total_bytes);
+    char *ws = static_cast<char *>(workspace);
+    struct Part { int64_t off; const void *src; int64_t bytes; };
+    const Part parts[] = {
+        {w.pack_segs, plan->pack_segs.data(), w.n_pack_segs * (int64_t)sizeof(Segment)},
+        {w.unpack_segs, plan->unpack_segs.data(), w.n_unpack_segs * (int64_t)sizeof(Segment)},
+        {w.pack_tiles_all, plan->pack_tiles_all.data(), w.n_pack_tiles_all * (int64_t)sizeof(Tile)},
+        {w.pack_tiles_rank, plan->pack_tiles_rank.data(), w.n_pack_tiles_rank * (int64_t)sizeof(Tile)},
+        {w.unpack_tiles, plan->unpack_tiles.data(), w.n_unpack_tiles * (int64_t)sizeof(Tile)},
+        {w.bufinfo, plan->bufinfo.data(), w.n_bufinfo * (int64_t)sizeof(BufInfo)},
+    };
+    for (const Part &p : parts) {
+        if (p.bytes == 0) continue;
+        hipError_t e = hipMemcpyAsync(ws + p.off, p.src, (size_t)p.bytes, hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_plan_upload: copy failed: %s", hipGetErrorString(e));
+    }
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_plan_upload: sync failed: %s", hipGetErrorString(e));
+    plan->dev_ws = workspace;
+    return FS_OK;
+}
+
+extern "C" int fs_pack(fs_plan_t plan, const void *const *params, void *out, int32_t rank,
+                       hipStream_t stream) {
+    fsi::clear_error();
+    if (!plan) return fsi::fail(FS_E_INVAL, "fs_pack: plan is NULL");
+    const fs_plan_info_t &I = plan->info;
+    if (!plan->dev_ws) return fsi::fail(FS_E_INVAL, "fs_pack: plan has no uploaded workspace (call fs_plan_upload)");
+    if (rank < -1 || rank >= I.world) return fsi::fail(FS_E_INVAL, "fs_pack: rank %d out of range [-1, %d)", rank, I.world);
+    const int64_t lo = rank < 0 ? 0 : (int64_t)rank * I.shard_numel;
+    const int64_t hi = rank < 0 ? I.gathered_numel : lo + I.shard_numel;
+    if (hi == lo) return FS_OK;
+    if (!out) return fsi::fail(FS_E_INVAL, "fs_pack: out is NULL");
+    if (I.n_params > 0 && !params) return fsi::fail(FS_E_INVAL, "fs_pack: params is NULL");
+    if (misaligned(out, I.elem_bytes)) return fsi::fail(FS_E_ALIGN, "fs_pack: out not aligned to %d bytes", I.elem_bytes);
+    const char *ws = static_cast<const char *>(plan->dev_ws);
+    const Segment *segs = reinterpret_cast<const Segment *>(ws + plan->ws.pack_segs);
+    const Tile *tiles;
+    int64_t ntiles;
+    if (rank < 0) {
+        tiles = reinterpret_cast<const Tile *>(ws + plan->ws.pack_tiles_all);
+        ntiles = plan->ws.n_pack_tiles_all;
+    } else {
+        tiles = reinterpret_cast<const Tile *>(ws + plan->ws.pack_tiles_rank) + plan->rank_tile_off[rank];
+        ntiles = plan->rank_tile_off[rank + 1] - plan->rank_tile_off[rank];
+    }
+    if (ntiles == 0) return FS_OK;
+    (void)hipGetLastError();
+    // `out` is addressed from the virtual element `lo` on
+    char *base = static_cast<char *>(out);
+    if (I.elem_bytes == 2)
+        hipLaunchKernelGGL(pack_kernel<2>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
+                           params, base, lo, hi);
+    else
+        hipLaunchKernelGGL(pack_kernel<4>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
+                           params, base, lo, hi);
+    return check_launch("fs_pack");
+}
+
+extern "C" int fs_unpack(fs_plan_t plan, const void *gathered, void *const *params, hipStream_t stream) {
+    fsi::clear_error();
+    if (!plan) return fsi::fail(FS_E_INVAL, "fs_unpack: plan is NULL");
+    const fs_plan_info_t &I = plan->info;
+    if (!plan->dev_ws) return fsi::fail(FS_E_INVAL, "fs_unpack: plan has no uploaded workspace (call fs_plan_upload)");
+    const int64_t ntiles = plan->ws.n_unpack_tiles;
+    if (ntiles == 0 || I.total_numel == 0) return FS_OK;
+    if (!gathered || !params) return fsi::fail(FS_E_INVAL, "fs_unpack: NULL pointer");
+    if (misaligned(gathered, I.elem_bytes))
+        return fsi::fail(FS_E_ALIGN, "fs_unpack: gathered not aligned to %d bytes", I.elem_bytes);
+    const char *ws = static_cast<const char *>(plan->dev_ws);
+    const Segment *segs = reinterpret_cast<const Segment *>(ws + plan->ws.unpack_segs);
+    const Tile *tiles = reinterpret_cast<const Tile *>(ws + plan->ws.unpack_tiles);
+    const BufInfo *bufs = reinterpret_cast<const BufInfo *>(ws + plan->ws.bufinfo);
+    (void)hipGetLastError();
+    const char *g = static_cast<const char *>(gathered);
+    if (I.elem_bytes == 2)
+        hipLaunchKernelGGL(unpack_kernel<2>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
+                           bufs, g, params);
+    else
+        hipLaunchKernelGGL(unpack_kernel<4>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
+                           bufs, g, params);
+    return check_launch("fs_unpack");
+}
+
+extern "C" int fs_reduce_shard(int64_t n, int32_t world, int32_t grad_acc, const uint16_t *const *slices,
+                               float *out, hipStream_t stream) {
+    fsi::clear_error();
+    if (n < 0) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: n < 0");
+    if (world < 1 || grad_acc < 1) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: world and grad_acc must be >= 1");
+    int64_t terms64;
+    if (__builtin_mul_overflow((int64_t)world, (int64_t)grad_acc, &terms64) || terms64 > (1 << 20))
+        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: too many terms");
+    int64_t bytes_in, bytes_out;
+    if (__builtin_mul_overflow(n, (int64_t)2, &bytes_in) || __builtin_mul_overflow(n, (int64_t)4, &bytes_out))
+        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large");
+    if (n == 0) return FS_OK;
+    if (!slices || !out) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: NULL pointer");
+    const int terms = (int)terms64;
+    bool aligned = !misaligned(out, 16);
+    if (misaligned(out, 4)) return fsi::fail(FS_E_ALIGN, "fs_reduce_shard: out not 4-byte aligned");
+    for (int t = 0; t < terms; ++t) {
+        if (!slices[t]) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: slice %d is NULL", t);
+        if (misaligned(slices[t], 2)) return fsi::fail(FS_E_ALIGN, "fs_reduce_shard: slice %d not 2-byte aligned", t);
+        if (misaligned(slices[t], 16)) aligned = false;
+        if (ranges_overlap(slices[t], bytes_in, out, bytes_out))
+            return fsi::fail(FS_E_INVAL, "fs_reduce_shard: out overlaps slice %d", t);
+    }
+    const int64_t nvec = n >> 3;
+    const int64_t grid = std::max<int64_t>(1, (nvec + kThreads - 1) / kThreads);
+    if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large for one launch");
+    (void)hipGetLastError();
+    for (int t0 = 0; t0 < terms; t0 += kTermsPerPass) {
+        SliceArgs sa;
+        memset(&sa, 0, sizeof sa);
+        const int cnt = std::min(kTermsPerPass, terms - t0);
+        for (int k = 0; k < cnt; ++k) sa.p[k] = slices[t0 + k];
+        const int first = t0 == 0, last = t0 + cnt == terms;
+        if (aligned)
+            hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, cnt,
+                               first, last, (float)world, n, out);
+        else
+            hipLaunchKernelGGL(reduce_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, cnt,
+                               first, last, (float)world, n, out);
+        int rc = check_launch("fs_reduce_shard");
+        if (rc != FS_OK) return rc;
+    }
+    return FS_OK;
+}
+
+extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *exp_avg_sq, const void *grad,
+                             fs_dtype grad_dtype, uint16_t *param_bf16, const fs_adamw_hparams_t *hp,
+                             hipStream_t stream) {
+    fsi::clear_error();
+    if (n < 0) return fsi::fail(FS_E_INVAL, "fs_adamw_step: n < 0");
+    if (!hp) return fsi::fail(FS_E_INVAL, "fs_adamw_step: hp is NULL");
+    if (grad_dtype != FS_BF16 && grad_dtype != FS_FP32) return fsi::fail(FS_E_DTYPE, "fs_adamw_step: unknown grad dtype");
+    if (hp->step < 1) return fsi::fail(FS_E_INVAL, "fs_adamw_step: step must be >= 1");
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f && hp->beta2 >= 0.f && hp->beta2 < 1.f))
+        return fsi::fail(FS_E_INVAL, "fs_adamw_step: betas must lie in [0, 1)");
+    int64_t nb;
+    if (__builtin_mul_overflow(n, (int64_t)4, &nb)) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large");
+    if (n == 0) return FS_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !grad) return fsi::fail(FS_E_INVAL, "fs_adamw_step: NULL pointer");
+    const int gb = grad_dtype == FS_BF16 ? 2 : 4;
+    if (misaligned(master, 4) || misaligned(exp_avg, 4) || misaligned(exp_avg_sq, 4) || misaligned(grad, gb) ||
+        (param_bf16 && misaligned(param_bf16, 2)))
+        return fsi::fail(FS_E_ALIGN, "fs_adamw_step: pointer not aligned to its element size");
+    AdamConsts c;
+    c.b1 = hp->beta1;
+    c.b2 = hp->beta2;
+    c.omb1 = 1.0 - c.b1;
+    c.omb2 = 1.0 - c.b2;
+    c.bc1 = 1.0 - pow(c.b1, (double)hp->step);
+    c.bc2 = 1.0 - pow(c.b2, (double)hp->step);
+    c.lr = hp->lr;
+    c.eps = hp->eps;
+    c.decay = 1.0 - (double)hp->lr * (double)hp->weight_decay;
+    const bool aligned = !misaligned(master, 16) && !misaligned(exp_avg, 16) && !misaligned(exp_avg_sq, 16) &&
+                         !misaligned(grad, 16) && !(param_bf16 && misaligned(param_bf16, 16));
+    (void)hipGetLastError();
+    int64_t done = 0;
+    if (aligned) {
+        const int64_t nvec = n >> 3;
+        if (nvec > 0) {
+            const int64_t grid = (nvec + kThreads - 1) / kThreads;
+            if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
+            const dim3 g((uint32_t)grid), b(kThreads);
+            if (grad_dtype == FS_BF16) {
+                if (param_bf16)
+                    hipLaunchKernelGGL((adamw_vec_kernel<true, true>), g, b, 0, stream, nvec, master, exp_avg,
+                                       exp_avg_sq, grad, param_bf16, c);
+                else
+                    hipLaunchKernelGGL((adamw_vec_kernel<true, false>), g, b, 0, stream, nvec, master, exp_avg,
+                                       exp_avg_sq, grad, param_bf16, c);
+            } else {
+                if (param_bf16)
+                    hipLaunchKernelGGL((adamw_vec_kernel<false, true>), g, b, 0, stream, nvec, master, exp_avg,
+                                       exp_avg_sq, grad, param_bf16, c);
+                else
+                    hipLaunchKernelGGL((adamw_vec_kernel<false, false>), g, b, 0, stream, nvec, master, exp_avg,
+                                       exp_avg_sq, grad, param_bf16, c);
+            }
+            done = nvec * 8;
+        }
+    }
+    if (done < n) {
+        const int64_t rest = n - done;
+        const int64_t grid = (rest + kThreads - 1) / kThreads;
+        if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
+        hipLaunchKernelGGL(adamw_scalar_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, done, n, master,
+                           exp_avg, exp_avg_sq, grad, (int)(grad_dtype == FS_BF16), param_bf16, c);
+    }
+    return check_launch("fs_adamw_step");
+}
+
+extern "C" int fs_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t stream) {
+    fsi::clear_error();
+    if (bytes < 0 || (bytes & 15)) return fsi::fail(FS_E_INVAL, "fs_copy_bytes: bytes must be a multiple of 16");
+    if (bytes == 0) return FS_OK;
+    if (!dst || !src) return fsi::fail(FS_E_INVAL, "fs_copy_bytes: NULL pointer");
+    if (misaligned(dst, 16) || misaligned(src, 16)) return fsi::fail(FS_E_ALIGN, "fs_copy_bytes: pointers must be 16-byte aligned");
+    if (ranges_overlap(dst, bytes, src, bytes)) return fsi::fail(FS_E_INVAL, "fs_copy_bytes: ranges overlap");
+    const int64_t nvec = bytes / 16;
+    const int64_t grid = (nvec + kThreads - 1) / kThreads;
+    if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_copy_bytes: too large for one launch");
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(copy_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, static_cast<char *>(dst),
+                       static_cast<const char *>(src), nvec);
+    return check_launch("fs_copy_bytes");
+}

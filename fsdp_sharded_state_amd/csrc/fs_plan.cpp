@@ -1,0 +1,332 @@
+// fs_plan.cpp -- host planner: shard layouts, segment lowering, tile index.
+//
+// Layout rules (page "FSDP1 vs FSDP2", section 03 and Table 3):
+//   FSDP1 FlatParameter: parameters flattened and concatenated in order; with
+//     use_orig_params every parameter after the first starts on a multiple of
+//     a = 16/bytes(dtype) elements (at most a-1 pad elements); the flat of
+//     length L is split into N equal shards of c = ceil(L/N) elements (world
+//     pad to a multiple of N with use_orig_params, chunk(N) padded to
+//     chunks[0] without -- the same c).
+//   FSDP2 per-parameter: parameter i is chunked on dim 0, ceil(d0_i/N) rows
+//     per rank with torch.chunk semantics (later ranks may get fewer or no
+//     rows), each chunk padded to the full row count; every rank's shard
+//     concatenates its chunks in parameter order, and the group's all-gather
+//     output is rank-major [N][T].
+// Memory ledger ("FSDP1 vs FSDP2" section 01; "Data parallelism, ZeRO and
+// FSDP" section 9; "ZeRO/FSDP explainer" section 03): per-rank bytes
+// P(2b + bopt)/N, plus 4P/N for an fp32 gradient accumulator.
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "fs_plan_impl.h"
+
+using fsi::Segment;
+using fsi::Tile;
+
+namespace fsi {
+
+static thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+}  // namespace fsi
+
+extern "C" const char *fs_last_error(void) { return fsi::g_err; }
+
+namespace {
+
+constexpr int64_t kMaxI64 = INT64_MAX;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow(a, b, out); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+// Cut the grid of blocks [lo + k*vec, lo + (k+1)*vec) covering [lo, hi) into
+// tiles of at most kTileBlocks blocks that overlap at most kTileSegs segments.
+// `segs` is sorted by vx and non-overlapping.
+void build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec,
+                 std::vector<Tile> &out) {
+    if (hi <= lo) return;
+    const int64_t nblocks = ceil_div(hi - lo, vec);
+    const int64_t nseg = (int64_t)segs.size();
+    // first segment whose end lies beyond x
+    auto first_ending_after = [&](int64_t from, int64_t x) {
+        int64_t a = from, b = nseg;
+        while (a < b) {
+            int64_t m = (a + b) / 2;
+            if (segs[m].vx + segs[m].len <= x) a = m + 1; else b = m;
+        }
+        return a;
+    };
+    // first segment starting at or beyond x
+    auto first_starting_at = [&](int64_t from, int64_t x) {
+        int64_t a = from, b = nseg;
+        while (a < b) {
+            int64_t m = (a + b) / 2;
+            if (segs[m].vx < x) a = m + 1; else b = m;
+        }
+        return a;
+    };
+    int64_t s0 = first_ending_after(0, lo);
+    int64_t b0 = 0;
+    while (b0 < nblocks) {
+        int64_t x0 = lo + b0 * vec;
+        s0 = first_ending_after(s0, x0);
+        int64_t b1 = std::min<int64_t>(nblocks, b0 + fsi::kTileBlocks);
+        if (s0 + fsi::kTileSegs < nseg) {
+            // keep the (kTileSegs+1)-th segment out of this tile
+            int64_t cut = (segs[s0 + fsi::kTileSegs].vx - lo) / vec;
+            if (cut < b1) b1 = cut;
+        }
+        int64_t x1 = std::min(hi, lo + b1 * vec);
+        int64_t s1 = first_starting_at(s0, x1);
+        Tile t;
+        t.x_begin = x0;
+        t.nblk = (int32_t)(b1 - b0);
+        t.seg_lo = (int32_t)s0;
+        t.nseg = (int32_t)(s1 - s0);
+        t.pad_ = 0;
+        out.push_back(t);
+        b0 = b1;
+    }
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dims,
+                       fs_dtype dtype, int32_t world, int32_t use_orig_params,
+                       fs_mode mode, int32_t grad_acc, fs_plan_t *out) {
+    fsi::clear_error();
+    if (!out) return fsi::fail(FS_E_INVAL, "fs_plan: out is NULL");
+    *out = nullptr;
+    if (n_params < 0) return fsi::fail(FS_E_INVAL, "fs_plan: n_params < 0");
+    if (n_params > 0 && (!ndim || !dims)) return fsi::fail(FS_E_INVAL, "fs_plan: ndim/dims is NULL");
+    if (world < 1) return fsi::fail(FS_E_INVAL, "fs_plan: world must be >= 1 (got %d)", world);
+    if (grad_acc < 1) return fsi::fail(FS_E_INVAL, "fs_plan: grad_acc must be >= 1 (got %d)", grad_acc);
+    if (dtype != FS_BF16 && dtype != FS_FP32) return fsi::fail(FS_E_DTYPE, "fs_plan: unknown dtype %d", (int)dtype);
+    if (mode != FS_FSDP1_FLAT && mode != FS_FSDP2_PER_PARAM)
+        return fsi::fail(FS_E_INVAL, "fs_plan: unknown mode %d", (int)mode);
+    if (use_orig_params != 0 && use_orig_params != 1)
+        return fsi::fail(FS_E_INVAL, "fs_plan: use_orig_params must be 0 or 1");
+    if (mode == FS_FSDP2_PER_PARAM && use_orig_params)
+        return fsi::fail(FS_E_UNSUPPORTED, "fs_plan: use_orig_params is an FSDP1 option; FSDP2 shards every parameter on dim 0");
+
+    fs_plan_s *p = new (std::nothrow) fs_plan_s();
+    if (!p) return fsi::fail(FS_E_NOMEM, "fs_plan: out of host memory");
+    try {
+        const int64_t eb = dtype == FS_BF16 ? 2 : 4;
+        const int vec = (int)(16 / eb);
+        p->vec = vec;
+        p->params.resize(n_params);
+        memset(&p->info, 0, sizeof p->info);
+
+        // ---- shapes -> numel, d0, row
+        int64_t di = 0, total = 0;
+        std::vector<int64_t> d0(n_params), row(n_params);
+        for (int32_t i = 0; i < n_params; ++i) {
+            if (ndim[i] < 0 || ndim[i] > 8) {
+                delete p;
+                return fsi::fail(FS_E_INVAL, "fs_plan: parameter %d has ndim %d (0..8 allowed)", i, ndim[i]);
+            }
+            int64_t n = 1, r = 1;
+            for (int32_t k = 0; k < ndim[i]; ++k) {
+                int64_t d = dims[di + k];
+                if (d < 0) {
+                    delete p;
+                    return fsi::fail(FS_E_INVAL, "fs_plan: parameter %d has a negative dim", i);
+                }
+                if (!mul_ok(n, d, &n) || (k > 0 && !mul_ok(r, d, &r))) {
+                    delete p;
+                    return fsi::fail(FS_E_OVERFLOW, "fs_plan: parameter %d numel overflows int64", i);
+                }
+            }
+            d0[i] = ndim[i] ? dims[di] : 1;   // a 0-d parameter counts as [1]
+            row[i] = r;
+            di += ndim[i];
+            p->params[i].numel = n;
+            if (!add_ok(total, n, &total)) {
+                delete p;
+                return fsi::fail(FS_E_OVERFLOW, "fs_plan: total numel overflows int64");
+            }
+        }
+
+        // ---- layout
+        int64_t shard = 0, flat = 0, align_pad = 0;
+        if (mode == FS_FSDP1_FLAT) {
+            const int64_t a = use_orig_params ? vec : 1;   // 16 bytes / element size
+            int64_t off = 0;
+            for (int32_t i = 0; i < n_params; ++i) {
+                if (i > 0) {
+                    int64_t aligned = align_up(off, a);
+                    align_pad += aligned - off;
+                    off = aligned;
+                }
+                p->params[i].start = off;
+                if (!add_ok(off, p->params[i].numel, &off) || off > kMaxI64 - 64) {
+                    delete p;
+                    return fsi::fail(FS_E_OVERFLOW, "fs_plan: flat length overflows int64");
+                }
+            }
+            flat = off;
+            shard = ceil_div(flat, world);
+        } else {
+            int64_t t = 0;
+            for (int32_t i = 0; i < n_params; ++i) {
+                fs_param_layout_t &pl = p->params[i];
+                pl.start = -1;
+                pl.chunk_rows = ceil_div(d0[i], world);
+                pl.row = row[i];
+                pl.pre = t;
+                int64_t part;
+                if (!mul_ok(pl.chunk_rows, row[i], &part) || !add_ok(t, part, &t)) {
+                    delete p;
+                    return fsi::fail(FS_E_OVERFLOW, "fs_plan: shard length overflows int64");
+                }
+            }
+            shard = t;
+        }
+        int64_t gathered, gathered_bytes;
+        if (!mul_ok(shard, world, &gathered) || !mul_ok(gathered, eb, &gathered_bytes) ||
+            gathered > kMaxI64 - 64) {
+            delete p;
+            return fsi::fail(FS_E_OVERFLOW, "fs_plan: gathered size overflows int64");
+        }
+
+        // ---- segments, split at rank boundaries, in gathered order
+        std::vector<Segment> &ps = p->pack_segs;
+        if (mode == FS_FSDP1_FLAT) {
+            for (int32_t i = 0; i < n_params; ++i) {
+                int64_t s = p->params[i].start, n = p->params[i].numel, e = 0;
+                while (e < n) {
+                    int64_t x = s + e;
+                    int32_t r = (int32_t)(x / shard);
+                    int64_t len = std::min(n - e, (int64_t)(r + 1) * shard - x);
+                    ps.push_back(Segment{x, e, len, i, r});
+                    e += len;
+                }
+            }
+        } else {
+            for (int32_t r = 0; r < world; ++r) {
+                for (int32_t i = 0; i < n_params; ++i) {
+                    const fs_param_layout_t &pl = p->params[i];
+                    int64_t first = (int64_t)r * pl.chunk_rows;
+                    int64_t rows = std::max<int64_t>(0, std::min(pl.chunk_rows, d0[i] - first));
+                    int64_t len = rows * pl.row;
+                    if (len > 0)
+                        ps.push_back(Segment{(int64_t)r * shard + pl.pre, first * pl.row, len, i, r});
+                }
+            }
+        }
+
+        // ---- unpack view: parameters laid end to end on 16-byte boundaries
+        p->bufinfo.resize(n_params);
+        int64_t vb = 0;
+        for (int32_t i = 0; i < n_params; ++i) {
+            p->bufinfo[i].vbase = vb;
+            p->bufinfo[i].numel = p->params[i].numel;
+            vb += align_up(p->params[i].numel, vec);
+        }
+        p->unpack_segs.reserve(ps.size());
+        for (const Segment &s : ps)
+            p->unpack_segs.push_back(Segment{p->bufinfo[s.buf].vbase + s.src_off, s.vx, s.len, s.buf, s.rank});
+        std::sort(p->unpack_segs.begin(), p->unpack_segs.end(),
+                  [](const Segment &a, const Segment &b) { return a.vx < b.vx; });
+
+        // ---- tiles
+        build_tiles(ps, 0, gathered, vec, p->pack_tiles_all);
+        p->rank_tile_off.push_back(0);
+        for (int32_t r = 0; r < world; ++r) {
+            build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, p->pack_tiles_rank);
+            p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
+        }
+        build_tiles(p->unpack_segs, 0, vb, vec, p->unpack_tiles);
+
+        // ---- workspace layout (each table on a 256-byte boundary)
+        fsi::WorkspaceLayout &w = p->ws;
+        int64_t off = 0;
+        auto place = [&](int64_t count, int64_t elem, int64_t *o, int64_t *n) {
+            *o = off;
+            *n = count;
+            off = align_up(off + count * elem, 256);
+        };
+        place((int64_t)ps.size(), sizeof(Segment), &w.pack_segs, &w.n_pack_segs);
+        place((int64_t)p->unpack_segs.size(), sizeof(Segment), &w.unpack_segs, &w.n_unpack_segs);
+        place((int64_t)p->pack_tiles_all.size(), sizeof(Tile), &w.pack_tiles_all, &w.n_pack_tiles_all);
+        place((int64_t)p->pack_tiles_rank.size(), sizeof(Tile), &w.pack_tiles_rank, &w.n_pack_tiles_rank);
+        place((int64_t)p->unpack_tiles.size(), sizeof(Tile), &w.unpack_tiles, &w.n_unpack_tiles);
+        place((int64_t)p->bufinfo.size(), sizeof(fsi::BufInfo), &w.bufinfo, &w.n_bufinfo);
+        w.total_bytes = std::max<int64_t>(off, 256);
+
+        // ---- summary and ledger
+        fs_plan_info_t &I = p->info;
+        I.mode = mode;
+        I.dtype = dtype;
+        I.world = world;
+        I.use_orig_params = use_orig_params;
+        I.grad_acc = grad_acc;
+        I.n_params = n_params;
+        I.elem_bytes = (int32_t)eb;
+        I.bopt = 12;
+        I.total_numel = total;
+        I.flat_numel = mode == FS_FSDP1_FLAT ? flat : 0;
+        I.shard_numel = shard;
+        I.gathered_numel = gathered;
+        I.align_pad = align_pad;
+        I.tail_pad = mode == FS_FSDP1_FLAT ? gathered - flat : gathered - total;
+        I.n_segments = (int64_t)ps.size();
+        I.workspace_bytes = w.total_bytes;
+        const double per_param = 2.0 * (double)eb + (double)I.bopt + (grad_acc > 1 ? 4.0 : 0.0);
+        I.ledger_ideal_bytes = (double)total * per_param / (double)world;
+        I.ledger_padded_bytes = (double)shard * per_param;
+    } catch (const std::bad_alloc &) {
+        delete p;
+        return fsi::fail(FS_E_NOMEM, "fs_plan: out of host memory");
+    }
+    *out = p;
+    return FS_OK;
+}
+
+extern "C" int fs_plan_info(fs_plan_t plan, fs_plan_info_t *out) {
+    fsi::clear_error();
+    if (!plan || !out) return fsi::fail(FS_E_INVAL, "fs_plan_info: NULL argument");
+    *out = plan->info;
+    return FS_OK;
+}
+
+extern "C" int fs_plan_param(fs_plan_t plan, int32_t i, fs_param_layout_t *out) {
+    fsi::clear_error();
+    if (!plan || !out) return fsi::fail(FS_E_INVAL, "fs_plan_param: NULL argument");
+    if (i < 0 || i >= plan->info.n_params)
+        return fsi::fail(FS_E_INVAL, "fs_plan_param: index %d out of range", i);
+    *out = plan->params[i];
+    return FS_OK;
+}
+
+extern "C" int fs_plan_segments(fs_plan_t plan, fs_segment_t *out, int64_t cap, int64_t *n) {
+    fsi::clear_error();
+    if (!plan || !n) return fsi::fail(FS_E_INVAL, "fs_plan_segments: NULL argument");
+    if (cap < 0 || (cap > 0 && !out)) return fsi::fail(FS_E_INVAL, "fs_plan_segments: bad output buffer");
+    const int64_t total = (int64_t)plan->pack_segs.size();
+    *n = total;
+    for (int64_t k = 0; k < std::min(cap, total); ++k) {
+        const Segment &s = plan->pack_segs[k];
+        out[k] = fs_segment_t{s.vx, s.src_off, s.len, s.buf, s.rank};
+    }
+    return FS_OK;
+}
+
+extern "C" void fs_plan_destroy(fs_plan_t plan) { delete plan; }

@@ -1,0 +1,32 @@
+// fs_plan_impl.h -- the plan object behind the opaque fs_plan_t, shared by
+// the host planner (fs_plan.cpp) and the launchers (fs_kernels.hip).
+#pragma once
+#include <stdarg.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/fs.h"
+#include "fs_internal.h"
+
+struct fs_plan_s {
+    fs_plan_info_t info;
+    int vec;                                   // elements per 16-byte block: 8 (bf16) or 4 (fp32)
+    std::vector<fs_param_layout_t> params;
+    std::vector<fsi::Segment> pack_segs;       // gathered order
+    std::vector<fsi::Segment> unpack_segs;     // parameter order
+    std::vector<fsi::Tile> pack_tiles_all;
+    std::vector<fsi::Tile> pack_tiles_rank;
+    std::vector<int64_t> rank_tile_off;        // N+1 offsets into pack_tiles_rank
+    std::vector<fsi::Tile> unpack_tiles;
+    std::vector<fsi::BufInfo> bufinfo;
+    fsi::WorkspaceLayout ws;
+    void *dev_ws = nullptr;                    // bound by fs_plan_upload
+    int dev_id = -1;
+};
+
+namespace fsi {
+// Record a message for fs_last_error() and return `code`.
+int fail(int code, const char *fmt, ...);
+void clear_error();
+}  // namespace fsi

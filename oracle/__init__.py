@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_fsdp2_layout.restype = ctypes.c_int
         L.oracle_index_map.argtypes = [vp, vp]
         L.oracle_index_map.restype = None
+        L.oracle_index_at.argtypes = [vp, i64, vp, vp, vp]
+        L.oracle_index_at.restype = None
         L.oracle_pack.argtypes = [vp, vp, vp, i32]
         L.oracle_pack.restype = None
         L.oracle_unpack.argtypes = [vp, vp, vp]
@@ -147,6 +149,17 @@ class Layout:
         c = self._c()
         lib().oracle_index_map(ctypes.byref(c), _ptr(out))
         return out
+
+
+    def index_at(self, param: np.ndarray, elem: np.ndarray) -> np.ndarray:
+        """Gathered index of element elem[k] of parameter param[k]."""
+        param = np.ascontiguousarray(param, np.int32)
+        elem = np.ascontiguousarray(elem, np.int64)
+        assert ((elem >= 0) & (elem < self.numel[param])).all()
+        out = np.empty(max(1, param.size), np.int64)
+        c = self._c()
+        lib().oracle_index_at(ctypes.byref(c), param.size, _ptr(param), _ptr(elem), _ptr(out))
+        return out[:param.size]
 
 
 def fsdp1_layout(shapes: Sequence[Sequence[int]], elem_bytes: int, world: int,

@@ -175,6 +175,15 @@ void oracle_index_map(const oracle_layout *L, int64_t *out)
             out[k++] = gathered_index(L, i, e);
 }
 
+/* Gathered index of sampled elements: out[k] = index of element elem[k] of
+ * parameter param[k]. */
+void oracle_index_at(const oracle_layout *L, int64_t n, const int32_t *param,
+                     const int64_t *elem, int64_t *out)
+{
+    for (int64_t k = 0; k < n; ++k)
+        out[k] = gathered_index(L, param[k], elem[k]);
+}
+
 /*
  * All-gather copy-in [P1 section 03 and the FSDP2 group concatenation]:
  * start from a zero-filled output and copy every parameter element to its

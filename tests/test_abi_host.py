@@ -1,0 +1,212 @@
+"""Host-side checks of the C-ABI library (no GPU call is made).
+
+* libfsstate.so loads and exports every function include/fs.h declares;
+* the planner (fs_plan) lays out exactly what the oracle lays out, on the
+  exhaustive tiny cases and on the workload shapes;
+* the ledger fields equal the oracle's ledger;
+* argument validation returns the documented error codes before touching
+  the GPU.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fsdp_sharded_state_amd as fs
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "fs.h")).read()
+    names = set(re.findall(r"^\s*(?:int|void|const char\s*\*)\s*\*?\s*(fs_\w+)\s*\(", hdr, re.M))
+    assert {"fs_plan", "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step"} <= names
+    L = ctypes.CDLL(fs.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def _plan_index_map(plan):
+    numels = [plan.param(i).numel for i in range(plan.n_params)]
+    offs = np.concatenate([[0], np.cumsum(numels)]).astype(np.int64)
+    out = np.full(int(offs[-1]), -1, np.int64)
+    for dst, src, ln, p, r in plan.segments():
+        assert ln > 0
+        assert dst // plan.shard_numel == r and (dst + ln - 1) // plan.shard_numel == r
+        tgt = out[offs[p] + src: offs[p] + src + ln]
+        assert (tgt == -1).all(), "element placed twice"
+        tgt[:] = np.arange(dst, dst + ln)
+    assert (out >= 0).all(), "element never placed"
+    return out
+
+
+def _oracle_layout(kind, shapes, eb, N, uo):
+    return (oracle.fsdp1_layout(shapes, eb, N, uo) if kind == "fsdp1"
+            else oracle.fsdp2_layout(shapes, eb, N))
+
+
+def _plan_index_sampled(plan, param, elem):
+    """Plan's gathered index of sampled elements, after checking that the
+    segments tile every parameter exactly once and never overlap in the
+    gathered buffer."""
+    segs = np.array(plan.segments(), np.int64).reshape(-1, 5)
+    d = segs[np.argsort(segs[:, 0], kind="stable")]
+    assert (d[1:, 0] >= d[:-1, 0] + d[:-1, 2]).all()            # disjoint in gathered
+    out = np.empty(param.size, np.int64)
+    for i in range(plan.n_params):
+        si = segs[segs[:, 3] == i]
+        si = si[np.argsort(si[:, 1])]
+        numel = plan.param(i).numel
+        if numel == 0:
+            assert si.size == 0
+            continue
+        assert si[0, 1] == 0 and (si[1:, 1] == si[:-1, 1] + si[:-1, 2]).all()
+        assert si[-1, 1] + si[-1, 2] == numel
+        sel = param == i
+        k = np.searchsorted(si[:, 1], elem[sel], side="right") - 1
+        out[sel] = si[k, 0] + elem[sel] - si[k, 1]
+    return out
+
+
+def _compare(kind, shapes, eb, N, uo, grad_acc=1):
+    P = fs.fs_plan(shapes, "bf16" if eb == 2 else "fp32", N, uo, kind, grad_acc)
+    L = _oracle_layout(kind, shapes, eb, N, uo)
+    assert P.shard_numel == L.shard
+    assert P.gathered_numel == N * L.shard
+    assert P.total_numel == int(L.numel.sum())
+    if P.total_numel <= 1 << 20:
+        np.testing.assert_array_equal(_plan_index_map(P), L.index_map())
+    else:   # sampled elements, plus the first and last element of every parameter
+        rng = np.random.default_rng(P.total_numel % 1000)
+        nz = np.nonzero(L.numel)[0]
+        param = np.concatenate([rng.choice(nz, 200000), nz, nz]).astype(np.int32)
+        elem = (rng.random(param.size) * L.numel[param]).astype(np.int64)
+        elem[200000:200000 + nz.size] = 0
+        elem[200000 + nz.size:] = L.numel[nz] - 1
+        np.testing.assert_array_equal(_plan_index_sampled(P, param, elem), L.index_at(param, elem))
+    for i in range(len(shapes)):
+        pl = P.param(i)
+        assert pl.numel == L.numel[i]
+        if kind == "fsdp1":
+            assert pl.start == L.start[i]
+        else:
+            assert (pl.chunk_rows, pl.row, pl.pre) == (L.chunk_rows[i], L.row[i], L.pre[i])
+    if kind == "fsdp1":
+        assert P.flat_numel == L.flat_len
+        assert P.align_pad == L.flat_len - P.total_numel
+        assert P.tail_pad == N * L.shard - L.flat_len
+    led = oracle.ledger(P.total_numel, N, eb, 12, fp32_grad_acc=grad_acc > 1)["zero3"]
+    assert P.ledger_ideal_bytes == pytest.approx(led, rel=1e-12)
+    return P
+
+
+@pytest.mark.parametrize("eb", [2, 4])
+@pytest.mark.parametrize("uo", [False, True])
+def test_plan_matches_oracle_fsdp1_exhaustive(eb, uo):
+    for n in (1, 2, 3):
+        for numels in itertools.product(range(0, 10, 1 if n < 3 else 2), repeat=n):
+            for N in (1, 2, 3, 4, 7, 8):
+                _compare("fsdp1", [(x,) for x in numels], eb, N, uo)
+
+
+def test_plan_matches_oracle_fsdp2_exhaustive():
+    shapes_1 = [(d0, d1) for d0 in range(10) for d1 in (1, 3)] + [(5,), ()]
+    for shapes in itertools.product(shapes_1, repeat=2):
+        for N in (1, 2, 3, 4, 8):
+            _compare("fsdp2", list(shapes), 2, N, False)
+
+
+def test_plan_matches_oracle_workloads():
+    _compare("fsdp1", synth.mlp_tiny_shapes(), 2, 4, True)
+    _compare("fsdp2", synth.llama_block_shapes(), 2, 8, False, grad_acc=1)
+    st = [(n,) for n in synth.padding_stress_numels()]
+    for eb in (2, 4):
+        for uo in (True, False):
+            _compare("fsdp1", st, eb, 8, uo)
+    for g in synth.llama_model_groups(1, 4096, 11008)[-1:]:
+        _compare("fsdp2", g, 2, 8, False, grad_acc=4)
+
+
+def test_seven_b_ledger_from_plans():
+    """Sum of the 33 group plans of the 7B model at N=8: the pages' 16 B/param
+    ZeRO-3 figure (14 GB for 7B) scales to this model's P = 6.738e9."""
+    groups = synth.llama_model_groups(32, 4096, 11008)
+    plans = [fs.fs_plan(g, "bf16", 8, False, "fsdp2", 1) for g in groups]
+    P = sum(p.total_numel for p in plans)
+    assert P == 6738411520
+    ideal = sum(p.ledger_ideal_bytes for p in plans)
+    assert ideal == pytest.approx(oracle.ledger(P, 8, 2, 12)["zero3"])
+    assert sum(p.shard_numel for p in plans) == 842301440
+    assert sum(p.tail_pad for p in plans) == 0
+
+
+def test_plan_errors():
+    L = fs.lib()
+    h = ctypes.c_void_p()
+    nd = (ctypes.c_int32 * 1)(1)
+    dm = (ctypes.c_int64 * 1)(5)
+    assert L.fs_plan(1, nd, dm, 0, 0, 0, 1, 1, ctypes.byref(h)) == fs.FS_E_INVAL      # N < 1
+    assert L.fs_plan(1, nd, dm, 0, 4, 0, 1, 0, ctypes.byref(h)) == fs.FS_E_INVAL      # grad_acc < 1
+    assert L.fs_plan(1, nd, dm, 7, 4, 0, 1, 1, ctypes.byref(h)) == fs.FS_E_DTYPE
+    assert L.fs_plan(1, nd, dm, 0, 4, 1, 2, 1, ctypes.byref(h)) == fs.FS_E_UNSUPPORTED
+    assert L.fs_plan(-1, nd, dm, 0, 4, 0, 1, 1, ctypes.byref(h)) == fs.FS_E_INVAL
+    assert L.fs_plan(1, None, None, 0, 4, 0, 1, 1, ctypes.byref(h)) == fs.FS_E_INVAL
+    assert L.fs_plan(1, nd, dm, 0, 4, 0, 3, 1, ctypes.byref(h)) == fs.FS_E_INVAL      # mode
+    neg = (ctypes.c_int64 * 1)(-2)
+    assert L.fs_plan(1, nd, neg, 0, 4, 0, 1, 1, ctypes.byref(h)) == fs.FS_E_INVAL
+    big_nd = (ctypes.c_int32 * 1)(3)
+    big = (ctypes.c_int64 * 3)(1 << 30, 1 << 30, 1 << 30)
+    assert L.fs_plan(1, big_nd, big, 0, 4, 0, 1, 1, ctypes.byref(h)) == fs.FS_E_OVERFLOW
+    nd9 = (ctypes.c_int32 * 1)(9)
+    assert L.fs_plan(1, nd9, (ctypes.c_int64 * 9)(*[1] * 9), 0, 4, 0, 1, 1, ctypes.byref(h)) == fs.FS_E_INVAL
+    assert b"world" in L.fs_last_error() or len(L.fs_last_error()) > 0
+
+
+def test_empty_and_degenerate_plans():
+    p = fs.fs_plan([], "bf16", 4, True, "fsdp1")
+    assert p.shard_numel == 0 and p.gathered_numel == 0 and p.n_segments == 0
+    p = fs.fs_plan([(0,), (0, 5)], "bf16", 4, False, "fsdp2")
+    assert p.shard_numel == 0 and p.n_segments == 0
+    p = fs.fs_plan([()], "fp32", 3, False, "fsdp2")       # scalar -> [1]
+    assert p.shard_numel == 1 and p.segments() == [(0, 0, 1, 0, 0)]
+    p = fs.fs_plan([(5,)], "bf16", 1, True, "fsdp1")      # N = 1
+    assert p.shard_numel == 5 and p.segments() == [(0, 0, 5, 0, 0)]
+
+
+def test_call_validation_before_gpu():
+    """Invalid calls fail on the host; n = 0 calls succeed without a launch."""
+    L = fs.lib()
+    p = fs.fs_plan([(3,), (5,)], "bf16", 4, True, "fsdp1")
+    # not uploaded
+    assert L.fs_pack(p._h, ctypes.c_void_p(16), ctypes.c_void_p(16), -1, None) == fs.FS_E_INVAL
+    assert L.fs_unpack(p._h, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == fs.FS_E_INVAL
+    assert L.fs_pack(None, None, None, -1, None) == fs.FS_E_INVAL
+    sl = (ctypes.c_void_p * 2)(16, 32)
+    assert L.fs_reduce_shard(-1, 2, 1, sl, ctypes.c_void_p(64), None) == fs.FS_E_INVAL
+    assert L.fs_reduce_shard(8, 0, 1, sl, ctypes.c_void_p(64), None) == fs.FS_E_INVAL
+    assert L.fs_reduce_shard(8, 2, 0, sl, ctypes.c_void_p(64), None) == fs.FS_E_INVAL
+    assert L.fs_reduce_shard(0, 2, 1, sl, ctypes.c_void_p(64), None) == fs.FS_OK
+    assert L.fs_reduce_shard(8, 2, 1, None, ctypes.c_void_p(64), None) == fs.FS_E_INVAL
+    odd = (ctypes.c_void_p * 2)(17, 32)
+    assert L.fs_reduce_shard(8, 2, 1, odd, ctypes.c_void_p(1 << 20), None) == fs.FS_E_ALIGN
+    assert L.fs_reduce_shard(8, 2, 1, sl, ctypes.c_void_p((1 << 20) + 2), None) == fs.FS_E_ALIGN
+    ov = (ctypes.c_void_p * 2)(1 << 20, 1 << 21)
+    assert L.fs_reduce_shard(8, 2, 1, ov, ctypes.c_void_p((1 << 20) + 8), None) == fs.FS_E_INVAL   # overlap
+    hp = fs.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0, 1)
+    f = ctypes.c_void_p(256)
+    assert L.fs_adamw_step(8, f, f, f, f, 1, None, None, None) == fs.FS_E_INVAL
+    assert L.fs_adamw_step(-1, f, f, f, f, 1, None, ctypes.byref(hp), None) == fs.FS_E_INVAL
+    assert L.fs_adamw_step(8, f, f, f, f, 5, None, ctypes.byref(hp), None) == fs.FS_E_DTYPE
+    assert L.fs_adamw_step(0, f, f, f, f, 1, None, ctypes.byref(hp), None) == fs.FS_OK
+    bad = fs.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0, 0)
+    assert L.fs_adamw_step(8, f, f, f, f, 1, None, ctypes.byref(bad), None) == fs.FS_E_INVAL
+    bad = fs.AdamWHparams(1e-3, 1.0, 0.999, 1e-8, 0.01, 0, 1)
+    assert L.fs_adamw_step(8, f, f, f, f, 1, None, ctypes.byref(bad), None) == fs.FS_E_INVAL
+    assert L.fs_adamw_step(8, ctypes.c_void_p(258), f, f, f, 1, None, ctypes.byref(hp), None) == fs.FS_E_ALIGN
+    assert L.fs_copy_bytes(ctypes.c_void_p(256), ctypes.c_void_p(512), 15, None) == fs.FS_E_INVAL
+    assert L.fs_copy_bytes(ctypes.c_void_p(264), ctypes.c_void_p(512), 16, None) == fs.FS_E_ALIGN

@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: bit-exact for pack, unpack and the reduce (fixed summation order);
+AdamW within 1e-6 relative on fp32 theta/m/v (|d| <= 1e-6 * max(|ref|, |in|)
+for theta, whose value can cross zero) and 1 bf16 ulp on the parameter copy.
+Every output sits in a canary guard band.  Inputs come from the seeded
+counter-based generator (synth.py), never from the HIP path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import Guarded, bits, from_bits, say
+
+pytestmark = pytest.mark.gpu
+
+fs = pytest.importorskip("fsdp_sharded_state_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fs.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_synth_same_bits_on_gpu_and_cpu():
+    idx = torch.tensor([0, 1, 2, 3, 1000, 2 ** 31 + 5, 2 ** 33 + 7, 6_738_411_519], dtype=torch.int64)
+    for fn in (lambda i: synth.bits16_at(5, 1, i), lambda i: synth.bits32_at(5, 2, i),
+               lambda i: synth.normal_f32_at(4, 101, i, 1e-3), lambda i: synth.normal_bf16_at(4, 1, i, 0.02)):
+        a = fn(idx)
+        b = fn(idx.cuda()).cpu()
+        assert torch.equal(a.view(torch.int16) if a.element_size() == 2 else a.view(torch.int32),
+                           b.view(torch.int16) if b.element_size() == 2 else b.view(torch.int32))
+
+
+# ------------------------------------------------------------ pack/unpack --
+
+def _layout_cases():
+    cases = [
+        ("mlp_tiny", "fsdp1", synth.mlp_tiny_shapes(), "bf16", 4, True),
+        ("mlp_tiny_fsdp2", "fsdp2", synth.mlp_tiny_shapes(), "bf16", 4, False),
+        ("worked_example_f1T", "fsdp1", [(3,), (5,)], "bf16", 4, True),
+        ("worked_example_f1F", "fsdp1", [(3,), (5,)], "bf16", 4, False),
+        ("worked_example_f2", "fsdp2", [(3,), (5,)], "bf16", 4, False),
+        ("tiny_mixed_f2_fp32", "fsdp2", [(6, 3), (), (0, 2), (9,), (1, 1), (13, 5)], "fp32", 4, False),
+        ("tiny_mixed_f1F_fp32", "fsdp1", [(1,), (7,), (0,), (3, 3), (2,), (17,)], "fp32", 3, False),
+        ("tiny_mixed_f1T", "fsdp1", [(1,), (7,), (0,), (3, 3), (2,), (17,)], "bf16", 5, True),
+        ("single_N1", "fsdp1", [(100003,)], "bf16", 1, True),
+        ("many_tiles_ragged", "fsdp2", [(1000, 37), (999,), (31, 3)], "bf16", 7, False),
+        ("many_segments_per_tile", "fsdp1", [(k % 5 + 1,) for k in range(700)], "bf16", 8, False),
+        ("many_segments_fsdp2", "fsdp2", [(k % 9 + 1, 2) for k in range(400)], "fp32", 8, False),
+    ]
+    st = [(n,) for n in synth.padding_stress_numels()]
+    for dt in ("bf16", "fp32"):
+        for uo in (True, False):
+            cases.append((f"padding_stress_{dt}_{'T' if uo else 'F'}", "fsdp1", st, dt, 8, uo))
+    cases.append(("llama_block_fsdp2", "fsdp2", synth.llama_block_shapes(), "bf16", 8, False))
+    return cases
+
+
+def _olayout(mode, shapes, dt, N, uo):
+    eb = 2 if dt == "bf16" else 4
+    return oracle.fsdp1_layout(shapes, eb, N, uo) if mode == "fsdp1" else oracle.fsdp2_layout(shapes, eb, N)
+
+
+def _params(shapes, dt, seed, shift=0):
+    """Uniform random bit patterns (NaN payloads included) per parameter."""
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = []
+    off = 0
+    for s in shapes:
+        n = int(np.prod(s)) if len(s) else 1
+        g = synth.bits16 if dt == "bf16" else synth.bits32
+        vals = g(seed, synth.STREAM_PARAMS, n, device="cuda", start=off).view(tdt)
+        out.append(Guarded(n, tdt, shift=shift, fill=vals))
+        off += n
+    return out
+
+
+@pytest.mark.parametrize("case", _layout_cases(), ids=lambda c: c[0])
+def test_pack_unpack_bitexact(case):
+    name, mode, shapes, dt, N, uo = case
+    say("pack/unpack", name)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    plan = fs.fs_plan(shapes, dt, N, uo, mode).upload()
+    L = _olayout(mode, shapes, dt, N, uo)
+    params = _params(shapes, dt, seed=17)
+    host = [bits(p.t) for p in params]
+    ref = oracle.pack(L, host)
+
+    G = Guarded(plan.gathered_numel, tdt)
+    fs.fs_pack(plan, [p.t for p in params], G.t)
+    torch.cuda.synchronize()
+    G.check()
+    np.testing.assert_array_equal(bits(G.t), ref)
+
+    for r in sorted({0, N // 2, N - 1}):
+        say("pack rank", name, r)
+        S = Guarded(plan.shard_numel, tdt)
+        fs.fs_pack(plan, [p.t for p in params], S.t, rank=r)
+        torch.cuda.synchronize()
+        S.check()
+        np.testing.assert_array_equal(bits(S.t), ref[r * plan.shard_numel:(r + 1) * plan.shard_numel])
+
+    # unpack from a gathered buffer whose pads hold garbage: pads are never read
+    junk = ref.copy()
+    idx = L.index_map()
+    mask = np.ones(junk.size, bool)
+    mask[idx] = False
+    junk[mask] = 0x7FFF if dt == "bf16" else 0x7FFFFFFF
+    say("unpack", name)
+    src = from_bits(junk, tdt)
+    outs = [Guarded(p.n, tdt) for p in params]
+    fs.fs_unpack(plan, src, [o.t for o in outs])
+    torch.cuda.synchronize()
+    for o, h in zip(outs, host):
+        o.check()
+        np.testing.assert_array_equal(bits(o.t), h)
+
+
+@pytest.mark.parametrize("case", [c for c in _layout_cases() if c[0] in (
+    "mlp_tiny", "worked_example_f1F", "tiny_mixed_f2_fp32", "tiny_mixed_f1T", "many_tiles_ragged",
+    "padding_stress_bf16_F", "many_segments_per_tile")], ids=lambda c: c[0])
+@pytest.mark.parametrize("shift", [1, 3])
+def test_pack_unpack_misaligned_buffers(case, shift):
+    """Parameters and outputs that start off their 16-byte boundary take the
+    realigning (funnel shift / shuffle) and per-element paths."""
+    name, mode, shapes, dt, N, uo = case
+    say("misaligned pack/unpack", name, shift)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    plan = fs.fs_plan(shapes, dt, N, uo, mode).upload()
+    L = _olayout(mode, shapes, dt, N, uo)
+    params = _params(shapes, dt, seed=29, shift=shift)
+    host = [bits(p.t) for p in params]
+    ref = oracle.pack(L, host)
+    G = Guarded(plan.gathered_numel, tdt)
+    fs.fs_pack(plan, [p.t for p in params], G.t)
+    r = N - 1
+    S = Guarded(plan.shard_numel, tdt, shift=shift)
+    fs.fs_pack(plan, [p.t for p in params], S.t, rank=r)
+    src = Guarded(plan.gathered_numel, tdt, shift=shift, fill=from_bits(ref, tdt))
+    outs = [Guarded(p.n, tdt, shift=(shift + i) % 5) for i, p in enumerate(params)]
+    fs.fs_unpack(plan, src.t, [o.t for o in outs])
+    torch.cuda.synchronize()
+    for g in (G, S, *outs):
+        g.check()
+    np.testing.assert_array_equal(bits(G.t), ref)
+    np.testing.assert_array_equal(bits(S.t), ref[r * plan.shard_numel:(r + 1) * plan.shard_numel])
+    for o, h in zip(outs, host):
+        np.testing.assert_array_equal(bits(o.t), h)
+
+
+def test_pack_empty_and_degenerate():
+    say("pack empty/degenerate")
+    p = fs.fs_plan([(0,), (0, 4)], "bf16", 4, False, "fsdp2").upload()
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    fs.fs_pack(p, [torch.empty(0, dtype=torch.bfloat16, device="cuda")] * 2, e)
+    fs.fs_unpack(p, e, [torch.empty(0, dtype=torch.bfloat16, device="cuda")] * 2)
+    # all ranks past the data are pure pads
+    p = fs.fs_plan([(3,)], "bf16", 8, False, "fsdp1").upload()
+    x = Guarded(3, torch.bfloat16, fill=torch.tensor([1.0, 2.0, 3.0], dtype=torch.bfloat16, device="cuda"))
+    for r in range(8):
+        S = Guarded(1, torch.bfloat16)
+        fs.fs_pack(p, [x.t], S.t, rank=r)
+        torch.cuda.synchronize()
+        S.check()
+        assert S.t.item() == (float(r + 1) if r < 3 else 0.0)
+
+
+# ----------------------------------------------------------------- reduce --
+
+def _slices(n, terms, seed, shift=0, sigma=1e-3, specials=False):
+    out = []
+    for t in range(terms):
+        vals = synth.normal_bf16(seed, 100 + t, n, sigma, device="cuda")
+        if specials and n >= 16:
+            sp = torch.tensor([float("nan"), float("inf"), -float("inf"), -0.0, 0.0, 1e-40, -1e-39,
+                               3e38, -3e38, 2.0 ** 24, 1.0, -1.0], dtype=torch.bfloat16, device="cuda")
+            vals[(t * 5) % 4: (t * 5) % 4 + sp.numel()] = sp.roll(t)
+        out.append(Guarded(n, torch.bfloat16, shift=shift, fill=vals))
+    return out
+
+
+REDUCE_CASES = [
+    # (n, world, grad_acc, slice shift, out shift)
+    (1, 1, 1, 0, 0), (7, 2, 1, 0, 0), (8, 8, 1, 0, 0), (9, 3, 1, 0, 0),
+    (1000, 8, 4, 0, 0), (65536 + 3, 8, 4, 0, 0), (4099, 3, 5, 0, 0),
+    (5003, 8, 5, 0, 0),          # 40 terms: two passes
+    (3001, 2, 33, 0, 0),         # 66 terms: three passes
+    (4097, 8, 4, 1, 0), (4097, 8, 4, 3, 1), (4096, 4, 2, 0, 2),   # misaligned slices / out
+    (25_297_920, 8, 1, 0, 0),    # one Llama-7B block shard, 8-buffer average
+]
+
+
+@pytest.mark.parametrize("case", REDUCE_CASES, ids=lambda c: "n%d_N%d_A%d_s%d_o%d" % c)
+def test_reduce_bitexact(case):
+    n, N, A, sh, osh = case
+    say("reduce", case)
+    sl = _slices(n, N * A, seed=n % 97, shift=sh, specials=True)
+    out = Guarded(n, torch.float32, shift=osh)
+    fs.fs_reduce_shard([s.t for s in sl], out.t, N, A)
+    torch.cuda.synchronize()
+    out.check()
+    for s in sl:
+        s.check()
+    ref = oracle.reduce_shard([bits(s.t) for s in sl], N, A)
+    got = bits(out.t)
+    refb = ref.view(np.uint32)
+    nan_ref = np.isnan(ref)
+    np.testing.assert_array_equal(got[~nan_ref], refb[~nan_ref])
+    assert np.isnan(got.view(np.float32)[nan_ref]).all()
+
+
+def test_reduce_linear_model_identity_on_gpu():
+    """The data-parallel identity on the GPU path: dyadic per-rank gradients
+    of a tiny linear model, averaged by the kernel, equal the full-batch
+    gradient; packed through the FSDP1 layout (the oracle carries the same
+    identity as a pin)."""
+    say("reduce linear-model identity")
+    rng = np.random.default_rng(4)
+    N, A, m, D, K = 8, 4, 4, 4, 3
+    B = N * A * m
+    X = rng.integers(-1, 2, size=(B, D))
+    W = rng.integers(-3, 4, size=(D, K))
+    T = rng.integers(-4, 5, size=(B, K))
+    shapes = [(D, K)]
+    plan = fs.fs_plan(shapes, "bf16", N, True, "fsdp1").upload()
+    grads = []
+    for j in range(A):
+        for k in range(N):
+            rows = slice((j * N + k) * m, (j * N + k + 1) * m)
+            g = (X[rows].T @ (X[rows] @ W - T[rows])) / (m * A)
+            gt = torch.tensor(g.reshape(-1), dtype=torch.float32).to(torch.bfloat16).cuda()
+            full = torch.empty(plan.gathered_numel, dtype=torch.bfloat16, device="cuda")
+            fs.fs_pack(plan, [gt], full)
+            grads.append(full)
+    full_grad = (X.T @ (X @ W - T)) / B
+    for r in range(N):
+        c = plan.shard_numel
+        out = torch.empty(c, dtype=torch.float32, device="cuda")
+        fs.fs_reduce_shard([g[r * c:(r + 1) * c] for g in grads], out, N, A)
+        torch.cuda.synchronize()
+        exp = np.zeros(c, np.float32)
+        lo, hi = r * c, min((r + 1) * c, D * K)
+        if hi > lo:
+            exp[:hi - lo] = full_grad.reshape(-1)[lo:hi].astype(np.float32)
+        np.testing.assert_array_equal(out.cpu().numpy(), exp)
+
+
+# ------------------------------------------------------------------ AdamW --
+
+def _adam_inputs(n, seed, step, grad_bf16, shift=0):
+    th = synth.normal_f32(seed, synth.STREAM_MASTER, n, 0.02, device="cuda")
+    if step == 1:
+        m = torch.zeros(n, device="cuda")
+        v = torch.zeros(n, device="cuda")
+    else:
+        m = synth.normal_f32(seed, synth.STREAM_EXP_AVG, n, 1e-3, device="cuda")
+        v = synth.normal_f32(seed, synth.STREAM_EXP_AVG_SQ, n, 1e-3, device="cuda") ** 2
+    g = synth.normal_f32(seed, 100, n, 1e-3, device="cuda")
+    if n > 20:
+        th[:4] = 0.0        # pad-like elements
+        m[:4] = 0.0
+        v[:4] = 0.0
+        g[:4] = 0.0
+    if grad_bf16:
+        g = g.to(torch.bfloat16)
+    G = [Guarded(n, torch.float32, shift=shift, fill=x) for x in (th, m, v)]
+    Gg = Guarded(n, g.dtype, shift=shift, fill=g)
+    P = Guarded(n, torch.bfloat16, shift=shift)
+    return G, Gg, P
+
+
+ADAM_CASES = [
+    # (n, step, grad_bf16, with p16, shift)
+    (1, 1, False, True, 0), (7, 1, False, True, 0), (8, 2, True, True, 0), (1003, 1000, False, True, 0),
+    (1 << 20, 1, False, True, 0), (1 << 20, 1000, True, False, 0), (4101, 7, False, True, 1),
+    (25_297_920, 1000, False, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", ADAM_CASES, ids=lambda c: "n%d_t%d_bf16g%d_p%d_s%d" % c)
+def test_adamw_parity(case):
+    n, step, gbf, with_p16, sh = case
+    say("adamw", case)
+    (T, M, V), Gg, P = _adam_inputs(n, seed=n % 89 + step, step=step, grad_bf16=gbf, shift=sh)
+    th0, m0, v0 = (x.t.cpu().numpy().copy() for x in (T, M, V))
+    g0 = bits(Gg.t) if gbf else Gg.t.cpu().numpy().copy()
+    hp = oracle.AdamWHparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=step)
+    fs.fs_adamw_step(T.t, M.t, V.t, Gg.t, P.t if with_p16 else None, lr=hp.lr, beta1=hp.beta1,
+                     beta2=hp.beta2, eps=hp.eps, weight_decay=hp.weight_decay, step=step)
+    torch.cuda.synchronize()
+    for g in (T, M, V, Gg, P):
+        g.check()
+    rt, rm, rv, rp = oracle.adamw_step(th0, m0, v0, g0, hp)
+    gt, gm, gv = (x.t.cpu().numpy() for x in (T, M, V))
+    assert np.all(np.abs(gt - rt) <= 1e-6 * np.maximum(np.abs(rt), np.abs(th0)))
+    assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm))
+    assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv))
+    if with_p16:
+        gp = bits(P.t).astype(np.int32)
+        assert np.all(np.abs(gp - rp.astype(np.int32)) <= 1)
+    if n > 20:
+        assert (bits(T.t)[:4] == 0).all() and (bits(M.t)[:4] == 0).all() and (bits(V.t)[:4] == 0).all()
+    exact = np.mean((bits(T.t) == rt.view(np.uint32)) & (bits(M.t) == rm.view(np.uint32)) &
+                    (bits(V.t) == rv.view(np.uint32)))
+    say("adamw bit-exact fraction", exact)
