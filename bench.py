@@ -74,8 +74,12 @@ def setup(workload: str, seed: int = 4):
         params.append(ps)
         gathered.append(torch.empty(p.gathered_numel, dtype=torch.bfloat16, device="cuda"))
         outs.append([torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in g])
-    slices = [synth.normal_bf16(seed, synth.stream_grad(j, k, world), S, 1e-3, device="cuda")
-              for j in range(grad_acc) for k in range(world)]
+    log(f"parameters generated in {time.time() - t0:.1f}s")
+    slices = []
+    for j in range(grad_acc):
+        for k in range(world):
+            slices.append(synth.normal_bf16(seed, synth.stream_grad(j, k, world), S, 1e-3, device="cuda"))
+        log(f"gradient slices of micro-step {j} generated ({time.time() - t0:.1f}s)")
     master = synth.normal_f32(seed, synth.STREAM_MASTER, S, 0.02, device="cuda")
     exp_avg = torch.zeros(S, dtype=torch.float32, device="cuda")
     exp_avg_sq = torch.zeros(S, dtype=torch.float32, device="cuda")
@@ -275,7 +279,7 @@ def main():
         "reduce_adamw_GBps": round(ra_gbps, 1),
         "reduce_adamw_frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4),
         "copy_ceiling_GBps": round(ceiling, 1),
-        "roofline": {"bound": "hbm", "kernel": "reduce_kernel", "achieved": round(red_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "reduce_chunk_kernel", "achieved": round(red_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(red_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": alg["reduce"]},
         "cpu_baseline": None,

@@ -143,6 +143,7 @@ class Plan:
         self.info = info
         self.workspace: Optional[torch.Tensor] = None
         self._ptr_cache = {}
+        self.numels = [self.param(i).numel for i in range(info.n_params)]
 
     def close(self):
         """Release the plan's host memory (also done on garbage collection)."""
@@ -187,15 +188,17 @@ class Plan:
         for i, t in enumerate(tensors):
             if t.element_size() != esz:
                 raise ValueError(f"{what}[{i}]: element size {t.element_size()} != plan's {esz}")
-            if t.numel() != self.param(i).numel:
-                raise ValueError(f"{what}[{i}]: numel {t.numel()} != {self.param(i).numel}")
+            if t.numel() != self.numels[i]:
+                raise ValueError(f"{what}[{i}]: numel {t.numel()} != {self.numels[i]}")
             ptrs.append(_dev_ptr(t, f"{what}[{i}]") if t.numel() else 0)
         key = (tuple(ptrs), str(tensors[0].device) if tensors else "")
         tab = self._ptr_cache.get(key)
         if tab is None:
             dev = tensors[0].device if tensors else torch.device("cuda")
             tab = torch.tensor(ptrs or [0], dtype=torch.int64, device=dev)
-            self._ptr_cache = {key: tab}
+            if len(self._ptr_cache) >= 8:          # keep a few pointer sets (pack and unpack sides)
+                self._ptr_cache.pop(next(iter(self._ptr_cache)))
+            self._ptr_cache[key] = tab
         return tab
 
 

@@ -22,8 +22,11 @@
 
 namespace fsi {
 
+#ifndef FS_TILE_BLOCKS_PER_THREAD
+#define FS_TILE_BLOCKS_PER_THREAD 4
+#endif
 constexpr int kThreads = 256;                 // threads per workgroup (4 waves of 64)
-constexpr int kBlocksPerThread = 8;           // 16-byte blocks per thread per tile
+constexpr int kBlocksPerThread = FS_TILE_BLOCKS_PER_THREAD;   // 16-byte blocks per thread per tile
 constexpr int kTileBlocks = kThreads * kBlocksPerThread;
 constexpr int kTileSegs = 256;                // max segments staged in LDS per tile
 
@@ -36,14 +39,16 @@ struct Segment {        // 32 bytes, sorted by vx, non-overlapping, len > 0
 };
 static_assert(sizeof(Segment) == 32, "segment layout");
 
-struct Tile {           // 24 bytes
+struct Tile {           // 40 bytes
     int64_t x_begin;    // virtual element of the tile's first block (multiple of VEC from its grid anchor)
+    int64_t run_src;    // single-run tiles: source element of the tile's first element
+    int64_t run_dst;    // single-run unpack tiles: destination element within parameter run_buf
     int32_t nblk;       // blocks in the tile (1..kTileBlocks)
     int32_t seg_lo;     // first overlapping segment
     int32_t nseg;       // overlapping segments (0..kTileSegs)
-    int32_t pad_;
+    int32_t run_buf;    // >= 0: every block of the tile lies inside one segment (of this buffer)
 };
-static_assert(sizeof(Tile) == 24, "tile layout");
+static_assert(sizeof(Tile) == 40, "tile layout");
 
 struct BufInfo {        // unpack destinations: 16 bytes per parameter
     int64_t vbase;      // virtual element of the parameter's element 0 (multiple of VEC)

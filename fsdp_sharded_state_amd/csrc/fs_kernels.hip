@@ -30,6 +30,7 @@ using fsi::Tile;
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = fsi::kThreads;
 
@@ -238,17 +239,15 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const Segment *__restric
     constexpr int VEC = 16 / W;
     __shared__ TileLds L;
     const Tile t = tiles[blockIdx.x];
-    stage_tile<W>(L, segs, t);
     const int64_t x_end = t.x_begin + (int64_t)t.nblk * VEC;
     char *dst0 = out + (t.x_begin - dst_lo) * W;
     const bool dst_full = t.x_begin >= dst_lo && x_end <= dst_hi &&
                           (reinterpret_cast<uintptr_t>(dst0) & 15) == 0;
-    if (dst_full && t.nseg == 1 && L.vx[0] <= t.x_begin && L.end[0] >= x_end) {
-        const char *src = reinterpret_cast<const char *>(params[L.buf[0]]) +
-                          (L.src[0] + (t.x_begin - L.vx[0])) * W;
-        copy_run(dst0, src, t.nblk);
+    if (dst_full && t.run_buf >= 0) {   // the whole tile is one contiguous run
+        copy_run(dst0, reinterpret_cast<const char *>(params[t.run_buf]) + t.run_src * W, t.nblk);
         return;
     }
+    stage_tile<W>(L, segs, t);
     const PackSrc S{params};
 #pragma unroll 2
     for (int u = 0; u < fsi::kBlocksPerThread; ++u) {
@@ -280,16 +279,14 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const Segment *__restr
     constexpr int VEC = 16 / W;
     __shared__ TileLds L;
     const Tile t = tiles[blockIdx.x];
-    stage_tile<W>(L, segs, t);
-    const int64_t x_end = t.x_begin + (int64_t)t.nblk * VEC;
-    if (t.nseg == 1 && L.vx[0] <= t.x_begin && L.end[0] >= x_end) {
-        const int j = L.buf[0];
-        char *dst0 = reinterpret_cast<char *>(params[j]) + (t.x_begin - bufs[j].vbase) * W;
+    if (t.run_buf >= 0) {   // the whole tile is one contiguous run of parameter run_buf
+        char *dst0 = reinterpret_cast<char *>(params[t.run_buf]) + t.run_dst * W;
         if ((reinterpret_cast<uintptr_t>(dst0) & 15) == 0) {
-            copy_run(dst0, gathered + (L.src[0] + (t.x_begin - L.vx[0])) * W, t.nblk);
+            copy_run(dst0, gathered + t.run_src * W, t.nblk);
             return;
         }
     }
+    stage_tile<W>(L, segs, t);
     const UnpackSrc S{gathered};
 #pragma unroll 2
     for (int u = 0; u < fsi::kBlocksPerThread; ++u) {
@@ -312,13 +309,26 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const Segment *__restr
 
 // ---------------------------------------------------------------- reduce --
 //
-// Lane i owns 8 consecutive elements of the shard: per term it issues one
-// dwordx4 load (8 bf16) and adds the widened values into 8 fp32
-// accumulators, in slice order, so the summation order is exactly the
-// sequential one with no cross-lane traffic; the last pass divides by N and
-// writes two dwordx4 (8 fp32).  More than kTermsPerPass terms are split into
-// passes that carry the fp32 partial sum through `out`, which is the same
-// arithmetic as one pass.
+// Every output element is the sum of its A*N terms added in fp32 in slice
+// order, then one division by N.  Each lane owns whole elements, so the order
+// is exactly the sequential one with no cross-lane traffic.
+//
+// Main kernel (16-byte-aligned slices and output): a workgroup owns a chunk
+// of kThreads*4*kRedGroups elements and walks the slices one after another,
+// reading kRedGroups groups of 4 bf16 (8 bytes) per lane from the current
+// slice -- 16 KB contiguous per slice per workgroup -- while the next slice's
+// loads are already in flight (two register slots).  The 4*kRedGroups fp32
+// accumulators live in registers; the chunk is written once, 16 bytes per
+// lane, every store instruction covering 1 KB contiguous.  Reading each
+// slice in long contiguous runs keeps the HBM row buffers busy on one stream
+// at a time, which measured faster than interleaving all slices per element.
+//
+// General kernel (misaligned slices or output, and the chunk remainder):
+// lane i owns 8 consecutive elements, one 16-byte (funnel-shifted when
+// misaligned) load per term, plus an element-wise tail.
+//
+// More than kTermsPerPass terms run as chained passes that carry the fp32
+// partial sum through `out` -- the same arithmetic as one pass.
 
 constexpr int kTermsPerPass = 32;
 
@@ -416,6 +426,72 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nter
     }
 }
 
+constexpr int kRedGroups = 16;
+constexpr int64_t kRedChunk = (int64_t)kThreads * 4 * kRedGroups;   // 16384 elements
+
+__device__ __forceinline__ void add_bf16x4(float *acc, u32x2 v) {
+    acc[0] = acc[0] + __uint_as_float(v.x << 16);
+    acc[1] = acc[1] + __uint_as_float(v.x & 0xFFFF0000u);
+    acc[2] = acc[2] + __uint_as_float(v.y << 16);
+    acc[3] = acc[3] + __uint_as_float(v.y & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ void load_groups(u32x2 (&x)[kRedGroups], const uint16_t *p, int64_t base) {
+#pragma unroll
+    for (int u = 0; u < kRedGroups; ++u)
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
+}
+
+__global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
+                                                                int last_pass, float world,
+                                                                float *__restrict__ out) {
+    const int64_t base = (int64_t)blockIdx.x * kRedChunk + 4 * threadIdx.x;
+    float acc[4 * kRedGroups];
+    u32x2 xa[kRedGroups], xb[kRedGroups];
+    int t = 0;
+    if (first_pass) {
+        load_groups(xa, sa.p[0], base);
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) {
+            acc[4 * u] = __uint_as_float(xa[u].x << 16);
+            acc[4 * u + 1] = __uint_as_float(xa[u].x & 0xFFFF0000u);
+            acc[4 * u + 2] = __uint_as_float(xa[u].y << 16);
+            acc[4 * u + 3] = __uint_as_float(xa[u].y & 0xFFFF0000u);
+        }
+        t = 1;
+    } else {
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) {
+            const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(out + base + u * kThreads * 4));
+            acc[4 * u] = __uint_as_float(o.x);
+            acc[4 * u + 1] = __uint_as_float(o.y);
+            acc[4 * u + 2] = __uint_as_float(o.z);
+            acc[4 * u + 3] = __uint_as_float(o.w);
+        }
+    }
+    // two-slot pipeline: slice t is added while slice t+1 is loading
+    if (t < nterms) load_groups(xa, sa.p[t], base);
+    while (t < nterms) {
+        if (t + 1 < nterms) load_groups(xb, sa.p[t + 1], base);
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xa[u]);
+        if (++t >= nterms) break;
+        if (t + 1 < nterms) load_groups(xa, sa.p[t + 1], base);
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xb[u]);
+        ++t;
+    }
+    if (last_pass) {
+#pragma unroll
+        for (int e = 0; e < 4 * kRedGroups; ++e) acc[e] = acc[e] / world;
+    }
+#pragma unroll
+    for (int u = 0; u < kRedGroups; ++u)
+        st16(reinterpret_cast<char *>(out + base + u * kThreads * 4),
+             u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
+                   __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])});
+}
+
 // ----------------------------------------------------------------- AdamW --
 //
 // One fused read-modify-write pass: read g, theta, m, v; write theta, m, v
@@ -458,52 +534,51 @@ __device__ __forceinline__ u32x4 u4(const float o[4]) {
     return u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
 }
 
+// Main AdamW kernel (all buffers 16-byte aligned): a wave owns 64*4*kAdamGroups
+// consecutive elements; lane l holds groups of 4 at offsets q*256 + 4l, so
+// every load and store instruction of the wave covers 1 KB (fp32) or 512 B
+// (bf16) contiguous -- no instruction leaves holes in a cache line.
+constexpr int kAdamGroups = 4;
+constexpr int64_t kAdamChunk = (int64_t)kThreads * 4 * kAdamGroups;   // 4096 elements per workgroup
+
 template <bool GRAD_BF16, bool HAS_P16>
-__global__ __launch_bounds__(kThreads) void adamw_vec_kernel(int64_t nvec, float *__restrict__ th,
-                                                             float *__restrict__ m,
-                                                             float *__restrict__ v,
-                                                             const void *__restrict__ grad,
-                                                             uint16_t *__restrict__ p16,
-                                                             AdamConsts c) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= nvec) return;
-    char *pt = reinterpret_cast<char *>(th + 8 * i);
-    char *pm = reinterpret_cast<char *>(m + 8 * i);
-    char *pv = reinterpret_cast<char *>(v + 8 * i);
-    float G[8], T[8], M[8], V[8];
-    if (GRAD_BF16) {
-        const u32x4 gb = ld16(reinterpret_cast<const char *>(grad) + 16 * i);
-        const uint32_t w[4] = {gb.x, gb.y, gb.z, gb.w};
+__global__ __launch_bounds__(kThreads) void adamw_wave_kernel(float *__restrict__ th, float *__restrict__ m,
+                                                              float *__restrict__ v,
+                                                              const void *__restrict__ grad,
+                                                              uint16_t *__restrict__ p16, AdamConsts c) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t base = (int64_t)blockIdx.x * kAdamChunk + (int64_t)wave * 256 * kAdamGroups + 4 * lane;
+    float G[4 * kAdamGroups], T[4 * kAdamGroups], M[4 * kAdamGroups], V[4 * kAdamGroups];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            G[2 * k] = __uint_as_float(w[k] << 16);
-            G[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    for (int q = 0; q < kAdamGroups; ++q) {
+        const int64_t e = base + q * 256;
+        if (GRAD_BF16) {
+            const u32x2 gb = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(
+                reinterpret_cast<const uint16_t *>(grad) + e));
+            G[4 * q] = __uint_as_float(gb.x << 16);
+            G[4 * q + 1] = __uint_as_float(gb.x & 0xFFFF0000u);
+            G[4 * q + 2] = __uint_as_float(gb.y << 16);
+            G[4 * q + 3] = __uint_as_float(gb.y & 0xFFFF0000u);
+        } else {
+            f4(ld16(reinterpret_cast<const char *>(reinterpret_cast<const float *>(grad) + e)), G + 4 * q);
         }
-    } else {
-        const char *pg = reinterpret_cast<const char *>(grad) + 32 * i;
-        f4(ld16(pg), G);
-        f4(ld16(pg + 16), G + 4);
+        f4(ld16(reinterpret_cast<const char *>(th + e)), T + 4 * q);
+        f4(ld16(reinterpret_cast<const char *>(m + e)), M + 4 * q);
+        f4(ld16(reinterpret_cast<const char *>(v + e)), V + 4 * q);
     }
-    f4(ld16(pt), T);
-    f4(ld16(pt + 16), T + 4);
-    f4(ld16(pm), M);
-    f4(ld16(pm + 16), M + 4);
-    f4(ld16(pv), V);
-    f4(ld16(pv + 16), V + 4);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) adam_elem(c, G[k], T[k], M[k], V[k]);
-    st16(pt, u4(T));
-    st16(pt + 16, u4(T + 4));
-    st16(pm, u4(M));
-    st16(pm + 16, u4(M + 4));
-    st16(pv, u4(V));
-    st16(pv + 16, u4(V + 4));
-    if (HAS_P16) {
-        uint32_t w[4];
+    for (int k = 0; k < 4 * kAdamGroups; ++k) adam_elem(c, G[k], T[k], M[k], V[k]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = (uint32_t)bf16_rne(T[2 * k]) | ((uint32_t)bf16_rne(T[2 * k + 1]) << 16);
-        st16(reinterpret_cast<char *>(p16 + 8 * i), u32x4{w[0], w[1], w[2], w[3]});
+    for (int q = 0; q < kAdamGroups; ++q) {
+        const int64_t e = base + q * 256;
+        st16(reinterpret_cast<char *>(th + e), u4(T + 4 * q));
+        st16(reinterpret_cast<char *>(m + e), u4(M + 4 * q));
+        st16(reinterpret_cast<char *>(v + e), u4(V + 4 * q));
+        if (HAS_P16) {
+            const u32x2 w = {(uint32_t)bf16_rne(T[4 * q]) | ((uint32_t)bf16_rne(T[4 * q + 1]) << 16),
+                             (uint32_t)bf16_rne(T[4 * q + 2]) | ((uint32_t)bf16_rne(T[4 * q + 3]) << 16)};
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p16 + e));
+        }
     }
 }
 
@@ -663,22 +738,33 @@ extern "C" int fs_reduce_shard(int64_t n, int32_t world, int32_t grad_acc, const
         if (ranges_overlap(slices[t], bytes_in, out, bytes_out))
             return fsi::fail(FS_E_INVAL, "fs_reduce_shard: out overlaps slice %d", t);
     }
-    const int64_t nvec = n >> 3;
-    const int64_t grid = std::max<int64_t>(1, (nvec + kThreads - 1) / kThreads);
-    if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large for one launch");
+    const int64_t nchunks = aligned ? n / kRedChunk : 0;
+    const int64_t done = nchunks * kRedChunk;
+    const int64_t rest = n - done;
+    const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
+    if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
+        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large for one launch");
     (void)hipGetLastError();
     for (int t0 = 0; t0 < terms; t0 += kTermsPerPass) {
+        const int cnt = std::min(kTermsPerPass, terms - t0);
+        const int first = t0 == 0, last = t0 + cnt == terms;
         SliceArgs sa;
         memset(&sa, 0, sizeof sa);
-        const int cnt = std::min(kTermsPerPass, terms - t0);
         for (int k = 0; k < cnt; ++k) sa.p[k] = slices[t0 + k];
-        const int first = t0 == 0, last = t0 + cnt == terms;
-        if (aligned)
-            hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, cnt,
-                               first, last, (float)world, n, out);
-        else
-            hipLaunchKernelGGL(reduce_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, cnt,
-                               first, last, (float)world, n, out);
+        if (nchunks > 0)
+            hipLaunchKernelGGL(reduce_chunk_kernel, dim3((uint32_t)nchunks), dim3(kThreads), 0, stream, sa, cnt,
+                               first, last, (float)world, out);
+        if (rest > 0) {   // the chunk remainder, or everything when misaligned
+            SliceArgs sr;   // advanced by `done`, a multiple of 8 elements: alignment is kept
+            memset(&sr, 0, sizeof sr);
+            for (int k = 0; k < cnt; ++k) sr.p[k] = slices[t0 + k] + done;
+            if (aligned)
+                hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
+                                   cnt, first, last, (float)world, rest, out + done);
+            else
+                hipLaunchKernelGGL(reduce_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
+                                   cnt, first, last, (float)world, rest, out + done);
+        }
         int rc = check_launch("fs_reduce_shard");
         if (rc != FS_OK) return rc;
     }
@@ -717,29 +803,26 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
                          !misaligned(grad, 16) && !(param_bf16 && misaligned(param_bf16, 16));
     (void)hipGetLastError();
     int64_t done = 0;
-    if (aligned) {
-        const int64_t nvec = n >> 3;
-        if (nvec > 0) {
-            const int64_t grid = (nvec + kThreads - 1) / kThreads;
-            if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
-            const dim3 g((uint32_t)grid), b(kThreads);
-            if (grad_dtype == FS_BF16) {
-                if (param_bf16)
-                    hipLaunchKernelGGL((adamw_vec_kernel<true, true>), g, b, 0, stream, nvec, master, exp_avg,
-                                       exp_avg_sq, grad, param_bf16, c);
-                else
-                    hipLaunchKernelGGL((adamw_vec_kernel<true, false>), g, b, 0, stream, nvec, master, exp_avg,
-                                       exp_avg_sq, grad, param_bf16, c);
-            } else {
-                if (param_bf16)
-                    hipLaunchKernelGGL((adamw_vec_kernel<false, true>), g, b, 0, stream, nvec, master, exp_avg,
-                                       exp_avg_sq, grad, param_bf16, c);
-                else
-                    hipLaunchKernelGGL((adamw_vec_kernel<false, false>), g, b, 0, stream, nvec, master, exp_avg,
-                                       exp_avg_sq, grad, param_bf16, c);
-            }
-            done = nvec * 8;
+    if (aligned && n >= kAdamChunk) {
+        const int64_t nchunks = n / kAdamChunk;
+        if (nchunks > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
+        const dim3 g((uint32_t)nchunks), b(kThreads);
+        if (grad_dtype == FS_BF16) {
+            if (param_bf16)
+                hipLaunchKernelGGL((adamw_wave_kernel<true, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
+                                   grad, param_bf16, c);
+            else
+                hipLaunchKernelGGL((adamw_wave_kernel<true, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
+                                   grad, param_bf16, c);
+        } else {
+            if (param_bf16)
+                hipLaunchKernelGGL((adamw_wave_kernel<false, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
+                                   grad, param_bf16, c);
+            else
+                hipLaunchKernelGGL((adamw_wave_kernel<false, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
+                                   grad, param_bf16, c);
         }
+        done = nchunks * kAdamChunk;
     }
     if (done < n) {
         const int64_t rest = n - done;

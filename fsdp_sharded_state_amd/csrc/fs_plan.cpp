@@ -97,7 +97,14 @@ void build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int v
         t.nblk = (int32_t)(b1 - b0);
         t.seg_lo = (int32_t)s0;
         t.nseg = (int32_t)(s1 - s0);
-        t.pad_ = 0;
+        t.run_buf = -1;
+        t.run_src = 0;
+        t.run_dst = 0;
+        const int64_t x_full = lo + b1 * vec;   // end of the tile's last block
+        if (t.nseg == 1 && segs[s0].vx <= x0 && segs[s0].vx + segs[s0].len >= x_full) {
+            t.run_buf = segs[s0].buf;
+            t.run_src = segs[s0].src_off + (x0 - segs[s0].vx);
+        }
         out.push_back(t);
         b0 = b1;
     }
@@ -232,6 +239,11 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
             }
         }
 
+        if ((int64_t)ps.size() > INT32_MAX) {
+            delete p;
+            return fsi::fail(FS_E_OVERFLOW, "fs_plan: too many copy segments");
+        }
+
         // ---- unpack view: parameters laid end to end on 16-byte boundaries
         p->bufinfo.resize(n_params);
         int64_t vb = 0;
@@ -254,6 +266,8 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
             p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
         }
         build_tiles(p->unpack_segs, 0, vb, vec, p->unpack_tiles);
+        for (Tile &t : p->unpack_tiles)
+            if (t.run_buf >= 0) t.run_dst = t.x_begin - p->bufinfo[t.run_buf].vbase;
 
         // ---- workspace layout (each table on a 256-byte boundary)
         fsi::WorkspaceLayout &w = p->ws;

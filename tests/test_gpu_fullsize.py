@@ -1,0 +1,135 @@
+"""GPU parity at full size: the 7B model's rank-0 FSDP2 shard (N = 8,
+grad_acc = 4, S = 842,301,440), in the launch configuration the benchmark
+times (one fs_reduce_shard over 32 separate bf16 slices, one fs_adamw_step
+with an fp32 gradient and a bf16 copy, fs_pack with rank -1 and fs_unpack
+per group).
+
+The oracle cannot run the whole shard here, so it computes sampled outputs
+one by one from inputs it regenerates itself (synth is counter-based: element
+i of every buffer is a function of (seed, stream, i)), and the sampled GPU
+outputs must match: bit-exact for the reduce, pack and unpack, within
+tolerance for AdamW.  Samples: random indices, both ends, and every 2^k
+boundary.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import bits, say
+
+pytestmark = pytest.mark.gpu
+fs = pytest.importorskip("fsdp_sharded_state_amd")
+
+SEED = 4
+N, A = 8, 4
+
+
+@pytest.fixture(scope="module")
+def plans():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    groups = synth.llama_model_groups(32, 4096, 11008)
+    ps = [fs.fs_plan(g, "bf16", N, False, "fsdp2", A).upload() for g in groups]
+    yield groups, ps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _sample(n, k, rng):
+    idx = set(rng.integers(0, n, size=k).tolist())
+    idx.update(range(0, min(n, 64)))
+    idx.update(range(max(0, n - 64), n))
+    p = 1
+    while p < n:
+        idx.update(x for x in (p - 1, p) if x < n)
+        p *= 2
+    return np.array(sorted(idx), np.int64)
+
+
+def test_fullsize_reduce_and_adamw(plans):
+    groups, ps = plans
+    S = sum(p.shard_numel for p in ps)
+    assert S == 842_301_440
+    say("full-size reduce: generating 32 slices of", S)
+    slices = [synth.normal_bf16(SEED, synth.stream_grad(j, k, N), S, 1e-3, device="cuda")
+              for j in range(A) for k in range(N)]
+    g32 = torch.empty(S, dtype=torch.float32, device="cuda")
+    say("full-size reduce: launch")
+    fs.fs_reduce_shard(slices, g32, N, A)
+    master = synth.normal_f32(SEED, synth.STREAM_MASTER, S, 0.02, device="cuda")
+    m = torch.zeros(S, device="cuda")
+    v = torch.zeros(S, device="cuda")
+    p16 = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    del slices
+    say("full-size AdamW: launch")
+    fs.fs_adamw_step(master, m, v, g32, p16, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                     weight_decay=0.01, step=1)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(11)
+    idx = _sample(S, 300_000, rng)
+    it = torch.from_numpy(idx)
+    sl_host = [synth.to_numpy_bits(synth.normal_bf16_at(SEED, synth.stream_grad(j, k, N), it, 1e-3))
+               for j in range(A) for k in range(N)]
+    ref_g = oracle.reduce_shard(sl_host, N, A)
+    it_dev = it.cuda()
+    got_g = g32[it_dev].cpu().numpy()
+    np.testing.assert_array_equal(got_g.view(np.uint32), ref_g.view(np.uint32))
+
+    th0 = synth.normal_f32_at(SEED, synth.STREAM_MASTER, it, 0.02).numpy()
+    z = np.zeros(idx.size, np.float32)
+    rt, rm, rv, rp = oracle.adamw_step(th0, z, z, ref_g, oracle.AdamWHparams(step=1))
+    gt = master[it_dev].cpu().numpy()
+    gm = m[it_dev].cpu().numpy()
+    gv = v[it_dev].cpu().numpy()
+    gp = bits(p16[it_dev]).astype(np.int32)
+    assert np.all(np.abs(gt - rt) <= 1e-6 * np.maximum(np.abs(rt), np.abs(th0)))
+    assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm))
+    assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv))
+    assert np.all(np.abs(gp - rp.astype(np.int32)) <= 1)
+    say("full-size AdamW bit-exact fraction",
+        float(np.mean((gt.view(np.uint32) == rt.view(np.uint32)) & (gm.view(np.uint32) == rm.view(np.uint32)))))
+
+
+@pytest.mark.parametrize("which", ["block0", "block31", "root"])
+def test_fullsize_pack_unpack_groups(plans, which):
+    """Pack (all ranks) and unpack of a full-size group; sampled elements of
+    the gathered buffer and of the unpacked parameters against the oracle's
+    layout, and every pad element zero."""
+    groups, ps = plans
+    gi = {"block0": 0, "block31": 31, "root": 32}[which]
+    shapes, plan = groups[gi], ps[gi]
+    off = sum(math.prod(s) for g in groups[:gi] for s in g)   # element offset of the group's parameters
+    say("full-size pack/unpack", which)
+    params, starts = [], []
+    o = off
+    for s in shapes:
+        n = math.prod(s)
+        params.append(synth.bits16(SEED, synth.STREAM_PARAMS, n, device="cuda", start=o).view(torch.bfloat16))
+        starts.append(o)
+        o += n
+    gathered = torch.empty(plan.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    fs.fs_pack(plan, params, gathered)
+    outs = [torch.empty_like(p) for p in params]
+    fs.fs_unpack(plan, gathered, outs)
+    torch.cuda.synchronize()
+
+    L = oracle.fsdp2_layout(shapes, 2, N)
+    rng = np.random.default_rng(gi)
+    for i, (s, st) in enumerate(zip(shapes, starts)):
+        n = math.prod(s)
+        e = _sample(n, 20_000, rng)
+        x = L.index_at(np.full(e.size, i, np.int32), e)
+        expect = synth.to_numpy_bits(synth.bits16_at(SEED, synth.STREAM_PARAMS, torch.from_numpy(e + st)))
+        got = bits(gathered.view(torch.int16)[torch.from_numpy(x).cuda()])
+        np.testing.assert_array_equal(got, expect)
+        got_u = bits(outs[i].view(-1).view(torch.int16)[torch.from_numpy(e).cuda()])
+        np.testing.assert_array_equal(got_u, expect)
+        assert torch.equal(outs[i].view(torch.int16), params[i].view(torch.int16))
+    # every dim 0 of this model is divisible by 8: no pads, the gathered
+    # buffer is all data, and the round trip above covers every element
+    assert plan.tail_pad == 0

@@ -193,7 +193,11 @@ REDUCE_CASES = [
     (1000, 8, 4, 0, 0), (65536 + 3, 8, 4, 0, 0), (4099, 3, 5, 0, 0),
     (5003, 8, 5, 0, 0),          # 40 terms: two passes
     (3001, 2, 33, 0, 0),         # 66 terms: three passes
+    (40000, 8, 5, 0, 0),         # 40 terms over whole 16384-element chunks + remainder
+    (20000 + 7, 2, 33, 0, 0),    # 66 terms, chunks + ragged remainder
+    (16384 * 3, 8, 4, 0, 0),     # whole chunks only
     (4097, 8, 4, 1, 0), (4097, 8, 4, 3, 1), (4096, 4, 2, 0, 2),   # misaligned slices / out
+    (70001, 8, 4, 1, 0),         # misaligned, large
     (25_297_920, 8, 1, 0, 0),    # one Llama-7B block shard, 8-buffer average
 ]
 
@@ -281,6 +285,8 @@ ADAM_CASES = [
     # (n, step, grad_bf16, with p16, shift)
     (1, 1, False, True, 0), (7, 1, False, True, 0), (8, 2, True, True, 0), (1003, 1000, False, True, 0),
     (1 << 20, 1, False, True, 0), (1 << 20, 1000, True, False, 0), (4101, 7, False, True, 1),
+    (4096 * 3 + 5, 3, True, True, 0), (4096, 1, False, False, 0), (4095, 2, False, True, 0),
+    (50003, 9, True, True, 2),
     (25_297_920, 1000, False, True, 0),
 ]
 
