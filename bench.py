@@ -202,7 +202,114 @@ def traffic_for(kernel: str, launch_bytes_alg: float):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+KERNELS = {  # rocprofv3 kernel-name fragment -> bench phase
+    "reduce_chunk_kernel": "reduce",
+    "adamw_wave_kernel": "adamw",
+    "pack_kernel": "pack",
+    "unpack_kernel": "unpack",
+    "copy_kernel": "copy",
+}
+
+
+def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: list, bench_line: str = "",
+                      out_dir: str = os.path.join(ROOT, "profiles")):
+    """Turn rocprofv3 CSV output (kernel trace + stats, and one --pmc pass each
+    for FETCH_SIZE and WRITE_SIZE) into profiles/kernels_7b_shard_step.md and
+    profiles/traffic_7b_shard_step.json.  HBM bytes per launch are the counter
+    values (KiB) scaled by what the same counter reads for the plain copy
+    kernel (bench's copy-ceiling launches: 4 GiB read and 4 GiB written)."""
+    import csv
+    import glob
+
+    def one(d, pat):
+        f = glob.glob(os.path.join(d, "**", pat), recursive=True)
+        if not f:
+            raise SystemExit(f"no {pat} under {d}")
+        return f[0]
+
+    def kname(n):
+        for frag in KERNELS:
+            if "(anonymous namespace)::" + frag + "(" in n or "(anonymous namespace)::" + frag + "<" in n:
+                return frag
+        return None
+
+    stats = {}
+    for r in csv.DictReader(open(one(kt_dir, "*kernel_stats.csv"))):
+        k = kname(r["Name"])
+        if k:
+            stats[k] = {"calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                        "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
+    counters = {}
+    for d, pat in ((fetch_dir, "*counter_collection.csv"), (write_dir, "*counter_collection.csv")):
+        for r in csv.DictReader(open(one(d, pat))):
+            k = kname(r["Kernel_Name"])
+            if k:
+                counters.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in counters.items()}
+    copy_bytes = float(1 << 32)
+    f_fetch = copy_bytes / (avg["copy_kernel"]["FETCH_SIZE"] * 1024)
+    f_write = copy_bytes / (avg["copy_kernel"]["WRITE_SIZE"] * 1024)
+    # algorithmic bytes per launch of the 7B shard step
+    S, N, A = 842301440, 8, 4
+    alg = {"reduce_chunk_kernel": (2 * N * A + 4) * S, "adamw_wave_kernel": 30 * S,
+           "copy_kernel": 2 * copy_bytes}
+    P_blk = 202383360
+    alg["pack_kernel"] = None    # per group; blocks and root differ: reported as totals below
+    alg["unpack_kernel"] = None
+    rec = {"kernel_source_sha256_16": kernel_source_hash(), "fetch_scale": f_fetch, "write_scale": f_write,
+           "kernels": {}}
+    rows = []
+    for k in KERNELS:
+        if k not in avg or k not in stats:
+            continue
+        fe = avg[k].get("FETCH_SIZE", 0.0) * 1024 * f_fetch
+        wr = avg[k].get("WRITE_SIZE", 0.0) * 1024 * f_write
+        hbm = fe + wr
+        a = alg.get(k)
+        ent = {"avg_ns": stats[k]["avg_ns"], "calls": stats[k]["calls"], "fetch_bytes_per_launch": fe,
+               "write_bytes_per_launch": wr, "hbm_bytes_per_launch": hbm}
+        if a:
+            ent["alg_bytes_per_launch"] = a
+            ent["hbm_over_alg"] = hbm / a
+            ent["alg_GBps_from_trace"] = a / stats[k]["avg_ns"]
+        rec["kernels"][KERNELS[k]] = ent
+        rows.append((k, stats[k], fe, wr, a))
+    os.makedirs(out_dir, exist_ok=True)
+    json.dump(rec, open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w"), indent=1)
+    md = ["# Kernel profile: 7B rank-0 FSDP2 shard step (N=8, grad_acc=4)", "",
+          "Produced by these commands (from the repository root, on one MI355X):", ""]
+    md += ["    " + c for c in commands]
+    md += ["", "then `python bench.py --rocprof-summary <trace dir> <FETCH_SIZE dir> <WRITE_SIZE dir>`.", "",
+           f"Counter scale (bytes per counted byte, from the 4 GiB copy kernel): FETCH_SIZE x{f_fetch:.4f}, "
+           f"WRITE_SIZE x{f_write:.4f}.", "",
+           "| kernel | calls | avg duration | HBM read / launch | HBM write / launch | algorithmic / launch | HBM / alg | alg GB/s (trace) |",
+           "|---|---|---|---|---|---|---|---|"]
+    for k, st, fe, wr, a in rows:
+        md.append(f"| {k} | {st['calls']} | {st['avg_ns'] / 1e3:.1f} us | {fe / 1e9:.3f} GB | {wr / 1e9:.3f} GB | "
+                  + (f"{a / 1e9:.3f} GB | {(fe + wr) / a:.3f} | {a / st['avg_ns']:.0f} |" if a else "per group (see below) | - | - |"))
+    if "pack_kernel" in stats:
+        P = 6738411520
+        for k in ("pack_kernel", "unpack_kernel"):
+            tot_alg = (2 * P + 2 * P) / 33
+            md.append("")
+            md.append(f"{k}: mean over the 33 group launches of one step: {stats[k]['avg_ns'] / 1e3:.1f} us, "
+                      f"mean algorithmic bytes per launch {tot_alg / 1e9:.3f} GB "
+                      f"({tot_alg / stats[k]['avg_ns']:.0f} GB/s).")
+    if bench_line:
+        md += ["", "Bench line of the traced run:", "", "    " + bench_line.strip()]
+    open(os.path.join(out_dir, "kernels_7b_shard_step.md"), "w").write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def main():
+    if len(sys.argv) >= 2 and sys.argv[1] == "--rocprof-summary":
+        # --rocprof-summary TRACE_DIR FETCH_DIR WRITE_DIR [COMMANDS_FILE [BENCH_JSON [OUT_DIR]]]
+        kt, fe, wr = sys.argv[2:5]
+        cmds = open(sys.argv[5]).read().strip().splitlines() if len(sys.argv) > 5 else []
+        line = open(sys.argv[6]).read() if len(sys.argv) > 6 else ""
+        out_dir = sys.argv[7] if len(sys.argv) > 7 else os.path.join(ROOT, "profiles")
+        summarize_rocprof(kt, fe, wr, cmds, line, out_dir)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)

@@ -133,3 +133,104 @@ def test_fullsize_pack_unpack_groups(plans, which):
     # every dim 0 of this model is divisible by 8: no pads, the gathered
     # buffer is all data, and the round trip above covers every element
     assert plan.tail_pad == 0
+
+
+# ---------------------------------------------------------------- 70B --
+#
+# The 70B Llama-style model (80 blocks, d 8192, f 28672, k/v 8192x1024, vocab
+# 32000): rank 0's FSDP2 shard holds S = 8,622,080,000 elements, so its fp32
+# master, moments and gradient plus the bf16 copy take 155 GB of HBM.  AdamW
+# runs over the whole shard; the reduce (grad_acc = 2) and pack/unpack run
+# per group, as FSDP issues one reduce-scatter and one all-gather per group,
+# on the first block, the last block and the root group.
+
+N70, A70 = 8, 2
+
+
+@pytest.fixture(scope="module")
+def plans70():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.empty_cache()
+    groups = synth.llama_model_groups(80, 8192, 28672, kv=1024)
+    ps = [fs.fs_plan(g, "bf16", N70, False, "fsdp2", A70).upload() for g in groups]
+    yield groups, ps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_70b_adamw_over_whole_shard(plans70):
+    groups, ps = plans70
+    S = sum(p.shard_numel for p in ps)
+    assert S == 8_622_080_000
+    say("70B AdamW: generating state for", S)
+    master = synth.normal_f32(SEED, synth.STREAM_MASTER, S, 0.02, device="cuda")
+    m = synth.normal_f32(SEED, synth.STREAM_EXP_AVG, S, 1e-3, device="cuda")
+    v = torch.zeros(S, dtype=torch.float32, device="cuda")
+    g32 = synth.normal_f32(SEED, 100, S, 1e-3, device="cuda")
+    p16 = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    say("70B AdamW: launch")
+    fs.fs_adamw_step(master, m, v, g32, p16, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                     weight_decay=0.01, step=7)
+    torch.cuda.synchronize()
+    idx = _sample(S, 300_000, np.random.default_rng(70))
+    it = torch.from_numpy(idx)
+    th0 = synth.normal_f32_at(SEED, synth.STREAM_MASTER, it, 0.02).numpy()
+    m0 = synth.normal_f32_at(SEED, synth.STREAM_EXP_AVG, it, 1e-3).numpy()
+    g0 = synth.normal_f32_at(SEED, 100, it, 1e-3).numpy()
+    rt, rm, rv, rp = oracle.adamw_step(th0, m0, np.zeros_like(m0), g0, oracle.AdamWHparams(step=7))
+    itd = it.cuda()
+    gt, gm, gv = (x[itd].cpu().numpy() for x in (master, m, v))
+    assert np.all(np.abs(gt - rt) <= 1e-6 * np.maximum(np.abs(rt), np.abs(th0)))
+    assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm))
+    assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv))
+    assert np.all(np.abs(bits(p16[itd]).astype(np.int32) - rp.astype(np.int32)) <= 1)
+    del master, m, v, g32, p16
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("which", ["block0", "block79", "root"])
+def test_fullsize_70b_group_reduce_pack_unpack(plans70, which):
+    groups, ps = plans70
+    gi = {"block0": 0, "block79": 79, "root": 80}[which]
+    shapes, plan = groups[gi], ps[gi]
+    shard_off = sum(p.shard_numel for p in ps[:gi])
+    n = plan.shard_numel
+    say("70B group reduce", which, n)
+    slices = [synth.normal_bf16(SEED, synth.stream_grad(j, k, N70), n, 1e-3, device="cuda", start=shard_off)
+              for j in range(A70) for k in range(N70)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    fs.fs_reduce_shard(slices, out, N70, A70)
+    torch.cuda.synchronize()
+    del slices
+    idx = _sample(n, 100_000, np.random.default_rng(gi))
+    it = torch.from_numpy(idx)
+    sl_host = [synth.to_numpy_bits(synth.normal_bf16_at(SEED, synth.stream_grad(j, k, N70), it + shard_off, 1e-3))
+               for j in range(A70) for k in range(N70)]
+    ref = oracle.reduce_shard(sl_host, N70, A70)
+    np.testing.assert_array_equal(out[it.cuda()].cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    del out
+
+    say("70B group pack/unpack", which)
+    off = sum(math.prod(s) for g in groups[:gi] for s in g)
+    params, starts, o = [], [], off
+    for s in shapes:
+        k = math.prod(s)
+        params.append(synth.bits16(SEED, synth.STREAM_PARAMS, k, device="cuda", start=o).view(torch.bfloat16))
+        starts.append(o)
+        o += k
+    gathered = torch.empty(plan.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    fs.fs_pack(plan, params, gathered)
+    outs = [torch.empty_like(p) for p in params]
+    fs.fs_unpack(plan, gathered, outs)
+    torch.cuda.synchronize()
+    L = oracle.fsdp2_layout(shapes, 2, N70)
+    rng = np.random.default_rng(gi + 1)
+    for i, (s, st) in enumerate(zip(shapes, starts)):
+        e = _sample(math.prod(s), 20_000, rng)
+        x = L.index_at(np.full(e.size, i, np.int32), e)
+        expect = synth.to_numpy_bits(synth.bits16_at(SEED, synth.STREAM_PARAMS, torch.from_numpy(e + st)))
+        np.testing.assert_array_equal(bits(gathered.view(torch.int16)[torch.from_numpy(x).cuda()]), expect)
+        assert torch.equal(outs[i].view(torch.int16), params[i].view(torch.int16))
+    del params, outs, gathered
+    torch.cuda.empty_cache()
