@@ -204,6 +204,7 @@ def traffic_for(kernel: str, launch_bytes_alg: float):
 
 KERNELS = {  # rocprofv3 kernel-name fragment -> bench phase
     "reduce_chunk_kernel": "reduce",
+    "reduce_adamw_chunk_kernel": "reduce_adamw_fused",
     "adamw_wave_kernel": "adamw",
     "pack_kernel": "pack",
     "unpack_kernel": "unpack",
@@ -252,6 +253,7 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     # algorithmic bytes per launch of the 7B shard step
     S, N, A = 842301440, 8, 4
     alg = {"reduce_chunk_kernel": (2 * N * A + 4) * S, "adamw_wave_kernel": 30 * S,
+           "reduce_adamw_chunk_kernel": (2 * N * A + 26) * S,
            "copy_kernel": 2 * copy_bytes}
     P_blk = 202383360
     alg["pack_kernel"] = None    # per group; blocks and root differ: reported as totals below
@@ -357,8 +359,25 @@ def main():
     ra_gbps = (alg["reduce"] + alg["adamw"]) / (ra_ms * 1e-3) / 1e9
     kern["reduce_adamw"] = {"ms": round(ra_ms, 4), "GBps": round(ra_gbps, 1),
                             "frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4)}
+    # the fused reduce + AdamW entry point on the same shard (timed separately;
+    # the headline step above is the two-kernel path)
+    fz = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        fz[k][0].record()
+        fs.fs_reduce_adamw_step(W["slices"], W["master"], W["exp_avg"], W["exp_avg_sq"], W["p16"], None,
+                                world=W["world"], grad_acc=W["grad_acc"], lr=1e-3, beta1=0.9, beta2=0.999,
+                                eps=1e-8, weight_decay=0.01, step=t)
+        fz[k][1].record()
+        t += 1
+    torch.cuda.synchronize()
+    fused_ms = sum(e[0].elapsed_time(e[1]) for e in fz) / args.steps
+    fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
     ceiling = copy_ceiling(fs)
 
+    kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
+                                  "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                  "step_ms_with_fused": round(ms["pack"] + ms["unpack"] + fused_ms, 4)}
     red_gbps = alg["reduce"] / (ms["reduce"] * 1e-3) / 1e9
     traffic = traffic_for("reduce", alg["reduce"])
     out = {

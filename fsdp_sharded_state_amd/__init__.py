@@ -87,11 +87,13 @@ def lib() -> ctypes.CDLL:
     L.fs_unpack.argtypes = [vp, vp, vp, vp]
     L.fs_reduce_shard.argtypes = [i64, i32, i32, vp, vp, vp]
     L.fs_adamw_step.argtypes = [i64, vp, vp, vp, vp, i32, vp, ctypes.POINTER(AdamWHparams), vp]
+    L.fs_reduce_adamw_step.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamWHparams), vp]
     L.fs_copy_bytes.argtypes = [vp, vp, i64, vp]
     L.fs_last_error.argtypes = []
     L.fs_last_error.restype = ctypes.c_char_p
     for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
-                 "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_copy_bytes"):
+                 "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_reduce_adamw_step",
+                 "fs_copy_bytes"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -269,6 +271,38 @@ def fs_adamw_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch
                                ptr(grad, "grad"), FS_BF16 if grad.dtype == torch.bfloat16 else FS_FP32,
                                ptr(param_bf16, "param_bf16") if param_bf16 is not None else None,
                                ctypes.byref(hp), _stream(stream)))
+
+
+def fs_reduce_adamw_step(slices: Sequence[torch.Tensor], master: torch.Tensor, exp_avg: torch.Tensor,
+                         exp_avg_sq: torch.Tensor, param_bf16: Optional[torch.Tensor] = None,
+                         grad_out: Optional[torch.Tensor] = None, *, world: int, grad_acc: int = 1,
+                         lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                         weight_decay: float = 0.01, step: int = 1, stream=None):
+    """Fused reduce + AdamW: average slices[j*world + k] (bf16) and apply one
+    AdamW step to the fp32 shard in place; the averaged gradient goes to
+    grad_out only if given."""
+    n = master.numel()
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if t.dtype != torch.float32 or t.numel() != n:
+            raise ValueError(f"fs_reduce_adamw_step: {name} must be float32 with {n} elements")
+    if len(slices) != world * grad_acc:
+        raise ValueError(f"fs_reduce_adamw_step: need world*grad_acc = {world * grad_acc} slices")
+    ptrs = []
+    for k, s in enumerate(slices):
+        if s.dtype != torch.bfloat16 or s.numel() != n:
+            raise ValueError(f"fs_reduce_adamw_step: slice {k} must be bf16 with {n} elements")
+        ptrs.append(_dev_ptr(s, f"slices[{k}]") if n else 0)
+    if param_bf16 is not None and (param_bf16.dtype != torch.bfloat16 or param_bf16.numel() != n):
+        raise ValueError("fs_reduce_adamw_step: param_bf16 must be bfloat16 with n elements")
+    if grad_out is not None and (grad_out.dtype != torch.float32 or grad_out.numel() != n):
+        raise ValueError("fs_reduce_adamw_step: grad_out must be float32 with n elements")
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    hp = AdamWHparams(lr, beta1, beta2, eps, weight_decay, 0, int(step))
+    ptr = (lambda t, w: (_dev_ptr(t, w) if n else 0) if t is not None else None)
+    _check(lib().fs_reduce_adamw_step(n, int(world), int(grad_acc), arr, ptr(master, "master"),
+                                      ptr(exp_avg, "exp_avg"), ptr(exp_avg_sq, "exp_avg_sq"),
+                                      ptr(param_bf16, "param_bf16"), ptr(grad_out, "grad_out"),
+                                      ctypes.byref(hp), _stream(stream)))
 
 
 def fs_copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None):

@@ -599,6 +599,147 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t begin, i
     if (p16) p16[e] = bf16_rne(T);
 }
 
+// ------------------------------------------------------- fused reduce+AdamW --
+//
+// The reduce's fp32 gradient feeds AdamW directly: per element, the A*N terms
+// are summed in slice order and divided by N exactly as in fs_reduce_shard,
+// and that fp32 value is the gradient of the same double-precision update as
+// fs_adamw_step -- so theta, m, v and the bf16 copy are bit-identical to the
+// two-kernel path, while the gradient shard is never written and re-read
+// (unless the caller asks for it).  Traffic per element: 2*A*N + 26 bytes
+// instead of 2*A*N + 4 + 30.
+
+template <bool HAS_P16, bool HAS_G>
+__global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
+                                                                      float world, float *__restrict__ th,
+                                                                      float *__restrict__ m,
+                                                                      float *__restrict__ v,
+                                                                      uint16_t *__restrict__ p16,
+                                                                      float *__restrict__ gout, AdamConsts c) {
+    const int64_t base = (int64_t)blockIdx.x * kRedChunk + 4 * threadIdx.x;
+    float acc[4 * kRedGroups];
+    u32x2 xa[kRedGroups], xb[kRedGroups];
+    int t = 0;
+    if (first_pass) {
+        load_groups(xa, sa.p[0], base);
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) {
+            acc[4 * u] = __uint_as_float(xa[u].x << 16);
+            acc[4 * u + 1] = __uint_as_float(xa[u].x & 0xFFFF0000u);
+            acc[4 * u + 2] = __uint_as_float(xa[u].y << 16);
+            acc[4 * u + 3] = __uint_as_float(xa[u].y & 0xFFFF0000u);
+        }
+        t = 1;
+    } else {   // partial sums of the earlier terms, left in gout by the reduce passes
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) {
+            const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(gout + base + u * kThreads * 4));
+            acc[4 * u] = __uint_as_float(o.x);
+            acc[4 * u + 1] = __uint_as_float(o.y);
+            acc[4 * u + 2] = __uint_as_float(o.z);
+            acc[4 * u + 3] = __uint_as_float(o.w);
+        }
+    }
+    if (t < nterms) load_groups(xa, sa.p[t], base);
+    while (t < nterms) {
+        if (t + 1 < nterms) load_groups(xb, sa.p[t + 1], base);
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xa[u]);
+        if (++t >= nterms) break;
+        if (t + 1 < nterms) load_groups(xa, sa.p[t + 1], base);
+#pragma unroll
+        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xb[u]);
+        ++t;
+    }
+#pragma unroll
+    for (int e = 0; e < 4 * kRedGroups; ++e) acc[e] = acc[e] / world;
+    // AdamW on the lane's 16 groups, four groups (16 elements) at a time
+#pragma unroll
+    for (int u0 = 0; u0 < kRedGroups; u0 += 4) {
+        float T[16], M[16], V[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = base + (u0 + q) * kThreads * 4;
+            f4(ld16(reinterpret_cast<const char *>(th + e)), T + 4 * q);
+            f4(ld16(reinterpret_cast<const char *>(m + e)), M + 4 * q);
+            f4(ld16(reinterpret_cast<const char *>(v + e)), V + 4 * q);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) adam_elem(c, acc[4 * u0 + k], T[k], M[k], V[k]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = base + (u0 + q) * kThreads * 4;
+            st16(reinterpret_cast<char *>(th + e), u4(T + 4 * q));
+            st16(reinterpret_cast<char *>(m + e), u4(M + 4 * q));
+            st16(reinterpret_cast<char *>(v + e), u4(V + 4 * q));
+            if (HAS_P16) {
+                const u32x2 w = {(uint32_t)bf16_rne(T[4 * q]) | ((uint32_t)bf16_rne(T[4 * q + 1]) << 16),
+                                 (uint32_t)bf16_rne(T[4 * q + 2]) | ((uint32_t)bf16_rne(T[4 * q + 3]) << 16)};
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p16 + e));
+            }
+            if (HAS_G) st16(reinterpret_cast<char *>(gout + e), u4(acc + 4 * (u0 + q)));
+        }
+    }
+}
+
+// Remainder / misaligned variant: lane i owns 8 consecutive elements (the
+// general reduce's loads), then updates them element by element; the last
+// n % 8 elements go one per lane of the first wave.
+template <bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArgs sa, int nterms, int first_pass,
+                                                                        float world, int64_t n, float *th,
+                                                                        float *m, float *v, uint16_t *p16,
+                                                                        float *gout, AdamConsts c) {
+    const int64_t nvec = n >> 3;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < nvec) {
+        const int64_t off = i * 16;
+        float acc[8];
+        int t = 0;
+        if (first_pass) {
+            set_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[0], off));
+            t = 1;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = gout[8 * i + e];
+        }
+        for (; t < nterms; ++t) add_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[t], off));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = 8 * i + e;
+            const float g = acc[e] / world;
+            float T = th[k], M = m[k], V = v[k];
+            adam_elem(c, g, T, M, V);
+            th[k] = T;
+            m[k] = M;
+            v[k] = V;
+            if (p16) p16[k] = bf16_rne(T);
+            if (gout) gout[k] = g;
+        }
+    }
+    const int64_t tail = n - nvec * 8;
+    if (blockIdx.x == 0 && (int64_t)threadIdx.x < tail) {
+        const int64_t k = nvec * 8 + threadIdx.x;
+        float acc;
+        int t = 0;
+        if (first_pass) {
+            acc = __uint_as_float((uint32_t)sa.p[0][k] << 16);
+            t = 1;
+        } else {
+            acc = gout[k];
+        }
+        for (; t < nterms; ++t) acc = acc + __uint_as_float((uint32_t)sa.p[t][k] << 16);
+        const float g = acc / world;
+        float T = th[k], M = m[k], V = v[k];
+        adam_elem(c, g, T, M, V);
+        th[k] = T;
+        m[k] = M;
+        v[k] = V;
+        if (p16) p16[k] = bf16_rne(T);
+        if (gout) gout[k] = g;
+    }
+}
+
 // ------------------------------------------------------------------ copy --
 
 __global__ __launch_bounds__(kThreads) void copy_kernel(char *__restrict__ dst,
@@ -608,6 +749,30 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(char *__restrict__ dst,
 }
 
 // -------------------------------------------------------------- launchers --
+
+// Per-step AdamW scalars, in double from the fp32 hyperparameters: the bias
+// corrections 1 - beta^t and the decoupled decay factor 1 - lr*wd.
+AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
+    AdamConsts c;
+    c.b1 = hp.beta1;
+    c.b2 = hp.beta2;
+    c.omb1 = 1.0 - c.b1;
+    c.omb2 = 1.0 - c.b2;
+    c.bc1 = 1.0 - pow(c.b1, (double)hp.step);
+    c.bc2 = 1.0 - pow(c.b2, (double)hp.step);
+    c.lr = hp.lr;
+    c.eps = hp.eps;
+    c.decay = 1.0 - (double)hp.lr * (double)hp.weight_decay;
+    return c;
+}
+
+int check_hparams(const char *what, const fs_adamw_hparams_t *hp) {
+    if (!hp) return fsi::fail(FS_E_INVAL, "%s: hp is NULL", what);
+    if (hp->step < 1) return fsi::fail(FS_E_INVAL, "%s: step must be >= 1", what);
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f && hp->beta2 >= 0.f && hp->beta2 < 1.f))
+        return fsi::fail(FS_E_INVAL, "%s: betas must lie in [0, 1)", what);
+    return FS_OK;
+}
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -776,11 +941,8 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
                              hipStream_t stream) {
     fsi::clear_error();
     if (n < 0) return fsi::fail(FS_E_INVAL, "fs_adamw_step: n < 0");
-    if (!hp) return fsi::fail(FS_E_INVAL, "fs_adamw_step: hp is NULL");
+    if (int rc = check_hparams("fs_adamw_step", hp)) return rc;
     if (grad_dtype != FS_BF16 && grad_dtype != FS_FP32) return fsi::fail(FS_E_DTYPE, "fs_adamw_step: unknown grad dtype");
-    if (hp->step < 1) return fsi::fail(FS_E_INVAL, "fs_adamw_step: step must be >= 1");
-    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f && hp->beta2 >= 0.f && hp->beta2 < 1.f))
-        return fsi::fail(FS_E_INVAL, "fs_adamw_step: betas must lie in [0, 1)");
     int64_t nb;
     if (__builtin_mul_overflow(n, (int64_t)4, &nb)) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large");
     if (n == 0) return FS_OK;
@@ -789,16 +951,7 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
     if (misaligned(master, 4) || misaligned(exp_avg, 4) || misaligned(exp_avg_sq, 4) || misaligned(grad, gb) ||
         (param_bf16 && misaligned(param_bf16, 2)))
         return fsi::fail(FS_E_ALIGN, "fs_adamw_step: pointer not aligned to its element size");
-    AdamConsts c;
-    c.b1 = hp->beta1;
-    c.b2 = hp->beta2;
-    c.omb1 = 1.0 - c.b1;
-    c.omb2 = 1.0 - c.b2;
-    c.bc1 = 1.0 - pow(c.b1, (double)hp->step);
-    c.bc2 = 1.0 - pow(c.b2, (double)hp->step);
-    c.lr = hp->lr;
-    c.eps = hp->eps;
-    c.decay = 1.0 - (double)hp->lr * (double)hp->weight_decay;
+    const AdamConsts c = adam_consts(*hp);
     const bool aligned = !misaligned(master, 16) && !misaligned(exp_avg, 16) && !misaligned(exp_avg_sq, 16) &&
                          !misaligned(grad, 16) && !(param_bf16 && misaligned(param_bf16, 16));
     (void)hipGetLastError();
@@ -832,6 +985,110 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
                            exp_avg, exp_avg_sq, grad, (int)(grad_dtype == FS_BF16), param_bf16, c);
     }
     return check_launch("fs_adamw_step");
+}
+
+extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, const uint16_t *const *slices,
+                                    float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_bf16,
+                                    float *grad_out, const fs_adamw_hparams_t *hp, hipStream_t stream) {
+    fsi::clear_error();
+    if (n < 0) return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: n < 0");
+    if (world < 1 || grad_acc < 1)
+        return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: world and grad_acc must be >= 1");
+    if (int rc = check_hparams("fs_reduce_adamw_step", hp)) return rc;
+    int64_t terms64, bytes_in, bytes_out;
+    if (__builtin_mul_overflow((int64_t)world, (int64_t)grad_acc, &terms64) || terms64 > (1 << 20))
+        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: too many terms");
+    if (__builtin_mul_overflow(n, (int64_t)2, &bytes_in) || __builtin_mul_overflow(n, (int64_t)4, &bytes_out))
+        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: n too large");
+    if (n == 0) return FS_OK;
+    const int terms = (int)terms64;
+    if (!slices || !master || !exp_avg || !exp_avg_sq)
+        return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: NULL pointer");
+    if (terms > kTermsPerPass && !grad_out)
+        return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: more than %d terms need grad_out for the partial sums",
+                         kTermsPerPass);
+    if (misaligned(master, 4) || misaligned(exp_avg, 4) || misaligned(exp_avg_sq, 4) ||
+        (grad_out && misaligned(grad_out, 4)) || (param_bf16 && misaligned(param_bf16, 2)))
+        return fsi::fail(FS_E_ALIGN, "fs_reduce_adamw_step: pointer not aligned to its element size");
+    bool aligned = !misaligned(master, 16) && !misaligned(exp_avg, 16) && !misaligned(exp_avg_sq, 16) &&
+                   !(grad_out && misaligned(grad_out, 16)) && !(param_bf16 && misaligned(param_bf16, 16));
+    const void *outs[5] = {master, exp_avg, exp_avg_sq, grad_out, param_bf16};
+    const int64_t out_bytes[5] = {bytes_out, bytes_out, bytes_out, grad_out ? bytes_out : 0,
+                                  param_bf16 ? bytes_in : 0};
+    for (int t = 0; t < terms; ++t) {
+        if (!slices[t]) return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: slice %d is NULL", t);
+        if (misaligned(slices[t], 2))
+            return fsi::fail(FS_E_ALIGN, "fs_reduce_adamw_step: slice %d not 2-byte aligned", t);
+        if (misaligned(slices[t], 16)) aligned = false;
+        for (int o = 0; o < 5; ++o)
+            if (ranges_overlap(slices[t], bytes_in, outs[o], out_bytes[o]))
+                return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: an output overlaps slice %d", t);
+    }
+    const AdamConsts c = adam_consts(*hp);
+    const int64_t nchunks = aligned ? n / kRedChunk : 0;
+    const int64_t done = nchunks * kRedChunk;
+    const int64_t rest = n - done;
+    const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
+    if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
+        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: n too large for one launch");
+    (void)hipGetLastError();
+    // terms beyond the last kTermsPerPass: plain reduce passes leave partial sums in grad_out
+    const int last_cnt = terms - (terms - 1) / kTermsPerPass * kTermsPerPass;
+    const int t_last = terms - last_cnt;
+    for (int t0 = 0; t0 < t_last; t0 += kTermsPerPass) {
+        SliceArgs sa;
+        memset(&sa, 0, sizeof sa);
+        for (int k = 0; k < kTermsPerPass; ++k) sa.p[k] = slices[t0 + k];
+        if (nchunks > 0)
+            hipLaunchKernelGGL(reduce_chunk_kernel, dim3((uint32_t)nchunks), dim3(kThreads), 0, stream, sa,
+                               kTermsPerPass, (int)(t0 == 0), 0, (float)world, grad_out);
+        if (rest > 0) {
+            SliceArgs sr;
+            memset(&sr, 0, sizeof sr);
+            for (int k = 0; k < kTermsPerPass; ++k) sr.p[k] = slices[t0 + k] + done;
+            if (aligned)
+                hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
+                                   kTermsPerPass, (int)(t0 == 0), 0, (float)world, rest, grad_out + done);
+            else
+                hipLaunchKernelGGL(reduce_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
+                                   kTermsPerPass, (int)(t0 == 0), 0, (float)world, rest, grad_out + done);
+        }
+    }
+    SliceArgs sa;
+    memset(&sa, 0, sizeof sa);
+    for (int k = 0; k < last_cnt; ++k) sa.p[k] = slices[t_last + k];
+    const int first = t_last == 0;
+    if (nchunks > 0) {
+        const dim3 g((uint32_t)nchunks), b(kThreads);
+        if (param_bf16 && grad_out)
+            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<true, true>), g, b, 0, stream, sa, last_cnt, first,
+                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
+        else if (param_bf16)
+            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<true, false>), g, b, 0, stream, sa, last_cnt, first,
+                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
+        else if (grad_out)
+            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<false, true>), g, b, 0, stream, sa, last_cnt, first,
+                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
+        else
+            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<false, false>), g, b, 0, stream, sa, last_cnt, first,
+                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
+    }
+    if (rest > 0) {
+        SliceArgs sr;
+        memset(&sr, 0, sizeof sr);
+        for (int k = 0; k < last_cnt; ++k) sr.p[k] = slices[t_last + k] + done;
+        uint16_t *p16r = param_bf16 ? param_bf16 + done : nullptr;
+        float *gr = grad_out ? grad_out + done : nullptr;
+        if (aligned)
+            hipLaunchKernelGGL(reduce_adamw_general_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
+                               stream, sr, last_cnt, first, (float)world, rest, master + done, exp_avg + done,
+                               exp_avg_sq + done, p16r, gr, c);
+        else
+            hipLaunchKernelGGL(reduce_adamw_general_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
+                               stream, sr, last_cnt, first, (float)world, rest, master + done, exp_avg + done,
+                               exp_avg_sq + done, p16r, gr, c);
+    }
+    return check_launch("fs_reduce_adamw_step");
 }
 
 extern "C" int fs_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t stream) {

@@ -255,6 +255,31 @@ int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *exp_avg_sq,
                   const fs_adamw_hparams_t *hp, hipStream_t stream);
 
 /*
+ * fs_reduce_adamw_step -- the reduce and the AdamW step fused into one pass
+ * over the shard [DPZ section 9.2: the own 1/N fp32 gradient feeds the update
+ * of the own fp32 parameters; KB section 04: optimizer step over the local
+ * shard].  The averaged gradient is not written to memory unless asked for.
+ *
+ *   n, world, grad_acc, slices: as fs_reduce_shard.
+ *   master, exp_avg, exp_avg_sq, param_bf16, hp: as fs_adamw_step (fp32
+ *                  gradient).
+ *   grad_out (device, fp32, n, nullable): also receives the averaged
+ *                  gradient.  Required when world*grad_acc > 32 (it holds
+ *                  the partial sums between passes).
+ * Results: theta, m, v and param_bf16 are bit-identical to fs_reduce_shard
+ * followed by fs_adamw_step(grad_dtype = FS_FP32); grad_out to
+ * fs_reduce_shard's output.  HBM traffic per element: 2*A*N + 26 bytes
+ * (+4 with grad_out) instead of 2*A*N + 34.
+ * Errors: those of fs_reduce_shard and fs_adamw_step; FS_E_INVAL also for an
+ * output overlapping a slice, or more than 32 terms without grad_out.
+ */
+int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc,
+                         const uint16_t *const *slices, float *master,
+                         float *exp_avg, float *exp_avg_sq, uint16_t *param_bf16,
+                         float *grad_out, const fs_adamw_hparams_t *hp,
+                         hipStream_t stream);
+
+/*
  * fs_copy_bytes -- plain streaming copy of `bytes` bytes (dst, src device,
  * both 16-byte aligned, bytes a multiple of 16).  A measurement aid, not
  * part of the method: it gives the practical copy ceiling of the HBM and the

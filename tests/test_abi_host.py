@@ -210,3 +210,23 @@ def test_call_validation_before_gpu():
     assert L.fs_adamw_step(8, ctypes.c_void_p(258), f, f, f, 1, None, ctypes.byref(hp), None) == fs.FS_E_ALIGN
     assert L.fs_copy_bytes(ctypes.c_void_p(256), ctypes.c_void_p(512), 15, None) == fs.FS_E_INVAL
     assert L.fs_copy_bytes(ctypes.c_void_p(264), ctypes.c_void_p(512), 16, None) == fs.FS_E_ALIGN
+
+
+def test_fused_call_validation_before_gpu():
+    L = fs.lib()
+    hp = fs.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0, 1)
+    f = ctypes.c_void_p(1 << 24)
+    sl = (ctypes.c_void_p * 2)(1 << 20, 1 << 21)
+    assert L.fs_reduce_adamw_step(-1, 2, 1, sl, f, f, f, None, None, ctypes.byref(hp), None) == fs.FS_E_INVAL
+    assert L.fs_reduce_adamw_step(8, 0, 1, sl, f, f, f, None, None, ctypes.byref(hp), None) == fs.FS_E_INVAL
+    assert L.fs_reduce_adamw_step(8, 2, 1, sl, f, f, f, None, None, None, None) == fs.FS_E_INVAL
+    assert L.fs_reduce_adamw_step(0, 2, 1, sl, f, f, f, None, None, ctypes.byref(hp), None) == fs.FS_OK
+    big = (ctypes.c_void_p * 40)(*[(1 << 20) * (k + 1) for k in range(40)])
+    assert L.fs_reduce_adamw_step(8, 8, 5, big, ctypes.c_void_p(1 << 30), ctypes.c_void_p(1 << 31),
+                                  ctypes.c_void_p(1 << 32), None, None, ctypes.byref(hp), None) == fs.FS_E_INVAL
+    assert b"grad_out" in L.fs_last_error()
+    assert L.fs_reduce_adamw_step(8, 2, 1, sl, ctypes.c_void_p((1 << 24) + 2), f, f, None, None,
+                                  ctypes.byref(hp), None) == fs.FS_E_ALIGN
+    # an output overlapping a slice
+    assert L.fs_reduce_adamw_step(8, 2, 1, sl, ctypes.c_void_p((1 << 20) + 4), ctypes.c_void_p(1 << 25),
+                                  ctypes.c_void_p(1 << 26), None, None, ctypes.byref(hp), None) == fs.FS_E_INVAL

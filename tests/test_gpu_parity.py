@@ -317,3 +317,60 @@ def test_adamw_parity(case):
     exact = np.mean((bits(T.t) == rt.view(np.uint32)) & (bits(M.t) == rm.view(np.uint32)) &
                     (bits(V.t) == rv.view(np.uint32)))
     say("adamw bit-exact fraction", exact)
+
+
+# ------------------------------------------------------ fused reduce+AdamW --
+
+FUSED_CASES = [
+    # (n, world, grad_acc, slice shift, with p16, with grad_out, step)
+    (1, 1, 1, 0, True, True, 1),
+    (16384 * 3 + 5, 8, 4, 0, True, True, 1),
+    (65536, 8, 4, 0, True, False, 3),
+    (4097, 3, 2, 1, True, True, 2),
+    (40000, 8, 5, 0, True, True, 5),      # 40 terms: partial sums pass through grad_out
+    (20007, 2, 33, 0, False, True, 2),    # 66 terms
+    (25_297_920, 8, 1, 0, True, False, 1000),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "n%d_N%d_A%d_s%d_p%d_g%d_t%d" % c)
+def test_reduce_adamw_fused(case):
+    """Fused path against the oracle (reduce, then AdamW on its fp32 output),
+    and bit-identical to the two-kernel path on the same inputs."""
+    n, N, A, sh, wp, wg, step = case
+    say("fused reduce+adamw", case)
+    sl = _slices(n, N * A, seed=n % 53 + 1, shift=sh)
+    (T, M, V), _, P = _adam_inputs(n, seed=n % 31 + step, step=step, grad_bf16=False)
+    th0, m0, v0 = (x.t.cpu().numpy().copy() for x in (T, M, V))
+    # two-kernel path on copies of the same state
+    T2, M2, V2 = (Guarded(n, torch.float32, fill=x.t.clone()) for x in (T, M, V))
+    P2 = Guarded(n, torch.bfloat16)
+    G2 = Guarded(n, torch.float32)
+    fs.fs_reduce_shard([s.t for s in sl], G2.t, N, A)
+    fs.fs_adamw_step(T2.t, M2.t, V2.t, G2.t, P2.t, step=step)
+    Gout = Guarded(n, torch.float32) if wg else None
+    fs.fs_reduce_adamw_step([s.t for s in sl], T.t, M.t, V.t, P.t if wp else None,
+                            Gout.t if wg else None, world=N, grad_acc=A, step=step)
+    torch.cuda.synchronize()
+    for g in (T, M, V, P, T2, M2, V2, P2, G2) + ((Gout,) if wg else ()):
+        g.check()
+    ref_g = oracle.reduce_shard([bits(s.t) for s in sl], N, A)
+    rt, rm, rv, rp = oracle.adamw_step(th0, m0, v0, ref_g, oracle.AdamWHparams(step=step))
+    gt, gm, gv = (x.t.cpu().numpy() for x in (T, M, V))
+    assert np.all(np.abs(gt - rt) <= 1e-6 * np.maximum(np.abs(rt), np.abs(th0)))
+    assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm))
+    assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv))
+    if wp:
+        assert np.all(np.abs(bits(P.t).astype(np.int32) - rp.astype(np.int32)) <= 1)
+        np.testing.assert_array_equal(bits(P.t), bits(P2.t))
+    if wg:
+        np.testing.assert_array_equal(bits(Gout.t), ref_g.view(np.uint32))
+    for a, b in ((T, T2), (M, M2), (V, V2)):
+        np.testing.assert_array_equal(bits(a.t), bits(b.t))
+
+
+def test_reduce_adamw_fused_needs_grad_out_beyond_32_terms():
+    sl = [torch.zeros(64, dtype=torch.bfloat16, device="cuda") for _ in range(40)]
+    st = [torch.zeros(64, device="cuda") for _ in range(3)]
+    with pytest.raises(fs.FsError, match="grad_out"):
+        fs.fs_reduce_adamw_step(sl, *st, world=8, grad_acc=5)
