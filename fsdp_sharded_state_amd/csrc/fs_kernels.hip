@@ -609,6 +609,23 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t begin, i
 // (unless the caller asks for it).  Traffic per element: 2*A*N + 26 bytes
 // instead of 2*A*N + 4 + 30.
 
+#ifndef FS_FUSED_GROUPS
+#define FS_FUSED_GROUPS 4
+#endif
+#ifndef FS_FUSED_BATCH
+#define FS_FUSED_BATCH 2
+#endif
+constexpr int kFusedGroups = FS_FUSED_GROUPS;
+constexpr int kFusedBatch = FS_FUSED_BATCH < FS_FUSED_GROUPS ? FS_FUSED_BATCH : FS_FUSED_GROUPS;
+constexpr int64_t kFusedChunk = (int64_t)kThreads * 4 * kFusedGroups;
+
+template <int G>
+__device__ __forceinline__ void load_groups_n(u32x2 (&x)[G], const uint16_t *p, int64_t base) {
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
+}
+
 template <bool HAS_P16, bool HAS_G>
 __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
                                                                       float world, float *__restrict__ th,
@@ -616,14 +633,14 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
                                                                       float *__restrict__ v,
                                                                       uint16_t *__restrict__ p16,
                                                                       float *__restrict__ gout, AdamConsts c) {
-    const int64_t base = (int64_t)blockIdx.x * kRedChunk + 4 * threadIdx.x;
-    float acc[4 * kRedGroups];
-    u32x2 xa[kRedGroups], xb[kRedGroups];
+    const int64_t base = (int64_t)blockIdx.x * kFusedChunk + 4 * threadIdx.x;
+    float acc[4 * kFusedGroups];
+    u32x2 xa[kFusedGroups], xb[kFusedGroups];
     int t = 0;
     if (first_pass) {
-        load_groups(xa, sa.p[0], base);
+        load_groups_n<kFusedGroups>(xa, sa.p[0], base);
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) {
+        for (int u = 0; u < kFusedGroups; ++u) {
             acc[4 * u] = __uint_as_float(xa[u].x << 16);
             acc[4 * u + 1] = __uint_as_float(xa[u].x & 0xFFFF0000u);
             acc[4 * u + 2] = __uint_as_float(xa[u].y << 16);
@@ -632,7 +649,7 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
         t = 1;
     } else {   // partial sums of the earlier terms, left in gout by the reduce passes
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) {
+        for (int u = 0; u < kFusedGroups; ++u) {
             const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(gout + base + u * kThreads * 4));
             acc[4 * u] = __uint_as_float(o.x);
             acc[4 * u + 1] = __uint_as_float(o.y);
@@ -640,34 +657,34 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
             acc[4 * u + 3] = __uint_as_float(o.w);
         }
     }
-    if (t < nterms) load_groups(xa, sa.p[t], base);
+    if (t < nterms) load_groups_n<kFusedGroups>(xa, sa.p[t], base);
     while (t < nterms) {
-        if (t + 1 < nterms) load_groups(xb, sa.p[t + 1], base);
+        if (t + 1 < nterms) load_groups_n<kFusedGroups>(xb, sa.p[t + 1], base);
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xa[u]);
+        for (int u = 0; u < kFusedGroups; ++u) add_bf16x4(acc + 4 * u, xa[u]);
         if (++t >= nterms) break;
-        if (t + 1 < nterms) load_groups(xa, sa.p[t + 1], base);
+        if (t + 1 < nterms) load_groups_n<kFusedGroups>(xa, sa.p[t + 1], base);
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xb[u]);
+        for (int u = 0; u < kFusedGroups; ++u) add_bf16x4(acc + 4 * u, xb[u]);
         ++t;
     }
 #pragma unroll
-    for (int e = 0; e < 4 * kRedGroups; ++e) acc[e] = acc[e] / world;
-    // AdamW on the lane's 16 groups, four groups (16 elements) at a time
+    for (int e = 0; e < 4 * kFusedGroups; ++e) acc[e] = acc[e] / world;
+    // AdamW on the lane's groups, kFusedBatch groups (4*kFusedBatch elements) at a time
 #pragma unroll
-    for (int u0 = 0; u0 < kRedGroups; u0 += 4) {
-        float T[16], M[16], V[16];
+    for (int u0 = 0; u0 < kFusedGroups; u0 += kFusedBatch) {
+        float T[4 * kFusedBatch], M[4 * kFusedBatch], V[4 * kFusedBatch];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kFusedBatch; ++q) {
             const int64_t e = base + (u0 + q) * kThreads * 4;
             f4(ld16(reinterpret_cast<const char *>(th + e)), T + 4 * q);
             f4(ld16(reinterpret_cast<const char *>(m + e)), M + 4 * q);
             f4(ld16(reinterpret_cast<const char *>(v + e)), V + 4 * q);
         }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) adam_elem(c, acc[4 * u0 + k], T[k], M[k], V[k]);
+        for (int k = 0; k < 4 * kFusedBatch; ++k) adam_elem(c, acc[4 * u0 + k], T[k], M[k], V[k]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kFusedBatch; ++q) {
             const int64_t e = base + (u0 + q) * kThreads * 4;
             st16(reinterpret_cast<char *>(th + e), u4(T + 4 * q));
             st16(reinterpret_cast<char *>(m + e), u4(M + 4 * q));
@@ -1025,8 +1042,8 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
                 return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: an output overlaps slice %d", t);
     }
     const AdamConsts c = adam_consts(*hp);
-    const int64_t nchunks = aligned ? n / kRedChunk : 0;
-    const int64_t done = nchunks * kRedChunk;
+    const int64_t nchunks = aligned ? n / kFusedChunk : 0;
+    const int64_t done = nchunks * kFusedChunk;
     const int64_t rest = n - done;
     const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
     if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
@@ -1039,9 +1056,19 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
         SliceArgs sa;
         memset(&sa, 0, sizeof sa);
         for (int k = 0; k < kTermsPerPass; ++k) sa.p[k] = slices[t0 + k];
-        if (nchunks > 0)
-            hipLaunchKernelGGL(reduce_chunk_kernel, dim3((uint32_t)nchunks), dim3(kThreads), 0, stream, sa,
+        const int64_t pre_chunks = done / kRedChunk, pre_done = pre_chunks * kRedChunk;
+        if (pre_chunks > 0)
+            hipLaunchKernelGGL(reduce_chunk_kernel, dim3((uint32_t)pre_chunks), dim3(kThreads), 0, stream, sa,
                                kTermsPerPass, (int)(t0 == 0), 0, (float)world, grad_out);
+        if (done > pre_done) {   // [pre_done, done): fused chunks smaller than the reduce chunk
+            SliceArgs sm;
+            memset(&sm, 0, sizeof sm);
+            for (int k = 0; k < kTermsPerPass; ++k) sm.p[k] = slices[t0 + k] + pre_done;
+            const int64_t mid = done - pre_done;
+            hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)(((mid >> 3) + kThreads - 1) / kThreads)),
+                               dim3(kThreads), 0, stream, sm, kTermsPerPass, (int)(t0 == 0), 0, (float)world, mid,
+                               grad_out + pre_done);
+        }
         if (rest > 0) {
             SliceArgs sr;
             memset(&sr, 0, sizeof sr);

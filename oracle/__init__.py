@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_bf16_round_array.restype = None
         L.oracle_reduce.argtypes = [i64, i32, i32, vp, vp]
         L.oracle_reduce.restype = None
+        L.oracle_reduce_bf16rs.argtypes = [i64, i32, i32, vp, vp]
+        L.oracle_reduce_bf16rs.restype = None
+        L.oracle_pack_cast.argtypes = [vp, vp, vp, i32]
+        L.oracle_pack_cast.restype = None
         L.oracle_adamw.argtypes = [i64, vp, vp, vp, vp, i32, vp,
                                    f32, f32, f32, f32, f32, i64]
         L.oracle_adamw.restype = None
@@ -216,6 +220,21 @@ def pack(layout: Layout, params: Sequence[np.ndarray], rank: int = -1) -> np.nda
     return out[:size]
 
 
+def pack_cast(layout: Layout, params: Sequence[np.ndarray], rank: int = -1) -> np.ndarray:
+    """Copy-in with the fp32 -> bf16 parameter cast.  layout: a bf16 layout;
+    params: float32 arrays.  Returns bf16 bits (uint16)."""
+    assert layout.elem_bytes == 2
+    ps = [np.ascontiguousarray(p, np.float32).reshape(-1) for p in params]
+    for p, n in zip(ps, layout.numel):
+        assert p.size == n
+    size = layout.shard if rank >= 0 else layout.gathered_numel
+    out = np.empty(max(1, size), np.uint16)
+    ptrs = (ctypes.c_void_p * max(1, len(ps)))(*[_ptr(p) for p in ps])
+    c = layout._c()
+    lib().oracle_pack_cast(ctypes.byref(c), ptrs, _ptr(out), int(rank))
+    return out[:size]
+
+
 def unpack(layout: Layout, gathered: np.ndarray) -> List[np.ndarray]:
     """All-gather copy-out: per-parameter 1-D arrays from a gathered buffer."""
     dt = np.uint16 if layout.elem_bytes == 2 else np.uint32
@@ -256,6 +275,19 @@ def reduce_shard(slices: Sequence[np.ndarray], world: int, grad_acc: int) -> np.
     out = np.empty(max(1, n), np.float32)
     ptrs = (ctypes.c_void_p * len(ss))(*[_ptr(s) for s in ss])
     lib().oracle_reduce(n, world, grad_acc, ptrs, _ptr(out))
+    return out[:n]
+
+
+def reduce_shard_bf16rs(slices: Sequence[np.ndarray], world: int, grad_acc: int) -> np.ndarray:
+    """Average with a bf16 reduce dtype: each micro-step's N-way average is
+    delivered as bf16, then accumulated in fp32 [P1 mixed precision; P2 9.2]."""
+    assert len(slices) == world * grad_acc
+    ss = [np.ascontiguousarray(s, np.uint16).reshape(-1) for s in slices]
+    n = ss[0].size
+    assert all(s.size == n for s in ss)
+    out = np.empty(max(1, n), np.float32)
+    ptrs = (ctypes.c_void_p * len(ss))(*[_ptr(s) for s in ss])
+    lib().oracle_reduce_bf16rs(n, world, grad_acc, ptrs, _ptr(out))
     return out[:n]
 
 

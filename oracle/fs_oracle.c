@@ -45,6 +45,8 @@
 #include <stdint.h>
 #include <string.h>
 
+uint16_t oracle_bf16_round(float f); /* defined with the number formats below */
+
 /* ------------------------------------------------------------------------ */
 /* Layouts                                                                  */
 /* ------------------------------------------------------------------------ */
@@ -213,6 +215,31 @@ void oracle_pack(const oracle_layout *L, const void *const *params, void *out,
 }
 
 /*
+ * Copy-in with the parameter-dtype cast at the all-gather boundary [P1
+ * section on mixed precision: the all-gather casts the parameters to
+ * param_dtype while the optimizer keeps the original dtype].  The layout is
+ * the bf16 one (elem_bytes 2); the parameters are fp32 and every element is
+ * written as the round-to-nearest-even bf16 of its value; pads are zero.
+ */
+void oracle_pack_cast(const oracle_layout *L, const float *const *params,
+                      uint16_t *out, int32_t rank)
+{
+    int64_t lo = 0, hi = (int64_t)L->world * L->shard;
+    if (rank >= 0) {
+        lo = (int64_t)rank * L->shard;
+        hi = lo + L->shard;
+    }
+    for (int64_t x = 0; x < hi - lo; ++x)
+        out[x] = 0;
+    for (int32_t i = 0; i < L->n_params; ++i)
+        for (int64_t e = 0; e < L->numel[i]; ++e) {
+            int64_t x = gathered_index(L, i, e);
+            if (x >= lo && x < hi)
+                out[x - lo] = oracle_bf16_round(params[i][e]);
+        }
+}
+
+/*
  * All-gather copy-out: read every parameter element back from its place in
  * the gathered buffer (the inverse of oracle_pack with rank < 0).  Pad
  * elements are never read.
@@ -294,6 +321,31 @@ void oracle_reduce(int64_t n, int32_t world, int32_t grad_acc,
             acc = acc + g;
         }
         out[e] = acc / (float)world;
+    }
+}
+
+/*
+ * The same averaging with a bf16 reduce dtype [P1 section on mixed
+ * precision: reduce_dtype sets the precision of the gradient reduction; P2
+ * section 9.2: the own 1/N_d fp32 buffer accumulates the bf16 gradients the
+ * reduce-scatter delivers].  Per micro-step j the N ranks' terms are added in
+ * fp32 in rank order and divided once by N -- the reduce-scatter's average --
+ * and that average is delivered as bf16 (round to nearest even); the
+ * micro-step averages are then accumulated in fp32, starting from the first.
+ */
+void oracle_reduce_bf16rs(int64_t n, int32_t world, int32_t grad_acc,
+                          const uint16_t *const *slices, float *out)
+{
+    for (int64_t e = 0; e < n; ++e) {
+        float acc = 0.0f;
+        for (int32_t j = 0; j < grad_acc; ++j) {
+            float s = bf16_to_float(slices[j * world][e]);
+            for (int32_t k = 1; k < world; ++k)
+                s = s + bf16_to_float(slices[j * world + k][e]);
+            float delivered = bf16_to_float(oracle_bf16_round(s / (float)world));
+            acc = (j == 0) ? delivered : acc + delivered;
+        }
+        out[e] = acc;
     }
 }
 

@@ -299,3 +299,75 @@ def test_adamw_bf16_grad_input():
     b = oracle.adamw_step(th, z, z, oracle.bf16_to_f32(gb), hp)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ------------------------------------------------- bf16 reduce dtype, cast --
+
+def test_reduce_bf16rs_single_microstep_is_rounded_fp32_average():
+    """A = 1: the delivered bf16 average is the bf16 rounding (torch's
+    conversion) of the fp32 average, widened exactly."""
+    rng = np.random.default_rng(12)
+    for N in (1, 2, 3, 8):
+        sl = [oracle.bf16_round((rng.standard_normal(20000) * 1e-3).astype(np.float32)) for _ in range(N)]
+        f32 = oracle.reduce_shard(sl, N, 1)
+        ref = torch.from_numpy(f32.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+        np.testing.assert_array_equal(oracle.reduce_shard_bf16rs(sl, N, 1).view(np.uint32), ref.view(np.uint32))
+
+
+def test_reduce_bf16rs_rounds_each_microstep():
+    """N = 2, A = 2, every micro-step's ranks hold 1 and 2^-8: the average
+    0.5 + 2^-9 lies halfway between the bf16 neighbours 0.5 and 0.5 + 2^-8 and
+    rounds to the even one, 0.5; two micro-steps give 1.0.  The fp32 path keeps
+    1 + 2^-8."""
+    one, tiny = _bf16_bits([1.0]), _bf16_bits([2.0 ** -8])
+    sl = [one, tiny, one, tiny]
+    assert oracle.reduce_shard_bf16rs(sl, 2, 2)[0] == 1.0
+    assert oracle.reduce_shard(sl, 2, 2)[0] == 1.0 + 2.0 ** -8
+
+
+@pytest.mark.parametrize("world,grad_acc", [(2, 2), (4, 2), (8, 4)])
+def test_reduce_bf16rs_linear_model_identity(world, grad_acc):
+    """With dyadic per-rank gradients whose micro-step averages are exact in
+    bf16, the bf16 reduce dtype loses nothing: the result is the full-batch
+    gradient of the data-parallel identity ("Data parallelism, ZeRO and
+    FSDP" section 2.2)."""
+    rng = np.random.default_rng(3 + world)
+    D, K, m = 2, 2, 2
+    B = world * grad_acc * m
+    X = rng.integers(-1, 2, size=(B, D))
+    W = rng.integers(-1, 2, size=(D, K))
+    T = rng.integers(-1, 2, size=(B, K))
+    slices = []
+    for j in range(grad_acc):
+        for k in range(world):
+            rows = slice((j * world + k) * m, (j * world + k + 1) * m)
+            g = (X[rows].T @ (X[rows] @ W - T[rows])).reshape(-1) / (m * grad_acc)
+            slices.append(_bf16_bits(g.astype(np.float32)))
+    full = (X.T @ (X @ W - T)).reshape(-1) / B
+    # micro-step averages must be exact in bf16 for the identity to be exact
+    for j in range(grad_acc):
+        avg = sum(oracle.bf16_to_f32(slices[j * world + k]).astype(np.float64) for k in range(world)) / world
+        assert np.array_equal(oracle.bf16_to_f32(oracle.bf16_round(avg.astype(np.float32))), avg.astype(np.float32))
+    np.testing.assert_array_equal(oracle.reduce_shard_bf16rs(slices, world, grad_acc), full.astype(np.float32))
+
+
+def test_pack_cast_is_pack_of_rounded_params():
+    """The cast copy-in equals the bit copy-in of the params rounded to bf16
+    by torch's conversion, for both layouts and every rank."""
+    rng = np.random.default_rng(8)
+    for kind, shapes, N, uo in (("f1", [(7,), (1,), (33,), (0,), (16,)], 4, True),
+                                ("f1", [(7,), (1,), (33,), (0,), (16,)], 3, False),
+                                ("f2", [(6, 3), (), (9,), (1, 5)], 4, None)):
+        L = oracle.fsdp1_layout(shapes, 2, N, uo) if kind == "f1" else oracle.fsdp2_layout(shapes, 2, N)
+        p32 = [(rng.standard_normal(int(n)) * 0.02).astype(np.float32) for n in L.numel]
+        if p32[0].size:
+            p32[0][0] = np.float32(np.nan)
+        rounded = [torch.from_numpy(p.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                   for p in p32]
+        ref = oracle.pack(L, rounded)
+        got = oracle.pack_cast(L, p32)
+        finite = ~np.isnan(oracle.bf16_to_f32(ref))
+        np.testing.assert_array_equal(got[finite], ref[finite])
+        assert np.isnan(oracle.bf16_to_f32(got[~finite])).all()
+        for r in range(N):
+            np.testing.assert_array_equal(oracle.pack_cast(L, p32, rank=r), got[r * L.shard:(r + 1) * L.shard])
