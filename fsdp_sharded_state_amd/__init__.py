@@ -45,7 +45,10 @@ class PlanInfo(ctypes.Structure):
                 ("shard_numel", ctypes.c_int64), ("gathered_numel", ctypes.c_int64),
                 ("align_pad", ctypes.c_int64), ("tail_pad", ctypes.c_int64),
                 ("n_segments", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("ledger_ideal_bytes", ctypes.c_double), ("ledger_padded_bytes", ctypes.c_double)]
+                ("ledger_ideal_bytes", ctypes.c_double), ("ledger_padded_bytes", ctypes.c_double),
+                ("ledger_ddp_bytes", ctypes.c_double), ("ledger_zero1_bytes", ctypes.c_double),
+                ("ledger_zero2_bytes", ctypes.c_double), ("peak_full_shard_bytes", ctypes.c_double),
+                ("comm_full_shard_bytes", ctypes.c_double), ("comm_shard_grad_op_bytes", ctypes.c_double)]
 
 
 class Segment(ctypes.Structure):
@@ -87,12 +90,15 @@ def lib() -> ctypes.CDLL:
     L.fs_unpack.argtypes = [vp, vp, vp, vp]
     L.fs_reduce_shard.argtypes = [i64, i32, i32, vp, vp, vp]
     L.fs_adamw_step.argtypes = [i64, vp, vp, vp, vp, i32, vp, ctypes.POINTER(AdamWHparams), vp]
+    L.fs_reduce_shard_ex.argtypes = [i64, i32, i32, i32, vp, vp, vp]
+    L.fs_pack_cast.argtypes = [vp, vp, i32, vp, i32, vp]
     L.fs_reduce_adamw_step.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamWHparams), vp]
     L.fs_copy_bytes.argtypes = [vp, vp, i64, vp]
     L.fs_last_error.argtypes = []
     L.fs_last_error.restype = ctypes.c_char_p
     for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
                  "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_reduce_adamw_step",
+                 "fs_reduce_shard_ex", "fs_pack_cast",
                  "fs_copy_bytes"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -226,6 +232,33 @@ def fs_pack(plan: Plan, params: Sequence[torch.Tensor], out: torch.Tensor, rank:
     _check(lib().fs_pack(plan._h, tab.data_ptr(), _dev_ptr(out, "out") if want else 0, int(rank), _stream(stream)))
 
 
+def fs_pack_cast(plan: Plan, params: Sequence[torch.Tensor], out: torch.Tensor, rank: int = -1, stream=None):
+    """Copy-in with the parameter-dtype cast: fp32 params into a bf16 plan's
+    gathered buffer (or rank's shard), rounded to nearest even."""
+    want = plan.info.gathered_numel if rank < 0 else plan.info.shard_numel
+    if out.numel() != want or out.dtype != torch.bfloat16:
+        raise ValueError(f"fs_pack_cast: out must be bfloat16 with {want} elements")
+    if not params:
+        raise ValueError("fs_pack_cast: no parameters")
+    dt = params[0].dtype
+    if any(p.dtype != dt for p in params):
+        raise ValueError("fs_pack_cast: parameters must share one dtype")
+    ptrs = []
+    for i, t in enumerate(params):
+        if t.numel() != plan.numels[i]:
+            raise ValueError(f"params[{i}]: numel {t.numel()} != {plan.numels[i]}")
+        ptrs.append(_dev_ptr(t, f"params[{i}]") if t.numel() else 0)
+    key = ("cast", tuple(ptrs))
+    tab = plan._ptr_cache.get(key)
+    if tab is None:
+        tab = torch.tensor(ptrs, dtype=torch.int64, device=params[0].device)
+        if len(plan._ptr_cache) >= 8:
+            plan._ptr_cache.pop(next(iter(plan._ptr_cache)))
+        plan._ptr_cache[key] = tab
+    _check(lib().fs_pack_cast(plan._h, tab.data_ptr(), _dtype_code(dt), _dev_ptr(out, "out") if want else 0,
+                              int(rank), _stream(stream)))
+
+
 def fs_unpack(plan: Plan, gathered: torch.Tensor, params: Sequence[torch.Tensor], stream=None):
     """All-gather copy-out: gathered -> params."""
     if gathered.numel() != plan.info.gathered_numel or gathered.element_size() != plan.info.elem_bytes:
@@ -250,6 +283,25 @@ def fs_reduce_shard(slices: Sequence[torch.Tensor], out: torch.Tensor, world: in
     arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
     _check(lib().fs_reduce_shard(n, int(world), int(grad_acc), arr, _dev_ptr(out, "out") if n else 0,
                                  _stream(stream)))
+
+
+def fs_reduce_shard_ex(slices: Sequence[torch.Tensor], out: torch.Tensor, world: int, grad_acc: int = 1,
+                       reduce_dtype="fp32", stream=None):
+    """fs_reduce_shard with a reduce dtype: "fp32" (same as fs_reduce_shard)
+    or "bf16" (each micro-step's average delivered in bf16, accumulated in fp32)."""
+    n = out.numel()
+    if out.dtype != torch.float32:
+        raise ValueError("fs_reduce_shard_ex: out must be float32")
+    if len(slices) != world * grad_acc:
+        raise ValueError(f"fs_reduce_shard_ex: need world*grad_acc = {world * grad_acc} slices")
+    ptrs = []
+    for k, s in enumerate(slices):
+        if s.dtype != torch.bfloat16 or s.numel() != n:
+            raise ValueError(f"fs_reduce_shard_ex: slice {k} must be bf16 with {n} elements")
+        ptrs.append(_dev_ptr(s, f"slices[{k}]") if n else 0)
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    _check(lib().fs_reduce_shard_ex(n, int(world), int(grad_acc), _dtype_code(reduce_dtype), arr,
+                                    _dev_ptr(out, "out") if n else 0, _stream(stream)))
 
 
 def fs_adamw_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, grad: torch.Tensor,

@@ -307,6 +307,86 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const Segment *__restr
     }
 }
 
+// ------------------------------------------------------------ cast pack --
+//
+// Copy-in with the parameter-dtype cast at the all-gather boundary: fp32
+// parameters, bf16 gathered buffer (the plan's dtype), each element rounded
+// to nearest even.  Same tiles and segments as the bit-copy pack (they are in
+// destination elements); a 16-byte destination block of 8 bf16 needs 32
+// source bytes: up to three aligned 16-byte loads and two funnel shifts.
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(uint32_t u) {
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ u32x4 cvt8_bf16(u32x4 a, u32x4 b) {
+    return u32x4{(uint32_t)bf16_rne_bits(a.x) | ((uint32_t)bf16_rne_bits(a.y) << 16),
+                 (uint32_t)bf16_rne_bits(a.z) | ((uint32_t)bf16_rne_bits(a.w) << 16),
+                 (uint32_t)bf16_rne_bits(b.x) | ((uint32_t)bf16_rne_bits(b.y) << 16),
+                 (uint32_t)bf16_rne_bits(b.z) | ((uint32_t)bf16_rne_bits(b.w) << 16)};
+}
+
+// 8 fp32 starting at byte address `base` (4-byte aligned), read with aligned
+// 16-byte loads of the blocks that overlap [valid_lo, valid_hi).
+__device__ __forceinline__ u32x4 load8_f32_as_bf16(intptr_t base, intptr_t valid_lo, intptr_t valid_hi) {
+    const intptr_t a0 = base & ~(intptr_t)15;
+    const uint32_t sh = (uint32_t)(base & 15);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 b0 = a0 + 16 > valid_lo ? ld16(reinterpret_cast<const char *>(a0)) : z;
+    const u32x4 b1 = (a0 + 16 < valid_hi && a0 + 32 > valid_lo) ? ld16(reinterpret_cast<const char *>(a0 + 16)) : z;
+    const u32x4 b2 = (sh != 0 && a0 + 32 < valid_hi) ? ld16(reinterpret_cast<const char *>(a0 + 32)) : z;
+    return cvt8_bf16(funnel16(b0, b1, sh), funnel16(b1, b2, sh));
+}
+
+__global__ __launch_bounds__(kThreads) void pack_cast_kernel(const Segment *__restrict__ segs,
+                                                             const Tile *__restrict__ tiles,
+                                                             const void *const *__restrict__ params,
+                                                             char *__restrict__ out, int64_t dst_lo,
+                                                             int64_t dst_hi) {
+    constexpr int VEC = 8;   // bf16 per destination block
+    __shared__ TileLds L;
+    const Tile t = tiles[blockIdx.x];
+    const int64_t x_end = t.x_begin + (int64_t)t.nblk * VEC;
+    char *dst0 = out + (t.x_begin - dst_lo) * 2;
+    const bool dst_full = t.x_begin >= dst_lo && x_end <= dst_hi &&
+                          (reinterpret_cast<uintptr_t>(dst0) & 15) == 0;
+    if (dst_full && t.run_buf >= 0) {   // one contiguous run: 32 source bytes per block
+        const intptr_t src = reinterpret_cast<intptr_t>(params[t.run_buf]) + t.run_src * 4;
+        for (int u = 0; u < fsi::kBlocksPerThread; ++u) {
+            const int b = u * kThreads + threadIdx.x;
+            if (b < t.nblk) {   // the run covers all 32 source bytes of every block
+                const intptr_t a = src + 32 * (intptr_t)b;
+                st16(dst0 + 16 * (int64_t)b, load8_f32_as_bf16(a, a, a + 32));
+            }
+        }
+        return;
+    }
+    stage_tile<2>(L, segs, t);
+    for (int u = 0; u < fsi::kBlocksPerThread; ++u) {
+        const int b = u * kThreads + threadIdx.x;
+        if (b >= t.nblk) break;
+        const int64_t x0 = t.x_begin + (int64_t)b * VEC;
+        u32x4 r = {0u, 0u, 0u, 0u};
+        for (int s = find_first_ending_after(L, t.nseg, x0); s < t.nseg && L.vx[s] < x0 + VEC; ++s) {
+            const int e_lo = (int)(imax(x0, L.vx[s]) - x0);
+            const int e_hi = (int)(imin(x0 + VEC, L.end[s]) - x0);
+            const intptr_t base = reinterpret_cast<intptr_t>(params[L.buf[s]]) + (L.src[s] + (x0 - L.vx[s])) * 4;
+            const u32x4 v = load8_f32_as_bf16(base, base + 4 * e_lo, base + 4 * e_hi);
+            const u32x4 m = elem_mask<2>(e_lo, e_hi);
+            r = (r & ~m) | (v & m);
+        }
+        char *dst = dst0 + 16 * (int64_t)b;
+        const int e_lo = (int)imax(0, dst_lo - x0);
+        const int e_hi = (int)imin(VEC, dst_hi - x0);
+        if (e_lo == 0 && e_hi == VEC && (reinterpret_cast<uintptr_t>(dst) & 15) == 0)
+            st16(dst, r);
+        else
+            store_elems<2>(dst, r, e_lo, e_hi);
+    }
+}
+
 // ---------------------------------------------------------------- reduce --
 //
 // Every output element is the sum of its A*N terms added in fp32 in slice
@@ -442,6 +522,13 @@ __device__ __forceinline__ void load_groups(u32x2 (&x)[kRedGroups], const uint16
         x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
 }
 
+template <int G>
+__device__ __forceinline__ void load_groups_n(u32x2 (&x)[G], const uint16_t *p, int64_t base) {
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
+}
+
 __global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
                                                                 int last_pass, float world,
                                                                 float *__restrict__ out) {
@@ -490,6 +577,123 @@ __global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, in
         st16(reinterpret_cast<char *>(out + base + u * kThreads * 4),
              u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
                    __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])});
+}
+
+// ------------------------------------------------- bf16 reduce dtype --
+//
+// The reduce-scatter delivers each micro-step's N-way average in bf16, and
+// the own shard accumulates those in fp32: per element and micro-step j, the
+// N terms are added in fp32 in rank order and divided once by N, the
+// quotient is rounded to bf16 (nearest even) and widened, and the micro-step
+// values are accumulated in fp32 starting from the first.  Same slice-major
+// chunk layout as the fp32 reduce, with a second register block for the
+// running micro-step sum.  A pass holds whole micro-steps (floor(32/N) of
+// them); passes carry the fp32 accumulator through `out`.
+
+constexpr int kRsGroups = 8;
+constexpr int64_t kRsChunk = (int64_t)kThreads * 4 * kRsGroups;   // 8192 elements
+
+__device__ __forceinline__ float bf16_round_f32(float f) {
+    return __uint_as_float((uint32_t)bf16_rne_bits(__float_as_uint(f)) << 16);
+}
+
+__global__ __launch_bounds__(kThreads) void reduce_rs_chunk_kernel(SliceArgs sa, int nsteps, int world,
+                                                                   int first_pass, float worldf,
+                                                                   float *__restrict__ out) {
+    const int64_t base = (int64_t)blockIdx.x * kRsChunk + 4 * threadIdx.x;
+    float acc[4 * kRsGroups], sum[4 * kRsGroups];
+    u32x2 xa[kRsGroups], xb[kRsGroups];
+    if (!first_pass) {
+#pragma unroll
+        for (int u = 0; u < kRsGroups; ++u) {
+            const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(out + base + u * kThreads * 4));
+            acc[4 * u] = __uint_as_float(o.x);
+            acc[4 * u + 1] = __uint_as_float(o.y);
+            acc[4 * u + 2] = __uint_as_float(o.z);
+            acc[4 * u + 3] = __uint_as_float(o.w);
+        }
+    }
+    const int total = nsteps * world;
+    // add term t (held in x) into the micro-step sum; fold the finished micro-step into acc
+    auto consume = [&](const u32x2 (&x)[kRsGroups], int t) {
+        const int k = t % world, j = t / world;
+#pragma unroll
+        for (int u = 0; u < kRsGroups; ++u) {
+            const float w[4] = {__uint_as_float(x[u].x << 16), __uint_as_float(x[u].x & 0xFFFF0000u),
+                                __uint_as_float(x[u].y << 16), __uint_as_float(x[u].y & 0xFFFF0000u)};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum[4 * u + q] = k == 0 ? w[q] : sum[4 * u + q] + w[q];
+        }
+        if (k == world - 1) {
+#pragma unroll
+            for (int e = 0; e < 4 * kRsGroups; ++e) {
+                const float d = bf16_round_f32(sum[e] / worldf);
+                acc[e] = (first_pass && j == 0) ? d : acc[e] + d;
+            }
+        }
+    };
+    int t = 0;
+    if (t < total) load_groups_n<kRsGroups>(xa, sa.p[t], base);
+    while (t < total) {
+        if (t + 1 < total) load_groups_n<kRsGroups>(xb, sa.p[t + 1], base);
+        consume(xa, t);
+        if (++t >= total) break;
+        if (t + 1 < total) load_groups_n<kRsGroups>(xa, sa.p[t + 1], base);
+        consume(xb, t);
+        ++t;
+    }
+#pragma unroll
+    for (int u = 0; u < kRsGroups; ++u)
+        st16(reinterpret_cast<char *>(out + base + u * kThreads * 4),
+             u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
+                   __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])});
+}
+
+// Remainder / misaligned variant: 8 elements per lane, element tail.
+template <bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void reduce_rs_general_kernel(SliceArgs sa, int nsteps, int world,
+                                                                     int first_pass, float worldf, int64_t n,
+                                                                     float *__restrict__ out) {
+    const int64_t nvec = n >> 3;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < nvec) {
+        const int64_t off = i * 16;
+        float acc[8], sum[8];
+        if (!first_pass) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = out[8 * i + e];
+        }
+        for (int j = 0; j < nsteps; ++j) {
+            set_bf16x8(sum, ld_slice16<ALIGNED>(sa.p[j * world], off));
+            for (int k = 1; k < world; ++k) add_bf16x8(sum, ld_slice16<ALIGNED>(sa.p[j * world + k], off));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = bf16_round_f32(sum[e] / worldf);
+                acc[e] = (first_pass && j == 0) ? d : acc[e] + d;
+            }
+        }
+        if (ALIGNED) {
+            st16(reinterpret_cast<char *>(out + 8 * i),
+                 u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])});
+            st16(reinterpret_cast<char *>(out + 8 * i + 4),
+                 u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]), __float_as_uint(acc[7])});
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[8 * i + e] = acc[e];
+        }
+    }
+    const int64_t tail = n - nvec * 8;
+    if (blockIdx.x == 0 && (int64_t)threadIdx.x < tail) {
+        const int64_t e = nvec * 8 + threadIdx.x;
+        float acc = first_pass ? 0.0f : out[e];
+        for (int j = 0; j < nsteps; ++j) {
+            float sum = __uint_as_float((uint32_t)sa.p[j * world][e] << 16);
+            for (int k = 1; k < world; ++k) sum = sum + __uint_as_float((uint32_t)sa.p[j * world + k][e] << 16);
+            const float d = bf16_round_f32(sum / worldf);
+            acc = (first_pass && j == 0) ? d : acc + d;
+        }
+        out[e] = acc;
+    }
 }
 
 // ----------------------------------------------------------------- AdamW --
@@ -619,12 +823,6 @@ constexpr int kFusedGroups = FS_FUSED_GROUPS;
 constexpr int kFusedBatch = FS_FUSED_BATCH < FS_FUSED_GROUPS ? FS_FUSED_BATCH : FS_FUSED_GROUPS;
 constexpr int64_t kFusedChunk = (int64_t)kThreads * 4 * kFusedGroups;
 
-template <int G>
-__device__ __forceinline__ void load_groups_n(u32x2 (&x)[G], const uint16_t *p, int64_t base) {
-#pragma unroll
-    for (int u = 0; u < G; ++u)
-        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
-}
 
 template <bool HAS_P16, bool HAS_G>
 __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
@@ -897,29 +1095,49 @@ extern "C" int fs_unpack(fs_plan_t plan, const void *gathered, void *const *para
     return check_launch("fs_unpack");
 }
 
+namespace {
+
+// Shared argument checks of the reduce entry points.  Sets *terms and
+// *aligned (every slice and `out` 16-byte aligned).  Returns FS_OK, or the
+// error; *skip is set when n == 0 (nothing to launch).
+int check_reduce(const char *what, int64_t n, int32_t world, int32_t grad_acc, const uint16_t *const *slices,
+                 const float *out, int *terms, bool *aligned, bool *skip) {
+    *skip = false;
+    if (n < 0) return fsi::fail(FS_E_INVAL, "%s: n < 0", what);
+    if (world < 1 || grad_acc < 1) return fsi::fail(FS_E_INVAL, "%s: world and grad_acc must be >= 1", what);
+    int64_t terms64;
+    if (__builtin_mul_overflow((int64_t)world, (int64_t)grad_acc, &terms64) || terms64 > (1 << 20))
+        return fsi::fail(FS_E_OVERFLOW, "%s: too many terms", what);
+    int64_t bytes_in, bytes_out;
+    if (__builtin_mul_overflow(n, (int64_t)2, &bytes_in) || __builtin_mul_overflow(n, (int64_t)4, &bytes_out))
+        return fsi::fail(FS_E_OVERFLOW, "%s: n too large", what);
+    if (n == 0) {
+        *skip = true;
+        return FS_OK;
+    }
+    if (!slices || !out) return fsi::fail(FS_E_INVAL, "%s: NULL pointer", what);
+    *terms = (int)terms64;
+    *aligned = !misaligned(out, 16);
+    if (misaligned(out, 4)) return fsi::fail(FS_E_ALIGN, "%s: out not 4-byte aligned", what);
+    for (int t = 0; t < *terms; ++t) {
+        if (!slices[t]) return fsi::fail(FS_E_INVAL, "%s: slice %d is NULL", what, t);
+        if (misaligned(slices[t], 2)) return fsi::fail(FS_E_ALIGN, "%s: slice %d not 2-byte aligned", what, t);
+        if (misaligned(slices[t], 16)) *aligned = false;
+        if (ranges_overlap(slices[t], bytes_in, out, bytes_out))
+            return fsi::fail(FS_E_INVAL, "%s: out overlaps slice %d", what, t);
+    }
+    return FS_OK;
+}
+
+}  // namespace
+
 extern "C" int fs_reduce_shard(int64_t n, int32_t world, int32_t grad_acc, const uint16_t *const *slices,
                                float *out, hipStream_t stream) {
     fsi::clear_error();
-    if (n < 0) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: n < 0");
-    if (world < 1 || grad_acc < 1) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: world and grad_acc must be >= 1");
-    int64_t terms64;
-    if (__builtin_mul_overflow((int64_t)world, (int64_t)grad_acc, &terms64) || terms64 > (1 << 20))
-        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: too many terms");
-    int64_t bytes_in, bytes_out;
-    if (__builtin_mul_overflow(n, (int64_t)2, &bytes_in) || __builtin_mul_overflow(n, (int64_t)4, &bytes_out))
-        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large");
-    if (n == 0) return FS_OK;
-    if (!slices || !out) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: NULL pointer");
-    const int terms = (int)terms64;
-    bool aligned = !misaligned(out, 16);
-    if (misaligned(out, 4)) return fsi::fail(FS_E_ALIGN, "fs_reduce_shard: out not 4-byte aligned");
-    for (int t = 0; t < terms; ++t) {
-        if (!slices[t]) return fsi::fail(FS_E_INVAL, "fs_reduce_shard: slice %d is NULL", t);
-        if (misaligned(slices[t], 2)) return fsi::fail(FS_E_ALIGN, "fs_reduce_shard: slice %d not 2-byte aligned", t);
-        if (misaligned(slices[t], 16)) aligned = false;
-        if (ranges_overlap(slices[t], bytes_in, out, bytes_out))
-            return fsi::fail(FS_E_INVAL, "fs_reduce_shard: out overlaps slice %d", t);
-    }
+    int terms = 0;
+    bool aligned = false, skip = false;
+    if (int rc = check_reduce("fs_reduce_shard", n, world, grad_acc, slices, out, &terms, &aligned, &skip)) return rc;
+    if (skip) return FS_OK;
     const int64_t nchunks = aligned ? n / kRedChunk : 0;
     const int64_t done = nchunks * kRedChunk;
     const int64_t rest = n - done;
@@ -951,6 +1169,89 @@ extern "C" int fs_reduce_shard(int64_t n, int32_t world, int32_t grad_acc, const
         if (rc != FS_OK) return rc;
     }
     return FS_OK;
+}
+
+extern "C" int fs_reduce_shard_ex(int64_t n, int32_t world, int32_t grad_acc, fs_dtype reduce_dtype,
+                                  const uint16_t *const *slices, float *out, hipStream_t stream) {
+    fsi::clear_error();
+    if (reduce_dtype == FS_FP32) return fs_reduce_shard(n, world, grad_acc, slices, out, stream);
+    if (reduce_dtype != FS_BF16) return fsi::fail(FS_E_DTYPE, "fs_reduce_shard_ex: unknown reduce dtype");
+    int terms = 0;
+    bool aligned = false, skip = false;
+    if (int rc = check_reduce("fs_reduce_shard_ex", n, world, grad_acc, slices, out, &terms, &aligned, &skip))
+        return rc;
+    if (skip) return FS_OK;
+    if (world > kTermsPerPass)
+        return fsi::fail(FS_E_UNSUPPORTED, "fs_reduce_shard_ex: bf16 reduce dtype supports world <= %d", kTermsPerPass);
+    const int steps_per_pass = kTermsPerPass / world;
+    const int64_t nchunks = aligned ? n / kRsChunk : 0;
+    const int64_t done = nchunks * kRsChunk;
+    const int64_t rest = n - done;
+    const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
+    if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
+        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard_ex: n too large for one launch");
+    (void)hipGetLastError();
+    for (int j0 = 0; j0 < grad_acc; j0 += steps_per_pass) {
+        const int steps = std::min(steps_per_pass, grad_acc - j0);
+        const int first = j0 == 0;
+        SliceArgs sa, sr;
+        memset(&sa, 0, sizeof sa);
+        memset(&sr, 0, sizeof sr);
+        for (int k = 0; k < steps * world; ++k) {
+            sa.p[k] = slices[j0 * world + k];
+            sr.p[k] = slices[j0 * world + k] + done;
+        }
+        if (nchunks > 0)
+            hipLaunchKernelGGL(reduce_rs_chunk_kernel, dim3((uint32_t)nchunks), dim3(kThreads), 0, stream, sa, steps,
+                               (int)world, first, (float)world, out);
+        if (rest > 0) {
+            if (aligned)
+                hipLaunchKernelGGL(reduce_rs_general_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
+                                   stream, sr, steps, (int)world, first, (float)world, rest, out + done);
+            else
+                hipLaunchKernelGGL(reduce_rs_general_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
+                                   stream, sr, steps, (int)world, first, (float)world, rest, out + done);
+        }
+        int rc = check_launch("fs_reduce_shard_ex");
+        if (rc != FS_OK) return rc;
+    }
+    return FS_OK;
+}
+
+extern "C" int fs_pack_cast(fs_plan_t plan, const void *const *params, fs_dtype param_dtype, void *out,
+                            int32_t rank, hipStream_t stream) {
+    fsi::clear_error();
+    if (!plan) return fsi::fail(FS_E_INVAL, "fs_pack_cast: plan is NULL");
+    const fs_plan_info_t &I = plan->info;
+    if (param_dtype != FS_BF16 && param_dtype != FS_FP32) return fsi::fail(FS_E_DTYPE, "fs_pack_cast: unknown dtype");
+    if ((int)param_dtype == I.dtype) return fs_pack(plan, params, out, rank, stream);
+    if (!(param_dtype == FS_FP32 && I.dtype == FS_BF16))
+        return fsi::fail(FS_E_UNSUPPORTED, "fs_pack_cast: only fp32 parameters into a bf16 layout are defined");
+    if (!plan->dev_ws) return fsi::fail(FS_E_INVAL, "fs_pack_cast: plan has no uploaded workspace (call fs_plan_upload)");
+    if (rank < -1 || rank >= I.world)
+        return fsi::fail(FS_E_INVAL, "fs_pack_cast: rank %d out of range [-1, %d)", rank, I.world);
+    const int64_t lo = rank < 0 ? 0 : (int64_t)rank * I.shard_numel;
+    const int64_t hi = rank < 0 ? I.gathered_numel : lo + I.shard_numel;
+    if (hi == lo) return FS_OK;
+    if (!out) return fsi::fail(FS_E_INVAL, "fs_pack_cast: out is NULL");
+    if (I.n_params > 0 && !params) return fsi::fail(FS_E_INVAL, "fs_pack_cast: params is NULL");
+    if (misaligned(out, 2)) return fsi::fail(FS_E_ALIGN, "fs_pack_cast: out not aligned to 2 bytes");
+    const char *ws = static_cast<const char *>(plan->dev_ws);
+    const Segment *segs = reinterpret_cast<const Segment *>(ws + plan->ws.pack_segs);
+    const Tile *tiles;
+    int64_t ntiles;
+    if (rank < 0) {
+        tiles = reinterpret_cast<const Tile *>(ws + plan->ws.pack_tiles_all);
+        ntiles = plan->ws.n_pack_tiles_all;
+    } else {
+        tiles = reinterpret_cast<const Tile *>(ws + plan->ws.pack_tiles_rank) + plan->rank_tile_off[rank];
+        ntiles = plan->rank_tile_off[rank + 1] - plan->rank_tile_off[rank];
+    }
+    if (ntiles == 0) return FS_OK;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(pack_cast_kernel, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles, params,
+                       static_cast<char *>(out), lo, hi);
+    return check_launch("fs_pack_cast");
 }
 
 extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *exp_avg_sq, const void *grad,

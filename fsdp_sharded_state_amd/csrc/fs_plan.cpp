@@ -303,9 +303,17 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
         I.tail_pad = mode == FS_FSDP1_FLAT ? gathered - flat : gathered - total;
         I.n_segments = (int64_t)ps.size();
         I.workspace_bytes = w.total_bytes;
-        const double per_param = 2.0 * (double)eb + (double)I.bopt + (grad_acc > 1 ? 4.0 : 0.0);
-        I.ledger_ideal_bytes = (double)total * per_param / (double)world;
+        const double b = (double)eb, bopt = (double)I.bopt, Pd = (double)total, Nd = (double)world;
+        const double acc = grad_acc > 1 ? 4.0 : 0.0;   // fp32 gradient accumulator
+        const double per_param = 2.0 * b + bopt + acc;
+        I.ledger_ideal_bytes = Pd * per_param / Nd;
         I.ledger_padded_bytes = (double)shard * per_param;
+        I.ledger_ddp_bytes = Pd * (2.0 * b + bopt) + acc * Pd;
+        I.ledger_zero1_bytes = 2.0 * Pd * b + Pd * bopt / Nd + acc * Pd;
+        I.ledger_zero2_bytes = Pd * b + Pd * (b + bopt) / Nd + acc * Pd / Nd;
+        I.peak_full_shard_bytes = I.ledger_ideal_bytes + Pd * b;
+        I.comm_full_shard_bytes = 3.0 * Pd * (Nd - 1.0) / Nd * b;
+        I.comm_shard_grad_op_bytes = 2.0 * Pd * (Nd - 1.0) / Nd * b;
     } catch (const std::bad_alloc &) {
         delete p;
         return fsi::fail(FS_E_NOMEM, "fs_plan: out of host memory");

@@ -85,6 +85,17 @@ typedef struct {
      * padded = shard_numel*(2b + bopt), plus 4*shard_numel when grad_acc > 1.  b = elem_bytes. */
     double ledger_ideal_bytes;
     double ledger_padded_bytes;
+    /* The same group under the other data-parallel schemes, per rank [FvF
+     * section 01 and strategy ledger; DPZ section 9]; P = total_numel,
+     * b = elem_bytes, bopt = 12, A = 4 B of fp32 gradient accumulator when
+     * grad_acc > 1 (kept for the whole gradient under DDP and ZeRO-1, for the
+     * own 1/N under ZeRO-2): */
+    double ledger_ddp_bytes;          /* P(2b + bopt) (+ A*P) */
+    double ledger_zero1_bytes;        /* 2Pb + P*bopt/N (+ A*P) */
+    double ledger_zero2_bytes;        /* Pb + P(b + bopt)/N (+ A*P/N) */
+    double peak_full_shard_bytes;     /* ideal ZeRO-3 bytes + P*b while the group is gathered */
+    double comm_full_shard_bytes;     /* 3P(N-1)/N * b per step (AG forward, AG backward, RS) */
+    double comm_shard_grad_op_bytes;  /* 2P(N-1)/N * b per step (one AG, one RS) */
 } fs_plan_info_t;
 
 /* One contiguous run of a parameter inside the gathered buffer.  Elements
@@ -230,6 +241,46 @@ int fs_unpack(fs_plan_t plan, const void *gathered, void *const *params,
 int fs_reduce_shard(int64_t n, int32_t world, int32_t grad_acc,
                     const uint16_t *const *slices, float *out,
                     hipStream_t stream);
+
+/*
+ * fs_reduce_shard_ex -- fs_reduce_shard with a choice of reduce dtype [FvF
+ * mixed-precision section: reduce_dtype sets the precision of the gradient
+ * reduction; DPZ section 9.2: the own fp32 shard accumulates the bf16
+ * gradients the reduce-scatter delivers].
+ *
+ *   reduce_dtype   FS_FP32: identical to fs_reduce_shard.
+ *                  FS_BF16: for each micro-step j, the N terms are added in
+ *                  fp32 in rank order and divided once by N, the quotient is
+ *                  rounded to bf16 (nearest even) -- what a bf16
+ *                  reduce-scatter delivers -- and the micro-step values are
+ *                  accumulated in fp32 starting from the first.  Needs
+ *                  world <= 32.  Bit-exact and deterministic.
+ *   other arguments as fs_reduce_shard.
+ * Errors: those of fs_reduce_shard; FS_E_DTYPE for another reduce_dtype;
+ * FS_E_UNSUPPORTED for world > 32 with FS_BF16.
+ */
+int fs_reduce_shard_ex(int64_t n, int32_t world, int32_t grad_acc,
+                       fs_dtype reduce_dtype, const uint16_t *const *slices,
+                       float *out, hipStream_t stream);
+
+/*
+ * fs_pack_cast -- the all-gather copy-in with the parameter-dtype cast at
+ * the all-gather boundary [FvF mixed-precision section: the all-gather casts
+ * the parameters to param_dtype, the optimizer keeps the original dtype].
+ *
+ *   plan           a plan made with dtype FS_BF16 (the param_dtype; FSDP1
+ *                  alignment follows it), uploaded.
+ *   params (device) array of n_params device pointers to parameters stored
+ *                  as `param_dtype`.
+ *   param_dtype    FS_FP32: every element is written as the
+ *                  round-to-nearest-even bf16 of its value (NaN stays a
+ *                  quiet NaN); FS_BF16: identical to fs_pack.
+ *   out, rank      as fs_pack (bf16 output).
+ * Errors: those of fs_pack; FS_E_DTYPE; FS_E_UNSUPPORTED for any other
+ * dtype pair.
+ */
+int fs_pack_cast(fs_plan_t plan, const void *const *params, fs_dtype param_dtype,
+                 void *out, int32_t rank, hipStream_t stream);
 
 /*
  * fs_adamw_step -- one mixed-precision AdamW step over the shard [DPZ

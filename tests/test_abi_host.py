@@ -230,3 +230,54 @@ def test_fused_call_validation_before_gpu():
     # an output overlapping a slice
     assert L.fs_reduce_adamw_step(8, 2, 1, sl, ctypes.c_void_p((1 << 20) + 4), ctypes.c_void_p(1 << 25),
                                   ctypes.c_void_p(1 << 26), None, None, ctypes.byref(hp), None) == fs.FS_E_INVAL
+
+
+def test_reduce_ex_and_pack_cast_validation_before_gpu():
+    L = fs.lib()
+    sl = (ctypes.c_void_p * 2)(1 << 20, 1 << 21)
+    out = ctypes.c_void_p(1 << 24)
+    assert L.fs_reduce_shard_ex(8, 2, 1, 7, sl, out, None) == fs.FS_E_DTYPE
+    assert L.fs_reduce_shard_ex(-1, 2, 1, fs.FS_BF16, sl, out, None) == fs.FS_E_INVAL
+    assert L.fs_reduce_shard_ex(0, 2, 1, fs.FS_BF16, sl, out, None) == fs.FS_OK
+    many = (ctypes.c_void_p * 33)(*[(1 << 20) * (k + 1) for k in range(33)])
+    assert L.fs_reduce_shard_ex(8, 33, 1, fs.FS_BF16, many, ctypes.c_void_p(1 << 30), None) == fs.FS_E_UNSUPPORTED
+    p32 = fs.fs_plan([(3,), (5,)], "fp32", 4, True, "fsdp1")
+    assert L.fs_pack_cast(p32._h, ctypes.c_void_p(16), fs.FS_BF16, ctypes.c_void_p(16), -1, None) == fs.FS_E_UNSUPPORTED
+    p16 = fs.fs_plan([(3,), (5,)], "bf16", 4, True, "fsdp1")
+    assert L.fs_pack_cast(p16._h, ctypes.c_void_p(16), fs.FS_FP32, ctypes.c_void_p(16), -1, None) == fs.FS_E_INVAL  # not uploaded
+    assert L.fs_pack_cast(p16._h, ctypes.c_void_p(16), 9, ctypes.c_void_p(16), -1, None) == fs.FS_E_DTYPE
+
+
+@pytest.mark.parametrize("dtype,eb", [("bf16", 2), ("fp32", 4)])
+@pytest.mark.parametrize("grad_acc", [1, 4])
+def test_plan_ledger_fields_match_oracle(dtype, eb, grad_acc):
+    """Every per-rank ledger field of a plan equals the oracle's ledger for
+    the group's P, N, b and bopt = 12."""
+    for N in (1, 2, 8, 64):
+        p = fs.fs_plan(synth.llama_block_shapes(), dtype, N, False, "fsdp2", grad_acc)
+        P = p.total_numel
+        led = oracle.ledger(P, N, eb, 12, fp32_grad_acc=grad_acc > 1)
+        strat = oracle.strategy_ledger(P, N, eb, 12)
+        assert p.ledger_ddp_bytes == pytest.approx(led["ddp"], rel=1e-12)
+        assert p.ledger_zero1_bytes == pytest.approx(led["zero1"], rel=1e-12)
+        assert p.ledger_zero2_bytes == pytest.approx(led["zero2"], rel=1e-12)
+        assert p.ledger_ideal_bytes == pytest.approx(led["zero3"], rel=1e-12)
+        assert p.comm_full_shard_bytes == pytest.approx(strat["FULL_SHARD"]["comm"], rel=1e-12, abs=1e-9)
+        assert p.comm_shard_grad_op_bytes == pytest.approx(strat["SHARD_GRAD_OP"]["comm"], rel=1e-12, abs=1e-9)
+        if grad_acc == 1:
+            assert p.peak_full_shard_bytes == pytest.approx(strat["FULL_SHARD"]["peak"], rel=1e-12)
+
+
+def test_seven_b_strategy_table_from_plans():
+    """The 7B model at N = 8 through the plans, with the pages' 8 B/param
+    optimizer convention of the strategy table restored (bopt 12 -> 8 moves
+    every sharded figure by 4P/N and the replicated one by 4P): the FULL_SHARD
+    communication and the replica sizes scale from the page's 7e9 to this
+    model's P exactly."""
+    groups = synth.llama_model_groups(32, 4096, 11008)
+    plans = [fs.fs_plan(g, "bf16", 8, False, "fsdp2", 1) for g in groups]
+    P = sum(p.total_numel for p in plans)
+    comm = sum(p.comm_full_shard_bytes for p in plans)
+    assert comm == pytest.approx(36.75e9 * P / 7e9, rel=1e-12)
+    ddp_bopt8 = sum(p.ledger_ddp_bytes for p in plans) - 4 * P
+    assert ddp_bopt8 == pytest.approx(84e9 * P / 7e9, rel=1e-12)

@@ -374,3 +374,75 @@ def test_reduce_adamw_fused_needs_grad_out_beyond_32_terms():
     st = [torch.zeros(64, device="cuda") for _ in range(3)]
     with pytest.raises(fs.FsError, match="grad_out"):
         fs.fs_reduce_adamw_step(sl, *st, world=8, grad_acc=5)
+
+
+# ------------------------------------------------------ bf16 reduce dtype --
+
+RS_CASES = [
+    # (n, world, grad_acc, slice shift, out shift)
+    (1, 1, 1, 0, 0), (7, 2, 2, 0, 0), (8192 * 2 + 5, 8, 4, 0, 0), (16384, 8, 4, 0, 0),
+    (5000, 8, 5, 0, 0),       # 40 terms: passes of 4 micro-steps
+    (20007, 2, 33, 0, 0),     # 66 terms: passes of 16 micro-steps
+    (4097, 8, 4, 1, 0), (9000, 3, 3, 3, 1),
+    (100003, 32, 1, 0, 0),    # N = 32
+    (25_297_920, 8, 4, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", RS_CASES, ids=lambda c: "n%d_N%d_A%d_s%d_o%d" % c)
+def test_reduce_bf16_reduce_dtype_bitexact(case):
+    n, N, A, sh, osh = case
+    say("reduce bf16 reduce dtype", case)
+    sl = _slices(n, N * A, seed=n % 71 + 5, shift=sh, specials=True)
+    out = Guarded(n, torch.float32, shift=osh)
+    fs.fs_reduce_shard_ex([s.t for s in sl], out.t, N, A, reduce_dtype="bf16")
+    torch.cuda.synchronize()
+    out.check()
+    ref = oracle.reduce_shard_bf16rs([bits(s.t) for s in sl], N, A)
+    got = bits(out.t)
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(got[~nan], ref.view(np.uint32)[~nan])
+    assert np.isnan(got.view(np.float32)[nan]).all()
+    # reduce dtype fp32 through the same entry point is fs_reduce_shard
+    out2 = Guarded(n, torch.float32)
+    fs.fs_reduce_shard_ex([s.t for s in sl], out2.t, N, A, reduce_dtype="fp32")
+    torch.cuda.synchronize()
+    ref2 = oracle.reduce_shard([bits(s.t) for s in sl], N, A)
+    nan2 = np.isnan(ref2)
+    np.testing.assert_array_equal(bits(out2.t)[~nan2], ref2.view(np.uint32)[~nan2])
+
+
+# ------------------------------------------------------------ cast pack --
+
+def _params_f32(shapes, seed, shift=0):
+    out, off = [], 0
+    for s in shapes:
+        n = int(np.prod(s)) if len(s) else 1
+        vals = synth.normal_f32(seed, synth.STREAM_MASTER, n, 0.02, device="cuda", start=off)
+        if n >= 12:   # specials: NaN, infinities, a bf16 tie, denormals, -0
+            vals[:8] = torch.tensor([float("nan"), float("inf"), -float("inf"), 1.0 + 2.0 ** -8,
+                                     1e-40, -0.0, 3.4e38, -2.0 ** -133], device="cuda")
+        out.append(Guarded(n, torch.float32, shift=shift, fill=vals))
+        off += n
+    return out
+
+
+@pytest.mark.parametrize("case", [c for c in _layout_cases() if c[3] == "bf16"], ids=lambda c: c[0])
+@pytest.mark.parametrize("shift", [0, 1])
+def test_pack_cast_bitexact(case, shift):
+    name, mode, shapes, dt, N, uo = case
+    say("pack cast", name, shift)
+    plan = fs.fs_plan(shapes, "bf16", N, uo, mode).upload()
+    L = _olayout(mode, shapes, "bf16", N, uo)
+    params = _params_f32(shapes, seed=41, shift=shift)
+    ref = oracle.pack_cast(L, [p.t.cpu().numpy() for p in params])
+    G = Guarded(plan.gathered_numel, torch.bfloat16)
+    fs.fs_pack_cast(plan, [p.t for p in params], G.t)
+    r = N - 1
+    S = Guarded(plan.shard_numel, torch.bfloat16, shift=shift)
+    fs.fs_pack_cast(plan, [p.t for p in params], S.t, rank=r)
+    torch.cuda.synchronize()
+    G.check()
+    S.check()
+    np.testing.assert_array_equal(bits(G.t), ref)
+    np.testing.assert_array_equal(bits(S.t), ref[r * plan.shard_numel:(r + 1) * plan.shard_numel])
