@@ -39,6 +39,8 @@ WORKLOADS = {
     "7b": (32, 4096, 11008, None, 32000, 8, 4),
     "70b": (80, 8192, 28672, 1024, 32000, 8, 2),
 }
+# llama_model_groups(n_blocks, d, f, vocab, kv) arguments per workload
+_WL_SHAPES = {k: (v[0], v[1], v[2], v[4], v[3]) for k, v in WORKLOADS.items()}
 
 
 def log(*a):
@@ -90,7 +92,7 @@ def setup(workload: str, seed: int = 4):
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
     return dict(fs=fs, plans=plans, params=params, gathered=gathered, outs=outs, slices=slices,
                 master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, grad32=grad32, p16=p16,
-                S=S, P=P, world=world, grad_acc=grad_acc, groups=len(groups))
+                S=S, P=P, world=world, grad_acc=grad_acc, groups=len(groups), workload=workload)
 
 
 def algorithmic_bytes(W) -> dict:
@@ -124,6 +126,70 @@ def run_step(W, step_t, ev=None):
                      lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=step_t)
     if ev:
         ev[4].record()
+
+
+def _timed(fn, reps):
+    import torch
+    fn()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in evs:
+        e[0].record()
+        fn()
+        e[1].record()
+    torch.cuda.synchronize()
+    return sum(e[0].elapsed_time(e[1]) for e in evs) / reps
+
+
+def extra_measurements(W, reps) -> dict:
+    """The engine's other entry points on the same workload, outside the
+    headline step: the bf16 reduce dtype over the same 32 slices, and the
+    fp32 -> bf16 cast copy-in of every group from fp32 parameters."""
+    import torch
+
+    import synth
+    fs, S, N, A = W["fs"], W["S"], W["world"], W["grad_acc"]
+    out = {}
+    ms = _timed(lambda: fs.fs_reduce_shard_ex(W["slices"], W["grad32"], N, A, reduce_dtype="bf16"), reps)
+    b = (2 * N * A + 4) * S
+    out["reduce_bf16_reduce_dtype"] = {"ms": round(ms, 4), "GB": round(b / 1e9, 3),
+                                       "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                       "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    p32, off = [], 0
+    for ps in W["params"]:
+        g = []
+        for t in ps:
+            g.append(synth.normal_f32(4, synth.STREAM_MASTER, t.numel(), 0.02, device="cuda", start=off))
+            off += t.numel()
+        p32.append(g)
+
+    def cast_all():
+        for p, g, gath in zip(W["plans"], p32, W["gathered"]):
+            fs.fs_pack_cast(p, g, gath)
+    ms = _timed(cast_all, reps)
+    b = 4 * W["P"] + 2 * sum(p.gathered_numel for p in W["plans"])
+    out["pack_cast_fp32_to_bf16"] = {"ms": round(ms, 4), "GB": round(b / 1e9, 3),
+                                     "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                     "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del p32
+    torch.cuda.empty_cache()
+    # re-shard every group's gathered buffer from N to N/2 logical ranks
+    import synth as _s
+    groups = _s.llama_model_groups(*_WL_SHAPES[W["workload"]])
+    half = [fs.fs_plan(g, "bf16", max(1, N // 2), False, "fsdp2", A).upload() for g in groups]
+    rs = [fs.fs_reshard_plan(p, q).upload() for p, q in zip(W["plans"], half)]
+    dst = [torch.empty(q.gathered_numel, dtype=torch.bfloat16, device="cuda") for q in half]
+
+    def reshard_all():
+        for r, g, d in zip(rs, W["gathered"], dst):
+            fs.fs_reshard(r, g, d)
+    ms = _timed(reshard_all, reps)
+    b = 2 * W["P"] + 2 * sum(q.gathered_numel for q in half)
+    out["reshard_n_to_half_n"] = {"ms": round(ms, 4), "GB": round(b / 1e9, 3),
+                                  "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del dst, rs, half
+    torch.cuda.empty_cache()
+    return out
 
 
 def copy_ceiling(fs, nbytes=1 << 32, reps=5):
@@ -204,9 +270,12 @@ def traffic_for(kernel: str, launch_bytes_alg: float):
 
 KERNELS = {  # rocprofv3 kernel-name fragment -> bench phase
     "reduce_chunk_kernel": "reduce",
+    "scatter_kernel<2, (anonymous namespace)::UnpackSrc": "reshard",
+    "reduce_rs_chunk_kernel": "reduce_bf16_reduce_dtype",
+    "pack_cast_kernel": "pack_cast",
     "reduce_adamw_chunk_kernel": "reduce_adamw_fused",
     "adamw_wave_kernel": "adamw",
-    "pack_kernel": "pack",
+    "scatter_kernel<2, (anonymous namespace)::PackSrc": "pack",
     "unpack_kernel": "unpack",
     "copy_kernel": "copy",
 }
@@ -230,7 +299,8 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
 
     def kname(n):
         for frag in KERNELS:
-            if "(anonymous namespace)::" + frag + "(" in n or "(anonymous namespace)::" + frag + "<" in n:
+            i = n.find("(anonymous namespace)::" + frag)
+            if i >= 0 and n[i + len("(anonymous namespace)::" + frag):][:1] in ("(", "<", ">"):
                 return frag
         return None
 
@@ -254,10 +324,11 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     S, N, A = 842301440, 8, 4
     alg = {"reduce_chunk_kernel": (2 * N * A + 4) * S, "adamw_wave_kernel": 30 * S,
            "reduce_adamw_chunk_kernel": (2 * N * A + 26) * S,
+           "reduce_rs_chunk_kernel": (2 * N * A + 4) * S,
            "copy_kernel": 2 * copy_bytes}
     P_blk = 202383360
-    alg["pack_kernel"] = None    # per group; blocks and root differ: reported as totals below
-    alg["unpack_kernel"] = None
+    for k in KERNELS:
+        alg.setdefault(k, None)   # pack / unpack / reshard: per group, reported as means below
     rec = {"kernel_source_sha256_16": kernel_source_hash(), "fetch_scale": f_fetch, "write_scale": f_write,
            "kernels": {}}
     rows = []
@@ -289,9 +360,10 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     for k, st, fe, wr, a in rows:
         md.append(f"| {k} | {st['calls']} | {st['avg_ns'] / 1e3:.1f} us | {fe / 1e9:.3f} GB | {wr / 1e9:.3f} GB | "
                   + (f"{a / 1e9:.3f} GB | {(fe + wr) / a:.3f} | {a / st['avg_ns']:.0f} |" if a else "per group (see below) | - | - |"))
-    if "pack_kernel" in stats:
+    pk = "scatter_kernel<2, (anonymous namespace)::PackSrc"
+    if pk in stats:
         P = 6738411520
-        for k in ("pack_kernel", "unpack_kernel"):
+        for k in (pk, "unpack_kernel"):
             tot_alg = (2 * P + 2 * P) / 33
             md.append("")
             md.append(f"{k}: mean over the 33 group launches of one step: {stats[k]['avg_ns'] / 1e3:.1f} us, "
@@ -372,12 +444,14 @@ def main():
     torch.cuda.synchronize()
     fused_ms = sum(e[0].elapsed_time(e[1]) for e in fz) / args.steps
     fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
+    extra = extra_measurements(W, args.steps)
     ceiling = copy_ceiling(fs)
 
     kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
                                   "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
                                   "frac_hbm_peak": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                   "step_ms_with_fused": round(ms["pack"] + ms["unpack"] + fused_ms, 4)}
+    kern.update(extra)
     red_gbps = alg["reduce"] / (ms["reduce"] * 1e-3) / 1e9
     traffic = traffic_for("reduce", alg["reduce"])
     out = {

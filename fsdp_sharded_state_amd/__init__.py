@@ -90,6 +90,12 @@ def lib() -> ctypes.CDLL:
     L.fs_unpack.argtypes = [vp, vp, vp, vp]
     L.fs_reduce_shard.argtypes = [i64, i32, i32, vp, vp, vp]
     L.fs_adamw_step.argtypes = [i64, vp, vp, vp, vp, i32, vp, ctypes.POINTER(AdamWHparams), vp]
+    L.fs_reshard_plan.argtypes = [vp, vp, ctypes.POINTER(vp)]
+    L.fs_reshard_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.fs_reshard_upload.argtypes = [vp, vp, sz, vp]
+    L.fs_reshard.argtypes = [vp, vp, vp, vp]
+    L.fs_reshard_destroy.argtypes = [vp]
+    L.fs_reshard_destroy.restype = None
     L.fs_reduce_shard_ex.argtypes = [i64, i32, i32, i32, vp, vp, vp]
     L.fs_pack_cast.argtypes = [vp, vp, i32, vp, i32, vp]
     L.fs_reduce_adamw_step.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamWHparams), vp]
@@ -98,7 +104,8 @@ def lib() -> ctypes.CDLL:
     L.fs_last_error.restype = ctypes.c_char_p
     for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
                  "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_reduce_adamw_step",
-                 "fs_reduce_shard_ex", "fs_pack_cast",
+                 "fs_reduce_shard_ex", "fs_pack_cast", "fs_reshard_plan", "fs_reshard_info",
+                 "fs_reshard_upload", "fs_reshard",
                  "fs_copy_bytes"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -221,6 +228,49 @@ def fs_plan(shapes: Sequence[Sequence[int]], dtype="bf16", world: int = 1, use_o
     _check(lib().fs_plan(n, ndim, dims, _dtype_code(dtype), int(world), int(bool(use_orig_params)),
                          _mode_code(mode), int(grad_acc), ctypes.byref(h)))
     return Plan(h.value)
+
+
+class Reshard:
+    """Relayout plan from one group plan to another (wraps fs_reshard_t)."""
+
+    def __init__(self, src: "Plan", dst: "Plan"):
+        h = ctypes.c_void_p()
+        _check(lib().fs_reshard_plan(src._h, dst._h, ctypes.byref(h)))
+        self._h = h
+        self._destroy = lib().fs_reshard_destroy
+        self.src_info, self.dst_info = src.info, dst.info
+        wb, ns = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().fs_reshard_info(h, ctypes.byref(wb), ctypes.byref(ns)))
+        self.workspace_bytes, self.n_segments = wb.value, ns.value
+        self.workspace: Optional[torch.Tensor] = None
+
+    def close(self):
+        h = self.__dict__.pop("_h", None)
+        if h is not None and h.value:
+            self._destroy(h)
+
+    def __del__(self):
+        self.close()
+
+    def upload(self, device="cuda", stream=None) -> "Reshard":
+        ws = torch.empty(max(16, self.workspace_bytes), dtype=torch.uint8, device=device)
+        _check(lib().fs_reshard_upload(self._h, ws.data_ptr(), ws.numel(), _stream(stream)))
+        self.workspace = ws
+        return self
+
+
+def fs_reshard_plan(src: "Plan", dst: "Plan") -> Reshard:
+    """Plan moving a group's gathered buffer from plan src (N) to plan dst (N')."""
+    return Reshard(src, dst)
+
+
+def fs_reshard(r: Reshard, src_gathered: torch.Tensor, dst_gathered: torch.Tensor, stream=None):
+    """dst_gathered <- src_gathered re-laid from the src plan to the dst plan."""
+    if src_gathered.numel() != r.src_info.gathered_numel or dst_gathered.numel() != r.dst_info.gathered_numel:
+        raise ValueError("fs_reshard: buffer sizes do not match the plans")
+    _check(lib().fs_reshard(r._h, _dev_ptr(src_gathered, "src_gathered") if src_gathered.numel() else 0,
+                            _dev_ptr(dst_gathered, "dst_gathered") if dst_gathered.numel() else 0,
+                            _stream(stream)))
 
 
 def fs_pack(plan: Plan, params: Sequence[torch.Tensor], out: torch.Tensor, rank: int = -1, stream=None):

@@ -230,12 +230,16 @@ __device__ __forceinline__ void copy_run(char *dst, const char *src, int nblk) {
     }
 }
 
-template <int W>
-__global__ __launch_bounds__(kThreads) void pack_kernel(const Segment *__restrict__ segs,
-                                                        const Tile *__restrict__ tiles,
-                                                        const void *const *__restrict__ params,
-                                                        char *__restrict__ out, int64_t dst_lo,
-                                                        int64_t dst_hi) {
+// Destination-driven copy into one contiguous buffer (`out`, addressed from
+// virtual element dst_lo): the gathered buffer for pack (Src = PackSrc, one
+// source per parameter) and for reshard (Src = UnpackSrc, one source: the
+// other plan's gathered buffer).  Elements no segment covers are written as
+// zero.
+template <int W, class Src>
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const Segment *__restrict__ segs,
+                                                           const Tile *__restrict__ tiles, Src S,
+                                                           char *__restrict__ out, int64_t dst_lo,
+                                                           int64_t dst_hi) {
     constexpr int VEC = 16 / W;
     __shared__ TileLds L;
     const Tile t = tiles[blockIdx.x];
@@ -244,11 +248,10 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const Segment *__restric
     const bool dst_full = t.x_begin >= dst_lo && x_end <= dst_hi &&
                           (reinterpret_cast<uintptr_t>(dst0) & 15) == 0;
     if (dst_full && t.run_buf >= 0) {   // the whole tile is one contiguous run
-        copy_run(dst0, reinterpret_cast<const char *>(params[t.run_buf]) + t.run_src * W, t.nblk);
+        copy_run(dst0, S(t.run_buf) + t.run_src * W, t.nblk);
         return;
     }
     stage_tile<W>(L, segs, t);
-    const PackSrc S{params};
 #pragma unroll 2
     for (int u = 0; u < fsi::kBlocksPerThread; ++u) {
         const int b = u * kThreads + threadIdx.x;
@@ -1061,13 +1064,66 @@ extern "C" int fs_pack(fs_plan_t plan, const void *const *params, void *out, int
     (void)hipGetLastError();
     // `out` is addressed from the virtual element `lo` on
     char *base = static_cast<char *>(out);
+    const PackSrc src{params};
     if (I.elem_bytes == 2)
-        hipLaunchKernelGGL(pack_kernel<2>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
-                           params, base, lo, hi);
+        hipLaunchKernelGGL((scatter_kernel<2, PackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+                           tiles, src, base, lo, hi);
     else
-        hipLaunchKernelGGL(pack_kernel<4>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
-                           params, base, lo, hi);
+        hipLaunchKernelGGL((scatter_kernel<4, PackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+                           tiles, src, base, lo, hi);
     return check_launch("fs_pack");
+}
+
+extern "C" int fs_reshard_upload(fs_reshard_t r, void *workspace, size_t bytes, hipStream_t stream) {
+    fsi::clear_error();
+    if (!r || !workspace) return fsi::fail(FS_E_INVAL, "fs_reshard_upload: NULL argument");
+    if (misaligned(workspace, 16)) return fsi::fail(FS_E_ALIGN, "fs_reshard_upload: workspace must be 16-byte aligned");
+    if ((int64_t)bytes < r->ws_bytes)
+        return fsi::fail(FS_E_INVAL, "fs_reshard_upload: workspace too small (%zu < %lld bytes)", bytes,
+                         (long long)r->ws_bytes);
+    char *ws = static_cast<char *>(workspace);
+    if (!r->segs.empty()) {
+        hipError_t e = hipMemcpyAsync(ws + r->ws_segs, r->segs.data(), r->segs.size() * sizeof(Segment),
+                                      hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_reshard_upload: copy failed: %s", hipGetErrorString(e));
+    }
+    if (!r->tiles.empty()) {
+        hipError_t e = hipMemcpyAsync(ws + r->ws_tiles, r->tiles.data(), r->tiles.size() * sizeof(Tile),
+                                      hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_reshard_upload: copy failed: %s", hipGetErrorString(e));
+    }
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_reshard_upload: sync failed: %s", hipGetErrorString(e));
+    r->dev_ws = workspace;
+    return FS_OK;
+}
+
+extern "C" int fs_reshard(fs_reshard_t r, const void *src_gathered, void *dst_gathered, hipStream_t stream) {
+    fsi::clear_error();
+    if (!r) return fsi::fail(FS_E_INVAL, "fs_reshard: plan is NULL");
+    if (!r->dev_ws) return fsi::fail(FS_E_INVAL, "fs_reshard: no uploaded workspace (call fs_reshard_upload)");
+    if (r->dst_gathered == 0) return FS_OK;
+    if (!dst_gathered || (r->src_gathered > 0 && !src_gathered)) return fsi::fail(FS_E_INVAL, "fs_reshard: NULL buffer");
+    if (misaligned(dst_gathered, r->elem_bytes) || (src_gathered && misaligned(src_gathered, r->elem_bytes)))
+        return fsi::fail(FS_E_ALIGN, "fs_reshard: buffers must be aligned to %d bytes", r->elem_bytes);
+    if (ranges_overlap(src_gathered, r->src_gathered * r->elem_bytes, dst_gathered, r->dst_gathered * r->elem_bytes))
+        return fsi::fail(FS_E_INVAL, "fs_reshard: source and destination overlap");
+    const char *ws = static_cast<const char *>(r->dev_ws);
+    const Segment *segs = reinterpret_cast<const Segment *>(ws + r->ws_segs);
+    const Tile *tiles = reinterpret_cast<const Tile *>(ws + r->ws_tiles);
+    const int64_t ntiles = (int64_t)r->tiles.size();
+    if (ntiles == 0) return FS_OK;
+    if (ntiles > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_reshard: too many tiles for one launch");
+    (void)hipGetLastError();
+    const UnpackSrc src{static_cast<const char *>(src_gathered)};
+    char *dst = static_cast<char *>(dst_gathered);
+    if (r->elem_bytes == 2)
+        hipLaunchKernelGGL((scatter_kernel<2, UnpackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+                           tiles, src, dst, (int64_t)0, r->dst_gathered);
+    else
+        hipLaunchKernelGGL((scatter_kernel<4, UnpackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+                           tiles, src, dst, (int64_t)0, r->dst_gathered);
+    return check_launch("fs_reshard");
 }
 
 extern "C" int fs_unpack(fs_plan_t plan, const void *gathered, void *const *params, hipStream_t stream) {

@@ -53,11 +53,13 @@ bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow
 
 int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 
+}  // namespace
+
 // Cut the grid of blocks [lo + k*vec, lo + (k+1)*vec) covering [lo, hi) into
 // tiles of at most kTileBlocks blocks that overlap at most kTileSegs segments.
 // `segs` is sorted by vx and non-overlapping.
-void build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec,
-                 std::vector<Tile> &out) {
+void fsi::build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec,
+                      std::vector<Tile> &out) {
     if (hi <= lo) return;
     const int64_t nblocks = ceil_div(hi - lo, vec);
     const int64_t nseg = (int64_t)segs.size();
@@ -109,6 +111,8 @@ void build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int v
         b0 = b1;
     }
 }
+
+namespace {
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -259,13 +263,13 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
                   [](const Segment &a, const Segment &b) { return a.vx < b.vx; });
 
         // ---- tiles
-        build_tiles(ps, 0, gathered, vec, p->pack_tiles_all);
+        fsi::build_tiles(ps, 0, gathered, vec, p->pack_tiles_all);
         p->rank_tile_off.push_back(0);
         for (int32_t r = 0; r < world; ++r) {
-            build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, p->pack_tiles_rank);
+            fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, p->pack_tiles_rank);
             p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
         }
-        build_tiles(p->unpack_segs, 0, vb, vec, p->unpack_tiles);
+        fsi::build_tiles(p->unpack_segs, 0, vb, vec, p->unpack_tiles);
         for (Tile &t : p->unpack_tiles)
             if (t.run_buf >= 0) t.run_dst = t.x_begin - p->bufinfo[t.run_buf].vbase;
 
@@ -352,3 +356,98 @@ extern "C" int fs_plan_segments(fs_plan_t plan, fs_segment_t *out, int64_t cap, 
 }
 
 extern "C" void fs_plan_destroy(fs_plan_t plan) { delete plan; }
+
+// ---------------------------------------------------------------- reshard --
+//
+// Re-shard one group from plan `src` (N ranks, one mode) to plan `dst` (N'
+// ranks, same or other mode): every parameter element moves from its place
+// in src's gathered buffer to its place in dst's.  Sources: "FSDP1 vs FSDP2",
+// memory and engineering section (FSDP2's shards are the sharded state dict,
+// FSDP1 must unshard for one); the FSDP tutorial page (m.xxqk.cn), section
+// 3.3 (sharded checkpoints do not carry over between card counts as they
+// are -- they must be re-sharded).  Both plans must list the same
+// parameters with the same element size.  Lowering: for each parameter, the
+// two plans' runs over its elements are intersected into pieces (dst
+// gathered offset, src gathered offset, length), merged when contiguous in
+// both, sorted by destination, and tiled like a pack.
+
+extern "C" int fs_reshard_plan(fs_plan_t src, fs_plan_t dst, fs_reshard_t *out) {
+    fsi::clear_error();
+    if (!src || !dst || !out) return fsi::fail(FS_E_INVAL, "fs_reshard_plan: NULL argument");
+    *out = nullptr;
+    if (src->info.n_params != dst->info.n_params)
+        return fsi::fail(FS_E_INVAL, "fs_reshard_plan: the plans list %d and %d parameters", src->info.n_params,
+                         dst->info.n_params);
+    if (src->info.elem_bytes != dst->info.elem_bytes)
+        return fsi::fail(FS_E_DTYPE, "fs_reshard_plan: the plans have different element sizes");
+    const int32_t np = src->info.n_params;
+    for (int32_t i = 0; i < np; ++i)
+        if (src->params[i].numel != dst->params[i].numel)
+            return fsi::fail(FS_E_INVAL, "fs_reshard_plan: parameter %d has %lld vs %lld elements", i,
+                             (long long)src->params[i].numel, (long long)dst->params[i].numel);
+    fs_reshard_s *r = new (std::nothrow) fs_reshard_s();
+    if (!r) return fsi::fail(FS_E_NOMEM, "fs_reshard_plan: out of host memory");
+    try {
+        r->elem_bytes = src->info.elem_bytes;
+        r->vec = 16 / r->elem_bytes;
+        r->src_gathered = src->info.gathered_numel;
+        r->dst_gathered = dst->info.gathered_numel;
+        // runs of each parameter, in parameter-element order: (gathered offset, param offset, len)
+        auto runs_of = [np](const fs_plan_s *p) {
+            std::vector<std::vector<Segment>> by(np);
+            for (const Segment &sg : p->pack_segs) by[sg.buf].push_back(sg);
+            for (auto &v : by)
+                std::sort(v.begin(), v.end(), [](const Segment &a, const Segment &b) { return a.src_off < b.src_off; });
+            return by;
+        };
+        const auto sr = runs_of(src), dr = runs_of(dst);
+        std::vector<Segment> pieces;
+        for (int32_t i = 0; i < np; ++i) {
+            size_t a = 0, b = 0;
+            int64_t off = 0;
+            const int64_t n = src->params[i].numel;
+            while (off < n) {
+                const Segment &s0 = sr[i][a], &d0 = dr[i][b];
+                const int64_t ls = s0.src_off + s0.len - off, ld = d0.src_off + d0.len - off;
+                const int64_t len = std::min(ls, ld);
+                Segment pc{d0.vx + (off - d0.src_off), s0.vx + (off - s0.src_off), len, 0, d0.rank};
+                if (!pieces.empty()) {
+                    Segment &q = pieces.back();
+                    if (q.vx + q.len == pc.vx && q.src_off + q.len == pc.src_off) {
+                        q.len += len;
+                        pc.len = 0;
+                    }
+                }
+                if (pc.len) pieces.push_back(pc);
+                off += len;
+                if (len == ls) ++a;
+                if (len == ld) ++b;
+            }
+        }
+        std::sort(pieces.begin(), pieces.end(), [](const Segment &x, const Segment &y) { return x.vx < y.vx; });
+        if ((int64_t)pieces.size() > INT32_MAX) {
+            delete r;
+            return fsi::fail(FS_E_OVERFLOW, "fs_reshard_plan: too many copy segments");
+        }
+        r->segs = std::move(pieces);
+        fsi::build_tiles(r->segs, 0, r->dst_gathered, r->vec, r->tiles);
+        r->ws_segs = 0;
+        r->ws_tiles = align_up((int64_t)r->segs.size() * (int64_t)sizeof(Segment), 256);
+        r->ws_bytes = std::max<int64_t>(256, r->ws_tiles + align_up((int64_t)r->tiles.size() * (int64_t)sizeof(Tile), 256));
+    } catch (const std::bad_alloc &) {
+        delete r;
+        return fsi::fail(FS_E_NOMEM, "fs_reshard_plan: out of host memory");
+    }
+    *out = r;
+    return FS_OK;
+}
+
+extern "C" int fs_reshard_info(fs_reshard_t r, int64_t *workspace_bytes, int64_t *n_segments) {
+    fsi::clear_error();
+    if (!r) return fsi::fail(FS_E_INVAL, "fs_reshard_info: NULL argument");
+    if (workspace_bytes) *workspace_bytes = r->ws_bytes;
+    if (n_segments) *n_segments = (int64_t)r->segs.size();
+    return FS_OK;
+}
+
+extern "C" void fs_reshard_destroy(fs_reshard_t r) { delete r; }

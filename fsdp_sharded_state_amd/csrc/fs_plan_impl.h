@@ -25,8 +25,24 @@ struct fs_plan_s {
     int dev_id = -1;
 };
 
+// Relayout of one group's gathered buffer from one plan to another (other N,
+// other mode): segments in destination-gathered order whose source offsets
+// index the source plan's gathered buffer, and a tile index over the
+// destination.
+struct fs_reshard_s {
+    int32_t elem_bytes = 0;
+    int vec = 0;
+    int64_t src_gathered = 0, dst_gathered = 0;
+    std::vector<fsi::Segment> segs;
+    std::vector<fsi::Tile> tiles;
+    int64_t ws_segs = 0, ws_tiles = 0, ws_bytes = 0;
+    void *dev_ws = nullptr;
+};
+
 namespace fsi {
 // Record a message for fs_last_error() and return `code`.
 int fail(int code, const char *fmt, ...);
 void clear_error();
+// Tile a sorted, non-overlapping segment list (see fs_plan.cpp).
+void build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec, std::vector<Tile> &out);
 }  // namespace fsi

@@ -59,7 +59,8 @@ typedef enum {
     FS_FSDP2_PER_PARAM = 2  /* each parameter chunked on dim 0          [FvF section 03] */
 } fs_mode;
 
-typedef struct fs_plan_s *fs_plan_t; /* opaque; host memory owned by the library */
+typedef struct fs_plan_s *fs_plan_t;       /* opaque; host memory owned by the library */
+typedef struct fs_reshard_s *fs_reshard_t; /* opaque; host memory owned by the library */
 
 /* Summary of a plan.  Counts are in elements of the plan's dtype. */
 typedef struct {
@@ -218,6 +219,39 @@ int fs_pack(fs_plan_t plan, const void *const *params, void *out, int32_t rank,
  */
 int fs_unpack(fs_plan_t plan, const void *gathered, void *const *params,
               hipStream_t stream);
+
+/*
+ * fs_reshard_plan -- plan moving one group's gathered buffer from plan `src`
+ * (N ranks) to plan `dst` (N' ranks; FSDP1 or FSDP2 on either side), host
+ * only.  Every parameter element goes from its place in src's gathered
+ * buffer to its place in dst's; dst's pads are written as zero.  Sources:
+ * [FvF] memory and engineering section (FSDP2's shards are the sharded state
+ * dict; FSDP1 must unshard to save one); the FSDP tutorial page (m.xxqk.cn),
+ * section 3.3 (sharded checkpoints do not carry over between card counts:
+ * they must be re-sharded).  With fp32 plans the same call re-shards fp32
+ * optimizer state (master, m, v).
+ * Errors: FS_E_INVAL (NULL, different parameter lists), FS_E_DTYPE
+ * (different element sizes), FS_E_OVERFLOW, FS_E_NOMEM.
+ */
+int fs_reshard_plan(fs_plan_t src, fs_plan_t dst, fs_reshard_t *out);
+
+/* fs_reshard_info -- device workspace bytes and copy-segment count (either
+ * output may be NULL). */
+int fs_reshard_info(fs_reshard_t r, int64_t *workspace_bytes, int64_t *n_segments);
+
+/* fs_reshard_upload -- as fs_plan_upload, for a reshard plan. */
+int fs_reshard_upload(fs_reshard_t r, void *workspace, size_t bytes, hipStream_t stream);
+
+/*
+ * fs_reshard -- dst_gathered (device, dst's gathered_numel elements) <- the
+ * re-sharded src_gathered (device, src's gathered_numel elements).  Pads of
+ * src are not read.  Errors: FS_E_INVAL (not uploaded, NULL, overlapping
+ * buffers), FS_E_ALIGN, FS_E_HIP.
+ */
+int fs_reshard(fs_reshard_t r, const void *src_gathered, void *dst_gathered, hipStream_t stream);
+
+/* fs_reshard_destroy -- free a reshard plan (NULL is a no-op). */
+void fs_reshard_destroy(fs_reshard_t r);
 
 /*
  * fs_reduce_shard -- this rank's averaged fp32 gradient shard [DPZ section

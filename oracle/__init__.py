@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_reduce.restype = None
         L.oracle_reduce_bf16rs.argtypes = [i64, i32, i32, vp, vp]
         L.oracle_reduce_bf16rs.restype = None
+        L.oracle_reshard.argtypes = [vp, vp, vp, vp]
+        L.oracle_reshard.restype = None
         L.oracle_pack_cast.argtypes = [vp, vp, vp, i32]
         L.oracle_pack_cast.restype = None
         L.oracle_adamw.argtypes = [i64, vp, vp, vp, vp, i32, vp,
@@ -233,6 +235,22 @@ def pack_cast(layout: Layout, params: Sequence[np.ndarray], rank: int = -1) -> n
     c = layout._c()
     lib().oracle_pack_cast(ctypes.byref(c), ptrs, _ptr(out), int(rank))
     return out[:size]
+
+
+def reshard(src_layout: Layout, dst_layout: Layout, gathered: np.ndarray) -> np.ndarray:
+    """Move a gathered buffer from src_layout to dst_layout (same parameters,
+    same element size); dst pads are zero."""
+    assert src_layout.elem_bytes == dst_layout.elem_bytes
+    assert list(src_layout.numel) == list(dst_layout.numel)
+    dt = np.uint16 if src_layout.elem_bytes == 2 else np.uint32
+    g = np.ascontiguousarray(gathered).view(dt).reshape(-1)
+    assert g.size == src_layout.gathered_numel
+    out = np.empty(max(1, dst_layout.gathered_numel), dt)
+    cs, cd = src_layout._c(), dst_layout._c()
+    keep = (src_layout._keep, dst_layout._keep)   # noqa: F841 (arrays behind the structs)
+    gsrc = g if g.size else np.zeros(1, dt)
+    lib().oracle_reshard(ctypes.byref(cs), ctypes.byref(cd), _ptr(gsrc), _ptr(out))
+    return out[:dst_layout.gathered_numel]
 
 
 def unpack(layout: Layout, gathered: np.ndarray) -> List[np.ndarray]:

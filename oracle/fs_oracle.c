@@ -258,6 +258,26 @@ void oracle_unpack(const oracle_layout *L, const void *gathered,
     }
 }
 
+/*
+ * Re-shard one group's gathered buffer from layout Ls (N ranks) to layout Ld
+ * (N' ranks, either mode) ["FSDP1 vs FSDP2", memory and engineering
+ * section: FSDP2's shards are the sharded state dict; the FSDP tutorial page
+ * (m.xxqk.cn), section 3.3: sharded checkpoints must be re-sharded to load at
+ * another card count]: start from a zero-filled output and copy every
+ * parameter element from its place under Ls to its place under Ld.
+ */
+void oracle_reshard(const oracle_layout *Ls, const oracle_layout *Ld,
+                    const void *src, void *dst)
+{
+    const int64_t w = Ld->elem_bytes;
+    memset(dst, 0, (size_t)((int64_t)Ld->world * Ld->shard * w));
+    for (int32_t i = 0; i < Ld->n_params; ++i)
+        for (int64_t e = 0; e < Ld->numel[i]; ++e)
+            memcpy((unsigned char *)dst + gathered_index(Ld, i, e) * w,
+                   (const unsigned char *)src + gathered_index(Ls, i, e) * w,
+                   (size_t)w);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                           */
 /* ------------------------------------------------------------------------ */

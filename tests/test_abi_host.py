@@ -281,3 +281,23 @@ def test_seven_b_strategy_table_from_plans():
     assert comm == pytest.approx(36.75e9 * P / 7e9, rel=1e-12)
     ddp_bopt8 = sum(p.ledger_ddp_bytes for p in plans) - 4 * P
     assert ddp_bopt8 == pytest.approx(84e9 * P / 7e9, rel=1e-12)
+
+
+def test_reshard_plan_validation():
+    L = fs.lib()
+    a = fs.fs_plan([(3,), (5,)], "bf16", 4, True, "fsdp1")
+    b = fs.fs_plan([(3,), (6,)], "bf16", 2, False, "fsdp2")
+    c = fs.fs_plan([(3,), (5,)], "fp32", 2, False, "fsdp2")
+    d = fs.fs_plan([(3,)], "bf16", 2, False, "fsdp2")
+    h = ctypes.c_void_p()
+    assert L.fs_reshard_plan(a._h, b._h, ctypes.byref(h)) == fs.FS_E_INVAL
+    assert L.fs_reshard_plan(a._h, c._h, ctypes.byref(h)) == fs.FS_E_DTYPE
+    assert L.fs_reshard_plan(a._h, d._h, ctypes.byref(h)) == fs.FS_E_INVAL
+    assert L.fs_reshard_plan(None, a._h, ctypes.byref(h)) == fs.FS_E_INVAL
+    r = fs.fs_reshard_plan(a, fs.fs_plan([(3,), (5,)], "bf16", 3, False, "fsdp2"))
+    assert r.n_segments >= 2 and r.workspace_bytes >= 256
+    assert L.fs_reshard(r._h, ctypes.c_void_p(16), ctypes.c_void_p(1 << 20), None) == fs.FS_E_INVAL  # not uploaded
+    # identical layouts collapse to one segment per parameter run
+    same = fs.fs_reshard_plan(fs.fs_plan([(40,), (24,)], "bf16", 8, False, "fsdp1"),
+                              fs.fs_plan([(40,), (24,)], "bf16", 8, False, "fsdp1"))
+    assert same.n_segments == 1

@@ -446,3 +446,47 @@ def test_pack_cast_bitexact(case, shift):
     S.check()
     np.testing.assert_array_equal(bits(G.t), ref)
     np.testing.assert_array_equal(bits(S.t), ref[r * plan.shard_numel:(r + 1) * plan.shard_numel])
+
+
+# ---------------------------------------------------------------- reshard --
+
+def _lay(kind, shapes, dt, N, uo):
+    return (kind, shapes, dt, N, uo)
+
+
+st97 = [(n,) for n in synth.padding_stress_numels()]
+RESHARD_CASES = [
+    ("block_f2_8to4", ("fsdp2", synth.llama_block_shapes(), "bf16", 8, False), ("fsdp2", None, None, 4, False)),
+    ("mixed_f2_8to3", ("fsdp2", [(6, 3), (1,), (0, 2), (9,), (), (17, 5)], "bf16", 8, False), ("fsdp2", None, None, 3, False)),
+    ("mlp_f1T4_to_f2_8", ("fsdp1", synth.mlp_tiny_shapes(), "bf16", 4, True), ("fsdp2", None, None, 8, False)),
+    ("stress_f1F8_to_f1T5", ("fsdp1", st97, "bf16", 8, False), ("fsdp1", None, None, 5, True)),
+    ("stress_fp32_f1T8_to_f2_16", ("fsdp1", st97, "fp32", 8, True), ("fsdp2", None, None, 16, False)),
+    ("segments_f1F8_to_f1F7", ("fsdp1", [(k % 5 + 1,) for k in range(700)], "bf16", 8, False), ("fsdp1", None, None, 7, False)),
+    ("state_fp32_f2_8to16", ("fsdp2", synth.llama_block_shapes(1024, 2816), "fp32", 8, False), ("fsdp2", None, None, 16, False)),
+]
+
+
+@pytest.mark.parametrize("case", RESHARD_CASES, ids=lambda c: c[0])
+@pytest.mark.parametrize("shift", [0, 1])
+def test_reshard_bitexact(case, shift):
+    name, (ks, shapes, dt, Ns, uos), (kd, _, _, Nd, uod) = case
+    say("reshard", name, shift)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    ps = fs.fs_plan(shapes, dt, Ns, uos, ks).upload()
+    pd = fs.fs_plan(shapes, dt, Nd, uod, kd).upload()
+    Ls, Ld = _olayout(ks, shapes, dt, Ns, uos), _olayout(kd, shapes, dt, Nd, uod)
+    params = _params(shapes, dt, seed=53)
+    src_bits = oracle.pack(Ls, [bits(p.t) for p in params])
+    # the source's pads hold garbage: they must not be read
+    mask = np.ones(src_bits.size, bool)
+    mask[Ls.index_map()] = False
+    src_bits[mask] = 0x7FFF if dt == "bf16" else 0x7FFFFFFF
+    ref = oracle.reshard(Ls, Ld, src_bits)
+    src = Guarded(ps.gathered_numel, tdt, shift=shift, fill=from_bits(src_bits, tdt))
+    dst = Guarded(pd.gathered_numel, tdt, shift=shift)
+    r = fs.fs_reshard_plan(ps, pd).upload()
+    fs.fs_reshard(r, src.t, dst.t)
+    torch.cuda.synchronize()
+    dst.check()
+    src.check()
+    np.testing.assert_array_equal(bits(dst.t), ref)
