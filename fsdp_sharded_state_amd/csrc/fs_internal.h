@@ -27,7 +27,12 @@ namespace fsi {
 #endif
 constexpr int kThreads = 256;                 // threads per workgroup (4 waves of 64)
 constexpr int kBlocksPerThread = FS_TILE_BLOCKS_PER_THREAD;   // 16-byte blocks per thread per tile
-constexpr int kTileBlocks = kThreads * kBlocksPerThread;
+constexpr int kTileBlocks = kThreads * kBlocksPerThread;      // unpack tiles (16 KB of destination)
+#ifndef FS_PACK_TILE_BLOCKS
+#define FS_PACK_TILE_BLOCKS (kTileBlocks / 2)
+#endif
+constexpr int kPackTileBlocks = FS_PACK_TILE_BLOCKS;          // pack / reshard tiles (8 KB of destination)
+static_assert(kPackTileBlocks <= kTileBlocks, "a tile must fit the kernel's per-thread loop");
 constexpr int kTileSegs = 256;                // max segments staged in LDS per tile
 
 struct Segment {        // 32 bytes, sorted by vx, non-overlapping, len > 0

@@ -509,8 +509,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nter
     }
 }
 
-constexpr int kRedGroups = 16;
-constexpr int64_t kRedChunk = (int64_t)kThreads * 4 * kRedGroups;   // 16384 elements
+#ifndef FS_RED_GROUPS
+#define FS_RED_GROUPS 16
+#endif
+constexpr int kRedGroups = FS_RED_GROUPS;
+constexpr int64_t kRedChunk = (int64_t)kThreads * 4 * kRedGroups;   // 16384 elements by default
 
 __device__ __forceinline__ void add_bf16x4(float *acc, u32x2 v) {
     acc[0] = acc[0] + __uint_as_float(v.x << 16);
@@ -745,7 +748,10 @@ __device__ __forceinline__ u32x4 u4(const float o[4]) {
 // consecutive elements; lane l holds groups of 4 at offsets q*256 + 4l, so
 // every load and store instruction of the wave covers 1 KB (fp32) or 512 B
 // (bf16) contiguous -- no instruction leaves holes in a cache line.
-constexpr int kAdamGroups = 4;
+#ifndef FS_ADAM_GROUPS
+#define FS_ADAM_GROUPS 4
+#endif
+constexpr int kAdamGroups = FS_ADAM_GROUPS;
 constexpr int64_t kAdamChunk = (int64_t)kThreads * 4 * kAdamGroups;   // 4096 elements per workgroup
 
 template <bool GRAD_BF16, bool HAS_P16>
@@ -817,10 +823,10 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t begin, i
 // instead of 2*A*N + 4 + 30.
 
 #ifndef FS_FUSED_GROUPS
-#define FS_FUSED_GROUPS 4
+#define FS_FUSED_GROUPS 8
 #endif
 #ifndef FS_FUSED_BATCH
-#define FS_FUSED_BATCH 2
+#define FS_FUSED_BATCH 4
 #endif
 constexpr int kFusedGroups = FS_FUSED_GROUPS;
 constexpr int kFusedBatch = FS_FUSED_BATCH < FS_FUSED_GROUPS ? FS_FUSED_BATCH : FS_FUSED_GROUPS;
@@ -858,6 +864,18 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
             acc[4 * u + 3] = __uint_as_float(o.w);
         }
     }
+    constexpr int NB = kFusedGroups / kFusedBatch;
+    float T[2][4 * kFusedBatch], M[2][4 * kFusedBatch], V[2][4 * kFusedBatch];
+    auto load_state = [&](int slot, int u0) {
+#pragma unroll
+        for (int q = 0; q < kFusedBatch; ++q) {
+            const int64_t e = base + (u0 + q) * kThreads * 4;
+            f4(ld16(reinterpret_cast<const char *>(th + e)), T[slot] + 4 * q);
+            f4(ld16(reinterpret_cast<const char *>(m + e)), M[slot] + 4 * q);
+            f4(ld16(reinterpret_cast<const char *>(v + e)), V[slot] + 4 * q);
+        }
+    };
+    load_state(0, 0);   // independent of the reduce: in flight during the slice loop
     if (t < nterms) load_groups_n<kFusedGroups>(xa, sa.p[t], base);
     while (t < nterms) {
         if (t + 1 < nterms) load_groups_n<kFusedGroups>(xb, sa.p[t + 1], base);
@@ -871,28 +889,24 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
     }
 #pragma unroll
     for (int e = 0; e < 4 * kFusedGroups; ++e) acc[e] = acc[e] / world;
-    // AdamW on the lane's groups, kFusedBatch groups (4*kFusedBatch elements) at a time
+    // AdamW on the lane's groups, kFusedBatch groups (4*kFusedBatch elements)
+    // at a time; batch b+1's state loads are issued before batch b's update
+    // (batch 0's before the slice loop), so they overlap the arithmetic.
 #pragma unroll
-    for (int u0 = 0; u0 < kFusedGroups; u0 += kFusedBatch) {
-        float T[4 * kFusedBatch], M[4 * kFusedBatch], V[4 * kFusedBatch];
+    for (int bi = 0; bi < NB; ++bi) {
+        const int slot = bi & 1, u0 = bi * kFusedBatch;
+        if (bi + 1 < NB) load_state(slot ^ 1, u0 + kFusedBatch);
 #pragma unroll
-        for (int q = 0; q < kFusedBatch; ++q) {
-            const int64_t e = base + (u0 + q) * kThreads * 4;
-            f4(ld16(reinterpret_cast<const char *>(th + e)), T + 4 * q);
-            f4(ld16(reinterpret_cast<const char *>(m + e)), M + 4 * q);
-            f4(ld16(reinterpret_cast<const char *>(v + e)), V + 4 * q);
-        }
-#pragma unroll
-        for (int k = 0; k < 4 * kFusedBatch; ++k) adam_elem(c, acc[4 * u0 + k], T[k], M[k], V[k]);
+        for (int k = 0; k < 4 * kFusedBatch; ++k) adam_elem(c, acc[4 * u0 + k], T[slot][k], M[slot][k], V[slot][k]);
 #pragma unroll
         for (int q = 0; q < kFusedBatch; ++q) {
             const int64_t e = base + (u0 + q) * kThreads * 4;
-            st16(reinterpret_cast<char *>(th + e), u4(T + 4 * q));
-            st16(reinterpret_cast<char *>(m + e), u4(M + 4 * q));
-            st16(reinterpret_cast<char *>(v + e), u4(V + 4 * q));
+            st16(reinterpret_cast<char *>(th + e), u4(T[slot] + 4 * q));
+            st16(reinterpret_cast<char *>(m + e), u4(M[slot] + 4 * q));
+            st16(reinterpret_cast<char *>(v + e), u4(V[slot] + 4 * q));
             if (HAS_P16) {
-                const u32x2 w = {(uint32_t)bf16_rne(T[4 * q]) | ((uint32_t)bf16_rne(T[4 * q + 1]) << 16),
-                                 (uint32_t)bf16_rne(T[4 * q + 2]) | ((uint32_t)bf16_rne(T[4 * q + 3]) << 16)};
+                const u32x2 w = {(uint32_t)bf16_rne(T[slot][4 * q]) | ((uint32_t)bf16_rne(T[slot][4 * q + 1]) << 16),
+                                 (uint32_t)bf16_rne(T[slot][4 * q + 2]) | ((uint32_t)bf16_rne(T[slot][4 * q + 3]) << 16)};
                 __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p16 + e));
             }
             if (HAS_G) st16(reinterpret_cast<char *>(gout + e), u4(acc + 4 * (u0 + q)));

@@ -56,9 +56,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 }  // namespace
 
 // Cut the grid of blocks [lo + k*vec, lo + (k+1)*vec) covering [lo, hi) into
-// tiles of at most kTileBlocks blocks that overlap at most kTileSegs segments.
+// tiles of at most tile_blocks blocks that overlap at most kTileSegs segments.
 // `segs` is sorted by vx and non-overlapping.
-void fsi::build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec,
+void fsi::build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec, int tile_blocks,
                       std::vector<Tile> &out) {
     if (hi <= lo) return;
     const int64_t nblocks = ceil_div(hi - lo, vec);
@@ -86,7 +86,7 @@ void fsi::build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, 
     while (b0 < nblocks) {
         int64_t x0 = lo + b0 * vec;
         s0 = first_ending_after(s0, x0);
-        int64_t b1 = std::min<int64_t>(nblocks, b0 + fsi::kTileBlocks);
+        int64_t b1 = std::min<int64_t>(nblocks, b0 + tile_blocks);
         if (s0 + fsi::kTileSegs < nseg) {
             // keep the (kTileSegs+1)-th segment out of this tile
             int64_t cut = (segs[s0 + fsi::kTileSegs].vx - lo) / vec;
@@ -263,13 +263,14 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
                   [](const Segment &a, const Segment &b) { return a.vx < b.vx; });
 
         // ---- tiles
-        fsi::build_tiles(ps, 0, gathered, vec, p->pack_tiles_all);
+        fsi::build_tiles(ps, 0, gathered, vec, fsi::kPackTileBlocks, p->pack_tiles_all);
         p->rank_tile_off.push_back(0);
         for (int32_t r = 0; r < world; ++r) {
-            fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, p->pack_tiles_rank);
+            fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, fsi::kPackTileBlocks,
+                             p->pack_tiles_rank);
             p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
         }
-        fsi::build_tiles(p->unpack_segs, 0, vb, vec, p->unpack_tiles);
+        fsi::build_tiles(p->unpack_segs, 0, vb, vec, fsi::kTileBlocks, p->unpack_tiles);
         for (Tile &t : p->unpack_tiles)
             if (t.run_buf >= 0) t.run_dst = t.x_begin - p->bufinfo[t.run_buf].vbase;
 
@@ -430,7 +431,7 @@ extern "C" int fs_reshard_plan(fs_plan_t src, fs_plan_t dst, fs_reshard_t *out) 
             return fsi::fail(FS_E_OVERFLOW, "fs_reshard_plan: too many copy segments");
         }
         r->segs = std::move(pieces);
-        fsi::build_tiles(r->segs, 0, r->dst_gathered, r->vec, r->tiles);
+        fsi::build_tiles(r->segs, 0, r->dst_gathered, r->vec, fsi::kPackTileBlocks, r->tiles);
         r->ws_segs = 0;
         r->ws_tiles = align_up((int64_t)r->segs.size() * (int64_t)sizeof(Segment), 256);
         r->ws_bytes = std::max<int64_t>(256, r->ws_tiles + align_up((int64_t)r->tiles.size() * (int64_t)sizeof(Tile), 256));

@@ -44,5 +44,6 @@ namespace fsi {
 int fail(int code, const char *fmt, ...);
 void clear_error();
 // Tile a sorted, non-overlapping segment list (see fs_plan.cpp).
-void build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec, std::vector<Tile> &out);
+void build_tiles(const std::vector<Segment> &segs, int64_t lo, int64_t hi, int vec, int tile_blocks,
+                 std::vector<Tile> &out);
 }  // namespace fsi
