@@ -1006,6 +1006,16 @@ int check_hparams(const char *what, const fs_adamw_hparams_t *hp) {
     return FS_OK;
 }
 
+// The tables live on the device they were uploaded to: launching from
+// another device would hand its kernels a foreign address.
+int check_device(const char *what, int dev_id) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fsi::fail(FS_E_HIP, "%s: no current device", what);
+    if (dev != dev_id)
+        return fsi::fail(FS_E_INVAL, "%s: the plan was uploaded on device %d, current device is %d", what, dev_id, dev);
+    return FS_OK;
+}
+
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 int check_launch(const char *what) {
@@ -1046,7 +1056,10 @@ extern "C" int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hip
     }
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_plan_upload: sync failed: %s", hipGetErrorString(e));
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fsi::fail(FS_E_HIP, "fs_plan_upload: no current device");
     plan->dev_ws = workspace;
+    plan->dev_id = dev;
     return FS_OK;
 }
 
@@ -1056,6 +1069,7 @@ extern "C" int fs_pack(fs_plan_t plan, const void *const *params, void *out, int
     if (!plan) return fsi::fail(FS_E_INVAL, "fs_pack: plan is NULL");
     const fs_plan_info_t &I = plan->info;
     if (!plan->dev_ws) return fsi::fail(FS_E_INVAL, "fs_pack: plan has no uploaded workspace (call fs_plan_upload)");
+    if (int rc = check_device("fs_pack", plan->dev_id)) return rc;
     if (rank < -1 || rank >= I.world) return fsi::fail(FS_E_INVAL, "fs_pack: rank %d out of range [-1, %d)", rank, I.world);
     const int64_t lo = rank < 0 ? 0 : (int64_t)rank * I.shard_numel;
     const int64_t hi = rank < 0 ? I.gathered_numel : lo + I.shard_numel;
@@ -1108,7 +1122,10 @@ extern "C" int fs_reshard_upload(fs_reshard_t r, void *workspace, size_t bytes, 
     }
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_reshard_upload: sync failed: %s", hipGetErrorString(e));
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fsi::fail(FS_E_HIP, "fs_reshard_upload: no current device");
     r->dev_ws = workspace;
+    r->dev_id = dev;
     return FS_OK;
 }
 
@@ -1116,6 +1133,7 @@ extern "C" int fs_reshard(fs_reshard_t r, const void *src_gathered, void *dst_ga
     fsi::clear_error();
     if (!r) return fsi::fail(FS_E_INVAL, "fs_reshard: plan is NULL");
     if (!r->dev_ws) return fsi::fail(FS_E_INVAL, "fs_reshard: no uploaded workspace (call fs_reshard_upload)");
+    if (int rc = check_device("fs_reshard", r->dev_id)) return rc;
     if (r->dst_gathered == 0) return FS_OK;
     if (!dst_gathered || (r->src_gathered > 0 && !src_gathered)) return fsi::fail(FS_E_INVAL, "fs_reshard: NULL buffer");
     if (misaligned(dst_gathered, r->elem_bytes) || (src_gathered && misaligned(src_gathered, r->elem_bytes)))
@@ -1145,6 +1163,7 @@ extern "C" int fs_unpack(fs_plan_t plan, const void *gathered, void *const *para
     if (!plan) return fsi::fail(FS_E_INVAL, "fs_unpack: plan is NULL");
     const fs_plan_info_t &I = plan->info;
     if (!plan->dev_ws) return fsi::fail(FS_E_INVAL, "fs_unpack: plan has no uploaded workspace (call fs_plan_upload)");
+    if (int rc = check_device("fs_unpack", plan->dev_id)) return rc;
     const int64_t ntiles = plan->ws.n_unpack_tiles;
     if (ntiles == 0 || I.total_numel == 0) return FS_OK;
     if (!gathered || !params) return fsi::fail(FS_E_INVAL, "fs_unpack: NULL pointer");
@@ -1298,6 +1317,7 @@ extern "C" int fs_pack_cast(fs_plan_t plan, const void *const *params, fs_dtype 
     if (!(param_dtype == FS_FP32 && I.dtype == FS_BF16))
         return fsi::fail(FS_E_UNSUPPORTED, "fs_pack_cast: only fp32 parameters into a bf16 layout are defined");
     if (!plan->dev_ws) return fsi::fail(FS_E_INVAL, "fs_pack_cast: plan has no uploaded workspace (call fs_plan_upload)");
+    if (int rc = check_device("fs_pack_cast", plan->dev_id)) return rc;
     if (rank < -1 || rank >= I.world)
         return fsi::fail(FS_E_INVAL, "fs_pack_cast: rank %d out of range [-1, %d)", rank, I.world);
     const int64_t lo = rank < 0 ? 0 : (int64_t)rank * I.shard_numel;

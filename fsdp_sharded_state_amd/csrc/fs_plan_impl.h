@@ -22,7 +22,7 @@ struct fs_plan_s {
     std::vector<fsi::BufInfo> bufinfo;
     fsi::WorkspaceLayout ws;
     void *dev_ws = nullptr;                    // bound by fs_plan_upload
-    int dev_id = -1;
+    int dev_id = -1;                           // device of dev_ws
 };
 
 // Relayout of one group's gathered buffer from one plan to another (other N,
@@ -36,7 +36,8 @@ struct fs_reshard_s {
     std::vector<fsi::Segment> segs;
     std::vector<fsi::Tile> tiles;
     int64_t ws_segs = 0, ws_tiles = 0, ws_bytes = 0;
-    void *dev_ws = nullptr;
+    void *dev_ws = nullptr;                    // bound by fs_reshard_upload
+    int dev_id = -1;
 };
 
 namespace fsi {

@@ -91,8 +91,9 @@ def test_fullsize_reduce_and_adamw(plans):
     assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm))
     assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv))
     assert np.all(np.abs(gp - rp.astype(np.int32)) <= 1)
-    say("full-size AdamW bit-exact fraction",
-        float(np.mean((gt.view(np.uint32) == rt.view(np.uint32)) & (gm.view(np.uint32) == rm.view(np.uint32)))))
+    inexact = np.mean((gt.view(np.uint32) != rt.view(np.uint32)) | (gm.view(np.uint32) != rm.view(np.uint32)) |
+                      (gv.view(np.uint32) != rv.view(np.uint32)))
+    assert inexact <= 1e-6, inexact
 
 
 @pytest.mark.parametrize("which", ["block0", "block31", "root"])

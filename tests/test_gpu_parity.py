@@ -314,9 +314,12 @@ def test_adamw_parity(case):
         assert np.all(np.abs(gp - rp.astype(np.int32)) <= 1)
     if n > 20:
         assert (bits(T.t)[:4] == 0).all() and (bits(M.t)[:4] == 0).all() and (bits(V.t)[:4] == 0).all()
-    exact = np.mean((bits(T.t) == rt.view(np.uint32)) & (bits(M.t) == rm.view(np.uint32)) &
-                    (bits(V.t) == rv.view(np.uint32)))
-    say("adamw bit-exact fraction", exact)
+    # beyond the tolerance: fp64 division and square root are correctly rounded
+    # on gfx950, so the kernel reproduces the oracle's fp64 evaluation bit for
+    # bit; allow one element in a million to differ in the last fp32 bit
+    inexact = np.mean((bits(T.t) != rt.view(np.uint32)) | (bits(M.t) != rm.view(np.uint32)) |
+                      (bits(V.t) != rv.view(np.uint32)))
+    assert inexact <= 1e-6, inexact
 
 
 # ------------------------------------------------------ fused reduce+AdamW --
@@ -367,6 +370,9 @@ def test_reduce_adamw_fused(case):
         np.testing.assert_array_equal(bits(Gout.t), ref_g.view(np.uint32))
     for a, b in ((T, T2), (M, M2), (V, V2)):
         np.testing.assert_array_equal(bits(a.t), bits(b.t))
+    inexact = np.mean((bits(T.t) != rt.view(np.uint32)) | (bits(M.t) != rm.view(np.uint32)) |
+                      (bits(V.t) != rv.view(np.uint32)))
+    assert inexact <= 1e-6, inexact
 
 
 def test_reduce_adamw_fused_needs_grad_out_beyond_32_terms():
