@@ -51,7 +51,13 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def setup(workload: str, seed: int = 4):
+def setup(workload: str, seed: int = 4, order: str = "params_first"):
+    """Allocate and fill every input in HBM.  By default the parameters and
+    gathered buffers come first, then the gradient slices and the fp32 shard
+    state, then the small plan tables.  The order fixes where the big buffers
+    land physically, and that moves HBM efficiency by several percent: on one
+    MI355X, AdamW ran at 6.45 TB/s with this order and at 5.7 TB/s with the
+    state allocated first ("state_first"); "plans_first" is in between."""
     import torch
 
     import fsdp_sharded_state_amd as fs
@@ -59,40 +65,56 @@ def setup(workload: str, seed: int = 4):
 
     n_blocks, d, f, kv, vocab, world, grad_acc = WORKLOADS[workload]
     groups = synth.llama_model_groups(n_blocks, d, f, vocab=vocab, kv=kv)
-    plans = [fs.fs_plan(g, "bf16", world, False, "fsdp2", grad_acc).upload() for g in groups]
-    S = sum(p.shard_numel for p in plans)
-    P = sum(p.total_numel for p in plans)
+    probe = [fs.fs_plan(g, "bf16", world, False, "fsdp2", grad_acc) for g in groups]   # host only
+    S = sum(p.shard_numel for p in probe)
+    P = sum(p.total_numel for p in probe)
+    gathered_numels = [p.gathered_numel for p in probe]
+    del probe
     log(f"workload {workload}: {len(groups)} groups, P={P}, shard S={S}, N={world}, A={grad_acc}")
 
     t0 = time.time()
-    params, gathered, outs = [], [], []
-    off = 0
-    for g, p in zip(groups, plans):
-        ps = []
-        for s in g:
-            n = math.prod(s)
-            ps.append(synth.normal_bf16(seed, synth.STREAM_PARAMS, n, 0.02, device="cuda", start=off).view(*s))
-            off += n
-        params.append(ps)
-        gathered.append(torch.empty(p.gathered_numel, dtype=torch.bfloat16, device="cuda"))
-        outs.append([torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in g])
-    log(f"parameters generated in {time.time() - t0:.1f}s")
-    slices = []
-    for j in range(grad_acc):
-        for k in range(world):
-            slices.append(synth.normal_bf16(seed, synth.stream_grad(j, k, world), S, 1e-3, device="cuda"))
-        log(f"gradient slices of micro-step {j} generated ({time.time() - t0:.1f}s)")
-    master = synth.normal_f32(seed, synth.STREAM_MASTER, S, 0.02, device="cuda")
-    exp_avg = torch.zeros(S, dtype=torch.float32, device="cuda")
-    exp_avg_sq = torch.zeros(S, dtype=torch.float32, device="cuda")
-    grad32 = torch.empty(S, dtype=torch.float32, device="cuda")
-    p16 = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    W = dict(fs=fs, S=S, P=P, world=world, grad_acc=grad_acc, groups=len(groups), workload=workload)
+
+    def alloc_state():
+        slices = []
+        for j in range(grad_acc):
+            for k in range(world):
+                slices.append(synth.normal_bf16(seed, synth.stream_grad(j, k, world), S, 1e-3, device="cuda"))
+            log(f"gradient slices of micro-step {j} generated ({time.time() - t0:.1f}s)")
+        W.update(slices=slices,
+                 master=synth.normal_f32(seed, synth.STREAM_MASTER, S, 0.02, device="cuda"),
+                 exp_avg=torch.zeros(S, dtype=torch.float32, device="cuda"),
+                 exp_avg_sq=torch.zeros(S, dtype=torch.float32, device="cuda"),
+                 grad32=torch.empty(S, dtype=torch.float32, device="cuda"),
+                 p16=torch.empty(S, dtype=torch.bfloat16, device="cuda"))
+
+    def alloc_params():
+        params, gathered, outs = [], [], []
+        off = 0
+        for g, gn in zip(groups, gathered_numels):
+            ps = []
+            for s in g:
+                n = math.prod(s)
+                ps.append(synth.normal_bf16(seed, synth.STREAM_PARAMS, n, 0.02, device="cuda", start=off).view(*s))
+                off += n
+            params.append(ps)
+            gathered.append(torch.empty(gn, dtype=torch.bfloat16, device="cuda"))
+            outs.append([torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in g])
+        W.update(params=params, gathered=gathered, outs=outs)
+        log(f"parameters generated ({time.time() - t0:.1f}s)")
+
+    def alloc_plans():
+        W["plans"] = [fs.fs_plan(g, "bf16", world, False, "fsdp2", grad_acc).upload() for g in groups]
+
+    steps = {"state_first": (alloc_state, alloc_params, alloc_plans),
+             "plans_first": (alloc_plans, alloc_params, alloc_state),
+             "params_first": (alloc_params, alloc_state, alloc_plans)}[order]
+    for fn in steps:
+        fn()
     torch.cuda.synchronize()
     log(f"inputs generated on the GPU in {time.time() - t0:.1f}s; "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
-    return dict(fs=fs, plans=plans, params=params, gathered=gathered, outs=outs, slices=slices,
-                master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, grad32=grad32, p16=p16,
-                S=S, P=P, world=world, grad_acc=grad_acc, groups=len(groups), workload=workload)
+    return W
 
 
 def algorithmic_bytes(W) -> dict:

@@ -762,6 +762,8 @@ __global__ __launch_bounds__(kThreads) void adamw_wave_kernel(float *__restrict_
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t base = (int64_t)blockIdx.x * kAdamChunk + (int64_t)wave * 256 * kAdamGroups + 4 * lane;
     float G[4 * kAdamGroups], T[4 * kAdamGroups], M[4 * kAdamGroups], V[4 * kAdamGroups];
+    // loads and stores are issued array by array (all of g, then theta, m,
+    // v), so each wave's 4 KB of one array go out back to back
 #pragma unroll
     for (int q = 0; q < kAdamGroups; ++q) {
         const int64_t e = base + q * 256;
@@ -775,22 +777,27 @@ __global__ __launch_bounds__(kThreads) void adamw_wave_kernel(float *__restrict_
         } else {
             f4(ld16(reinterpret_cast<const char *>(reinterpret_cast<const float *>(grad) + e)), G + 4 * q);
         }
-        f4(ld16(reinterpret_cast<const char *>(th + e)), T + 4 * q);
-        f4(ld16(reinterpret_cast<const char *>(m + e)), M + 4 * q);
-        f4(ld16(reinterpret_cast<const char *>(v + e)), V + 4 * q);
     }
+#pragma unroll
+    for (int q = 0; q < kAdamGroups; ++q) f4(ld16(reinterpret_cast<const char *>(th + base + q * 256)), T + 4 * q);
+#pragma unroll
+    for (int q = 0; q < kAdamGroups; ++q) f4(ld16(reinterpret_cast<const char *>(m + base + q * 256)), M + 4 * q);
+#pragma unroll
+    for (int q = 0; q < kAdamGroups; ++q) f4(ld16(reinterpret_cast<const char *>(v + base + q * 256)), V + 4 * q);
 #pragma unroll
     for (int k = 0; k < 4 * kAdamGroups; ++k) adam_elem(c, G[k], T[k], M[k], V[k]);
 #pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) {
-        const int64_t e = base + q * 256;
-        st16(reinterpret_cast<char *>(th + e), u4(T + 4 * q));
-        st16(reinterpret_cast<char *>(m + e), u4(M + 4 * q));
-        st16(reinterpret_cast<char *>(v + e), u4(V + 4 * q));
-        if (HAS_P16) {
+    for (int q = 0; q < kAdamGroups; ++q) st16(reinterpret_cast<char *>(th + base + q * 256), u4(T + 4 * q));
+#pragma unroll
+    for (int q = 0; q < kAdamGroups; ++q) st16(reinterpret_cast<char *>(m + base + q * 256), u4(M + 4 * q));
+#pragma unroll
+    for (int q = 0; q < kAdamGroups; ++q) st16(reinterpret_cast<char *>(v + base + q * 256), u4(V + 4 * q));
+    if (HAS_P16) {
+#pragma unroll
+        for (int q = 0; q < kAdamGroups; ++q) {
             const u32x2 w = {(uint32_t)bf16_rne(T[4 * q]) | ((uint32_t)bf16_rne(T[4 * q + 1]) << 16),
                              (uint32_t)bf16_rne(T[4 * q + 2]) | ((uint32_t)bf16_rne(T[4 * q + 3]) << 16)};
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p16 + e));
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p16 + base + q * 256));
         }
     }
 }
