@@ -37,7 +37,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard_step.json")
 WORKLOADS = {
     # name: (n_blocks, d, f, kv, vocab, world, grad_acc)
     "7b": (32, 4096, 11008, None, 32000, 8, 4),
-    "70b": (80, 8192, 28672, 1024, 32000, 8, 2),
 }
 # llama_model_groups(n_blocks, d, f, vocab, kv) arguments per workload
 _WL_SHAPES = {k: (v[0], v[1], v[2], v[4], v[3]) for k, v in WORKLOADS.items()}
@@ -212,6 +211,62 @@ def extra_measurements(W, reps) -> dict:
     del dst, rs, half
     torch.cuda.empty_cache()
     return out
+
+
+def tiny_step_latency(fs, reps=200) -> dict:
+    """The launch-bound tiny case (2-layer MLP, FSDP1 with use_orig_params,
+    N = 4): pack of all ranks, unpack, reduce and AdamW, timed per step
+    eagerly and as one replayed HIP graph of the same four launches."""
+    import torch
+
+    import synth
+    shapes = synth.mlp_tiny_shapes()
+    N = 4
+    plan = fs.fs_plan(shapes, "bf16", N, True, "fsdp1", 1).upload()
+    S = plan.shard_numel
+    params, off = [], 0
+    for s in shapes:
+        n = math.prod(s)
+        params.append(synth.normal_bf16(1, synth.STREAM_PARAMS, n, 0.02, device="cuda", start=off).view(*s))
+        off += n
+    outs = [torch.empty_like(p) for p in params]
+    gathered = torch.empty(plan.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    slices = [synth.normal_bf16(1, synth.stream_grad(0, k, N), S, 1e-3, device="cuda") for k in range(N)]
+    master = synth.normal_f32(1, synth.STREAM_MASTER, S, 0.02, device="cuda")
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    g32, p16 = torch.empty_like(master), torch.empty(S, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        fs.fs_pack(plan, params, gathered)
+        fs.fs_unpack(plan, gathered, outs)
+        fs.fs_reduce_shard(slices, g32, N, 1)
+        fs.fs_adamw_step(master, m, v, g32, p16, lr=1e-3, step=1)
+
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        step()
+    e.record()
+    e.synchronize()
+    eager_us = s.elapsed_time(e) * 1e3 / reps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    e.synchronize()
+    graph_us = s.elapsed_time(e) * 1e3 / reps
+    del g
+    return {"eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+            "launches_per_step": 4, "shard_numel": S}
 
 
 def copy_ceiling(fs, nbytes=1 << 32, reps=5):
@@ -468,6 +523,7 @@ def main():
     fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
     extra = extra_measurements(W, args.steps)
     ceiling = copy_ceiling(fs)
+    tiny = tiny_step_latency(fs)
 
     kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
                                   "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
@@ -492,15 +548,14 @@ def main():
                          "adamw": "f64 math on fp32 state, bf16 copy"},
         "data": "synthetic",
         "config": {"workload": ("7B Llama-style model, rank 0's FSDP2 1/8 shard: pack + unpack of all 33 groups, "
-                                "reduce of 4x8 bf16 gradient slices, AdamW" if args.workload == "7b" else
-                                "70B Llama-style model, rank 0's FSDP2 1/8 shard: pack + unpack of all 81 groups, "
-                                "reduce of 2x8 bf16 gradient slices, AdamW"),
+                                "reduce of 4x8 bf16 gradient slices, AdamW"),
                    "params": W["P"], "shard_numel": W["S"], "world": W["world"], "grad_acc": W["grad_acc"],
                    "groups": W["groups"], "step_bytes": step_bytes},
         "kernels": kern,
         "reduce_adamw_GBps": round(ra_gbps, 1),
         "reduce_adamw_frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4),
         "copy_ceiling_GBps": round(ceiling, 1),
+        "tiny_mlp_step": tiny,
         "roofline": {"bound": "hbm", "kernel": "reduce_chunk_kernel", "achieved": round(red_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(red_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": alg["reduce"]},
