@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -31,7 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, 8 TB/s
-KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_state_amd", "csrc", "fs_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "fsdp_sharded_state_amd", "csrc", f)
+               for f in ("fs_kernels.hip", "fs_internal.h", "fs_plan_impl.h", "fs_plan.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard_step.json")
 
 WORKLOADS = {
@@ -47,7 +49,16 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the library's sources with comments and layout removed: it
+    changes when the code of a kernel, its launch shape or the planner's
+    tiling changes, not when a comment does."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        src = open(path).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def setup(workload: str, seed: int = 4, order: str = "params_first"):

@@ -705,10 +705,9 @@ __global__ __launch_bounds__(kThreads) void reduce_rs_general_kernel(SliceArgs s
 // ----------------------------------------------------------------- AdamW --
 //
 // One fused read-modify-write pass: read g, theta, m, v; write theta, m, v
-// and the bf16 parameter.  Lane i owns 8 consecutive elements (dwordx4
-// accesses).  The update is evaluated in double from the fp32 inputs and
-// rounded to fp32 once per stored value; the bias corrections 1 - beta^t are
-// per-step scalars computed on the host.
+// and the bf16 parameter.  The update is evaluated in double from the fp32
+// inputs and rounded to fp32 once per stored value; the bias corrections
+// 1 - beta^t are per-step scalars computed on the host.
 
 struct AdamConsts {
     double b1, b2, omb1, omb2, bc1, bc2, lr, eps, decay;
