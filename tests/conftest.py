@@ -19,12 +19,17 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session", autouse=True)
 def _libraries_built():
-    """Build the oracle (gcc) and, on a machine with hipcc, the HIP library if
-    they are missing; an existing build is used as it is."""
+    """Build the oracle (gcc), on a machine with hipcc the HIP library, and
+    the C client of the library, if they are missing; an existing build is
+    used as it is."""
     import oracle
     oracle.build(force=not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")))
     lib = os.path.join(ROOT, "fsdp_sharded_state_amd", "libfsstate.so")
     if not os.path.exists(lib) and os.path.exists("/opt/rocm/bin/hipcc"):
         from fsdp_sharded_state_amd import build as _b
         _b.build()
+    if os.path.exists(lib):
+        sys.path.insert(0, os.path.join(ROOT, "tests", "c"))
+        import build_client
+        build_client.build(force=False)
     yield
