@@ -23,7 +23,10 @@
  *     (2 bytes for bf16, 4 for fp32); 16-byte alignment is not required but
  *     is the fast path.
  *   - Work is issued asynchronously on `stream` (NULL = the null stream) as
- *     one kernel per call (fs_reduce_shard: one kernel per 32 terms).
+ *     kernel launches only -- no copies, allocations or waits -- so the calls
+ *     can be captured into a HIP graph.  A call launches its main kernel and
+ *     at most one more for a ragged tail or a misaligned remainder; the
+ *     reduces do so once per pass of up to 32 terms.
  *   - Inputs and outputs must not overlap, except the in-place AdamW state.
  *   - Errors are reported by return code (fs_status); the call then has
  *     launched nothing.  fs_last_error() describes the last failure of the
