@@ -15,6 +15,7 @@ functions raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import List, Optional, Sequence
 
@@ -159,6 +160,7 @@ class Plan:
         self.workspace: Optional[torch.Tensor] = None
         self._ptr_cache = {}
         self.numels = [self.param(i).numel for i in range(info.n_params)]
+        self.shapes: Optional[List[tuple]] = None   # set by fs_plan()
 
     def close(self):
         """Release the plan's host memory (also done on garbage collection)."""
@@ -187,6 +189,59 @@ class Plan:
         arr = (Segment * max(1, n.value))()
         _check(lib().fs_plan_segments(self._h, arr, n.value, ctypes.byref(n)))
         return [(s.dst_off, s.src_off, s.len, s.param, s.rank) for s in arr[:n.value]]
+
+    def local_pieces(self, rank: int) -> List[Optional[tuple]]:
+        """Where each parameter's elements held by `rank` sit: per parameter,
+        (offset in the rank's shard, first element of the flattened
+        parameter, count), or None when the rank holds none of it.  A
+        parameter's elements on one rank are always one contiguous run, in
+        both layouts."""
+        if not 0 <= rank < self.info.world:
+            raise ValueError(f"rank {rank} out of range [0, {self.info.world})")
+        c = self.info.shard_numel
+        out: List[Optional[tuple]] = [None] * self.info.n_params
+        for dst, src, ln, p, r in self.segments():
+            if r == rank:
+                if out[p] is not None:
+                    raise RuntimeError(f"parameter {p} has two runs on rank {rank}")
+                out[p] = (dst - r * c, src, ln)
+        return out
+
+    def local_views(self, shard: torch.Tensor, rank: int) -> List[torch.Tensor]:
+        """The sharded state dict of `rank`, zero-copy: for each parameter,
+        the view of `shard` (that rank's shard buffer, shard_numel elements:
+        parameters, gradients or optimizer state laid out by this plan) that
+        holds the parameter's local elements.  FSDP2: shaped (rows, *shape[1:])
+        -- the rank's dim-0 chunk, empty when it has no rows; FSDP1: 1-D, the
+        flattened parameter's elements that fall in the rank's flat shard."""
+        if shard.dim() != 1 or shard.numel() != self.info.shard_numel:
+            raise ValueError(f"shard must be 1-D with {self.info.shard_numel} elements")
+        if shard.element_size() != self.info.elem_bytes:
+            raise ValueError(f"shard element size {shard.element_size()} != plan's {self.info.elem_bytes}")
+        fsdp2 = self.info.mode == FS_FSDP2_PER_PARAM
+        views = []
+        for i, piece in enumerate(self.local_pieces(rank)):
+            off, _, ln = piece if piece is not None else (0, 0, 0)
+            v = shard[off:off + ln]
+            tail = tuple(self.shapes[i][1:]) if fsdp2 and self.shapes and self.shapes[i] else ()
+            row = math.prod(tail)
+            views.append(v.view((ln // row,) + tail) if fsdp2 and row else v)
+        return views
+
+    def load_local(self, shard: torch.Tensor, rank: int, tensors: Sequence[torch.Tensor]):
+        """Import a sharded state dict: zero `shard` (pads stay zero) and copy
+        each parameter's local tensor (shaped as local_views returns it)
+        into its place."""
+        views = self.local_views(shard, rank)
+        if len(tensors) != len(views):
+            raise ValueError(f"expected {len(views)} local tensors, got {len(tensors)}")
+        for i, (v, t) in enumerate(zip(views, tensors)):
+            if t.numel() != v.numel():
+                raise ValueError(f"local tensor {i}: {t.numel()} elements, rank {rank} holds {v.numel()}")
+        shard.zero_()
+        for v, t in zip(views, tensors):
+            if v.numel():
+                v.copy_(t.reshape(v.shape))
 
     def upload(self, device="cuda", stream=None) -> "Plan":
         ws = torch.empty(max(16, self.info.workspace_bytes), dtype=torch.uint8, device=device)
@@ -227,7 +282,9 @@ def fs_plan(shapes: Sequence[Sequence[int]], dtype="bf16", world: int = 1, use_o
     h = ctypes.c_void_p()
     _check(lib().fs_plan(n, ndim, dims, _dtype_code(dtype), int(world), int(bool(use_orig_params)),
                          _mode_code(mode), int(grad_acc), ctypes.byref(h)))
-    return Plan(h.value)
+    plan = Plan(h.value)
+    plan.shapes = [tuple(int(d) for d in s) for s in shapes]
+    return plan
 
 
 class Reshard:

@@ -1,0 +1,150 @@
+"""Sharded state dict: each rank's shard buffer already holds every
+parameter's local elements ("FSDP1 vs FSDP2", memory and engineering
+section: FSDP2's shards are the sharded state dict, no communication
+needed), so Plan.local_views exports them as zero-copy views and
+Plan.load_local imports them.
+
+Expected local pieces come from the pages' definitions, not from the plan:
+FSDP2 -- torch.chunk(param, N, dim=0)[r] (section 03); FSDP1 -- the
+flattened parameter's elements whose flat index falls in [r*c, (r+1)*c),
+with flat indices from the oracle's layout.  Shards are cut from the
+oracle's pack.  The CPU tests run on host tensors; the GPU test takes the
+shard from fs_pack(rank=r).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+fs = pytest.importorskip("fsdp_sharded_state_amd")
+
+CASES = [
+    ("worked_example_f1T", "fsdp1", [(3,), (5,)], "bf16", 4, True),
+    ("worked_example_f1F", "fsdp1", [(3,), (5,)], "bf16", 4, False),
+    ("worked_example_f2", "fsdp2", [(3,), (5,)], "bf16", 4, False),
+    ("tiny_mixed_f2_fp32", "fsdp2", [(6, 3), (), (0, 2), (9,), (1, 1), (13, 5)], "fp32", 4, False),
+    ("tiny_mixed_f1F_fp32", "fsdp1", [(1,), (7,), (0,), (3, 3), (2,), (17,)], "fp32", 3, False),
+    ("tiny_mixed_f1T", "fsdp1", [(1,), (7,), (0,), (3, 3), (2,), (17,)], "bf16", 5, True),
+    ("mlp_tiny", "fsdp1", synth.mlp_tiny_shapes(), "bf16", 4, True),
+    ("llama_block_d256_fsdp2", "fsdp2", synth.llama_block_shapes(256, 688), "bf16", 8, False),
+    ("llama_block_d256_fsdp2_N3", "fsdp2", synth.llama_block_shapes(256, 688), "fp32", 3, False),
+]
+
+
+def _tdt(dt):
+    return torch.int16 if dt == "bf16" else torch.int32
+
+
+def _layout(mode, shapes, dt, N, uo):
+    eb = 2 if dt == "bf16" else 4
+    return oracle.fsdp1_layout(shapes, eb, N, uo) if mode == "fsdp1" else oracle.fsdp2_layout(shapes, eb, N)
+
+
+def _params(shapes, dt, seed=23):
+    out, off = [], 0
+    for s in shapes:
+        n = int(np.prod(s)) if len(s) else 1
+        g = synth.bits16 if dt == "bf16" else synth.bits32
+        out.append(g(seed, synth.STREAM_PARAMS, n, start=off).view(_tdt(dt)).reshape(s))
+        off += n
+    return out
+
+
+def _expected_local(mode, L, params, shapes, N, r):
+    """Each parameter's local elements on rank r, by the pages' definitions."""
+    exp = []
+    offs = np.concatenate([[0], np.cumsum(L.numel)]).astype(np.int64)
+    imap = L.index_map()
+    for i, (p, s) in enumerate(zip(params, shapes)):
+        if mode == "fsdp2":
+            q = p.reshape(1) if len(s) == 0 else p
+            ch = torch.chunk(q, N, dim=0) if q.shape[0] > 0 else ()
+            exp.append(ch[r] if r < len(ch) else q[0:0])
+        else:
+            flat_idx = imap[offs[i]:offs[i + 1]]
+            sel = np.nonzero(flat_idx // L.shard == r)[0]
+            if sel.size:
+                assert np.all(np.diff(sel) == 1), "a parameter's piece on one rank must be contiguous"
+            exp.append(p.reshape(-1)[torch.from_numpy(sel)])
+    return exp
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_local_views_are_the_sharded_state_dict(case):
+    name, mode, shapes, dt, N, uo = case
+    plan = fs.fs_plan(shapes, dt, N, uo, mode)
+    L = _layout(mode, shapes, dt, N, uo)
+    params = _params(shapes, dt)
+    host = [p.reshape(-1).numpy().view(np.uint16 if dt == "bf16" else np.uint32) for p in params]
+    gathered = torch.from_numpy(oracle.pack(L, host).view(np.int16 if dt == "bf16" else np.int32))
+    c = plan.shard_numel
+    held = np.zeros(len(shapes), np.int64)
+    for r in range(N):
+        shard = gathered[r * c:(r + 1) * c].clone()
+        views = plan.local_views(shard, r)
+        exp = _expected_local(mode, L, params, shapes, N, r)
+        for i, (v, e) in enumerate(zip(views, exp)):
+            assert tuple(v.shape) == tuple(e.shape), (name, r, i, v.shape, e.shape)
+            assert torch.equal(v, e), (name, r, i)
+            assert v.numel() == 0 or v.data_ptr() >= shard.data_ptr()       # a view, not a copy
+            held[i] += v.numel()
+        # import into a scribbled buffer: pads come back zero, pieces in place
+        back = torch.full_like(shard, 0x5A5A if dt == "bf16" else 0x5A5A5A5A)
+        plan.load_local(back, r, [e.clone() for e in exp])
+        assert torch.equal(back, shard), (name, r)
+    np.testing.assert_array_equal(held, L.numel)     # every element on exactly one rank
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[1] == "fsdp2"], ids=lambda c: c[0])
+def test_unshard_from_sharded_state_dict(case):
+    """Concatenating the ranks' local views on dim 0 gives back each parameter."""
+    name, mode, shapes, dt, N, uo = case
+    plan = fs.fs_plan(shapes, dt, N, uo, mode)
+    L = _layout(mode, shapes, dt, N, uo)
+    params = _params(shapes, dt, seed=29)
+    host = [p.reshape(-1).numpy().view(np.uint16 if dt == "bf16" else np.uint32) for p in params]
+    gathered = torch.from_numpy(oracle.pack(L, host).view(np.int16 if dt == "bf16" else np.int32))
+    c = plan.shard_numel
+    per_rank = [plan.local_views(gathered[r * c:(r + 1) * c], r) for r in range(N)]
+    for i, (p, s) in enumerate(zip(params, shapes)):
+        full = torch.cat([per_rank[r][i] for r in range(N)], dim=0)
+        assert torch.equal(full.reshape(s), p), (name, i)
+
+
+def test_local_views_argument_checks():
+    plan = fs.fs_plan([(3,), (5,)], "bf16", 4, True, "fsdp1")
+    with pytest.raises(ValueError):
+        plan.local_views(torch.zeros(plan.shard_numel + 1, dtype=torch.int16), 0)
+    with pytest.raises(ValueError):
+        plan.local_views(torch.zeros(plan.shard_numel, dtype=torch.int32), 0)
+    with pytest.raises(ValueError):
+        plan.local_views(torch.zeros(plan.shard_numel, dtype=torch.int16), 4)
+    with pytest.raises(ValueError):
+        plan.load_local(torch.zeros(plan.shard_numel, dtype=torch.int16), 0, [torch.zeros(2, dtype=torch.int16)])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("mlp_tiny", "llama_block_d256_fsdp2",
+                                                                   "tiny_mixed_f2_fp32")],
+                         ids=lambda c: c[0])
+def test_gpu_pack_rank_then_local_views(case):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gpu_util import say
+    name, mode, shapes, dt, N, uo = case
+    say("state dict: pack rank r then local views", name)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    plan = fs.fs_plan(shapes, dt, N, uo, mode).upload()
+    L = _layout(mode, shapes, dt, N, uo)
+    params = _params(shapes, dt, seed=31)
+    dev = [p.reshape(-1).view(tdt).cuda() for p in params]
+    for r in range(N):
+        shard = torch.empty(plan.shard_numel, dtype=tdt, device="cuda")
+        fs.fs_pack(plan, dev, shard, rank=r)
+        torch.cuda.synchronize()
+        views = plan.local_views(shard, r)
+        exp = _expected_local(mode, L, params, shapes, N, r)
+        for i, (v, e) in enumerate(zip(views, exp)):
+            assert torch.equal(v.cpu().view(_tdt(dt)), e), (name, r, i)
