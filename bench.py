@@ -511,7 +511,8 @@ def main():
 
     phases = ["pack", "unpack", "reduce", "adamw"]
     ms = {ph: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, ph in enumerate(phases)}
-    kern = {ph: {"ms": round(ms[ph], 4), "GB": round(alg[ph] / 1e9, 3),
+    med = {ph: sorted(e[i].elapsed_time(e[i + 1]) for e in evs)[args.steps // 2] for i, ph in enumerate(phases)}
+    kern = {ph: {"ms": round(ms[ph], 4), "ms_median": round(med[ph], 4), "GB": round(alg[ph] / 1e9, 3),
                  "GBps": round(alg[ph] / (ms[ph] * 1e-3) / 1e9, 1),
                  "frac_hbm_peak": round(alg[ph] / (ms[ph] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
             for ph in phases}
