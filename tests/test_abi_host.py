@@ -301,3 +301,45 @@ def test_reshard_plan_validation():
     same = fs.fs_reshard_plan(fs.fs_plan([(40,), (24,)], "bf16", 8, False, "fsdp1"),
                               fs.fs_plan([(40,), (24,)], "bf16", 8, False, "fsdp1"))
     assert same.n_segments == 1
+
+
+def test_planner_is_thread_safe_and_errors_are_per_thread():
+    """Plans made concurrently from 8 threads (ctypes releases the GIL during
+    the C call) match the oracle, and each thread's fs_last_error names its
+    own failure."""
+    import threading
+    L = fs.lib()
+    errors, failures = {}, []
+    barrier = threading.Barrier(8)
+
+    def work(tid):
+        try:
+            barrier.wait()
+            for rep in range(20):
+                shapes = [((tid * 7 + rep * 3 + k) % 13 + 1, (k % 3) + 1) for k in range(5)]
+                N = 1 + (tid + rep) % 8
+                _compare("fsdp2", shapes, 2, N, False)
+                _compare("fsdp1", [(int(np.prod(s)),) for s in shapes], 4, N, bool(rep & 1))
+            h = ctypes.c_void_p()
+            nd = (ctypes.c_int32 * 1)(1)
+            dm = (ctypes.c_int64 * 1)(5)
+            if tid % 2:
+                rc = L.fs_plan(1, nd, dm, 0, 0, 0, 1, 1, ctypes.byref(h))       # world < 1
+            else:
+                rc = L.fs_plan(1, nd, dm, 0, 4, 1, 2, 1, ctypes.byref(h))       # use_orig_params in FSDP2
+            barrier.wait()      # every thread has failed before any reads its message
+            errors[tid] = (rc, L.fs_last_error().decode())
+        except Exception as e:  # noqa: BLE001 -- reported below
+            failures.append((tid, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not failures, failures
+    for tid, (rc, msg) in errors.items():
+        if tid % 2:
+            assert rc == fs.FS_E_INVAL and "world" in msg, (tid, msg)
+        else:
+            assert rc == fs.FS_E_UNSUPPORTED and "use_orig_params" in msg, (tid, msg)
