@@ -443,6 +443,9 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     md += ["", "then `python bench.py --rocprof-summary <trace dir> <FETCH_SIZE dir> <WRITE_SIZE dir>`.", "",
            f"Counter scale (bytes per counted byte, from the 4 GiB copy kernel): FETCH_SIZE x{f_fetch:.4f}, "
            f"WRITE_SIZE x{f_write:.4f}.", "",
+           "Kernel rates move by up to about 8% between processes running the same code, with the",
+           "physical placement of the buffers; compare the trace with the bench line of the same run",
+           "(at the end), not with another run's.", "",
            "| kernel | calls | avg duration | HBM read / launch | HBM write / launch | algorithmic / launch | HBM / alg | alg GB/s (trace) |",
            "|---|---|---|---|---|---|---|---|"]
     for k, st, fe, wr, a in rows:
