@@ -343,3 +343,22 @@ def test_planner_is_thread_safe_and_errors_are_per_thread():
             assert rc == fs.FS_E_INVAL and "world" in msg, (tid, msg)
         else:
             assert rc == fs.FS_E_UNSUPPORTED and "use_orig_params" in msg, (tid, msg)
+
+
+# ------------------------------------------------------ randomized planner --
+
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+_dims = st.integers(min_value=0, max_value=97)
+_shape = st.one_of(st.tuples(), st.tuples(_dims), st.tuples(_dims, st.integers(1, 9)),
+                   st.tuples(_dims, st.integers(1, 5), st.integers(1, 3)))
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(shapes=st.lists(_shape, min_size=0, max_size=12), N=st.integers(1, 64),
+       eb=st.sampled_from([2, 4]), uo=st.booleans(), mode=st.sampled_from(["fsdp1", "fsdp2"]))
+def test_planner_matches_oracle_randomized(shapes, N, eb, uo, mode):
+    """Random parameter lists (scalars, empty and 1- to 3-D shapes) and N up
+    to 64: the library's plan places every element where the oracle does."""
+    _compare(mode, shapes, eb, N, uo and mode == "fsdp1")
