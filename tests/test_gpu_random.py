@@ -2,7 +2,11 @@
 tensors, 1- to 3-D shapes of awkward sizes), random N, dtype, mode and
 use_orig_params, random 0..7-element misalignment of every buffer.  Pack
 (all ranks and one rank), unpack and re-shard to another random plan must
-equal the oracle bit for bit; all outputs sit in canary guard bands.
+equal the oracle bit for bit.  The reduce family (fp32 and bf16 reduce
+dtype, fused reduce + AdamW) runs on random sizes, N, grad_acc and
+per-slice misalignment: reduces bit-exact, fused bit-identical to the two
+kernels, AdamW within its tolerance of the oracle.  Every buffer sits in a
+canary guard band.
 """
 import numpy as np
 import pytest
@@ -111,3 +115,60 @@ def test_random_layout_pack_unpack_reshard(seed):
     D.check()
     src.check()
     np.testing.assert_array_equal(bits(D.t), oracle.reshard(L, L2, junk))
+
+
+def _random_reduce_case(seed):
+    rng = np.random.default_rng(2000 + seed)
+    n = int(rng.integers(1, 200000))
+    N = int(rng.integers(1, 17))
+    A = int(rng.integers(1, 6))
+    if rng.random() < 0.5:
+        shifts = [0] * (N * A)
+        osh = 0
+    else:
+        shifts = [int(x) for x in rng.integers(0, 8, size=N * A)]
+        osh = int(rng.integers(0, 4))
+    return n, N, A, shifts, osh
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_reduce_family(seed):
+    """fs_reduce_shard, the bf16 reduce dtype and the fused reduce + AdamW on
+    random sizes, world sizes, micro-step counts (up to 80 terms: several
+    passes) and per-slice misalignment."""
+    n, N, A, shifts, osh = _random_reduce_case(seed)
+    say("random reduce family", seed, n, N, A, shifts[:4], osh)
+    sl = [Guarded(n, torch.bfloat16, shift=sh,
+                  fill=synth.normal_bf16(seed, synth.stream_grad(t // N, t % N, N), n, 1e-3, device="cuda"))
+          for t, sh in enumerate(shifts)]
+    host = [bits(s.t) for s in sl]
+    out = Guarded(n, torch.float32, shift=osh)
+    fs.fs_reduce_shard([s.t for s in sl], out.t, N, A)
+    rs = Guarded(n, torch.float32, shift=osh)
+    fs.fs_reduce_shard_ex([s.t for s in sl], rs.t, N, A, reduce_dtype="bf16")
+    th = synth.normal_f32(seed, synth.STREAM_MASTER, n, 0.02, device="cuda")
+    m = synth.normal_f32(seed, synth.STREAM_EXP_AVG, n, 1e-3, device="cuda")
+    v = synth.normal_f32(seed, synth.STREAM_EXP_AVG_SQ, n, 1e-3, device="cuda") ** 2
+    two = [Guarded(n, torch.float32, shift=osh, fill=x) for x in (th, m, v)]
+    fused = [Guarded(n, torch.float32, shift=osh, fill=x) for x in (th, m, v)]
+    p_two, p_fused = Guarded(n, torch.bfloat16, shift=osh), Guarded(n, torch.bfloat16, shift=osh)
+    g_fused = Guarded(n, torch.float32, shift=osh)
+    fs.fs_adamw_step(*[x.t for x in two], out.t, p_two.t, step=seed + 1)
+    fs.fs_reduce_adamw_step([s.t for s in sl], *[x.t for x in fused], p_fused.t, g_fused.t, world=N,
+                            grad_acc=A, step=seed + 1)
+    torch.cuda.synchronize()
+    for g in [out, rs, p_two, p_fused, g_fused] + two + fused + sl:
+        g.check()
+    ref = oracle.reduce_shard(host, N, A)
+    np.testing.assert_array_equal(bits(out.t), ref.view(np.uint32))
+    np.testing.assert_array_equal(bits(g_fused.t), ref.view(np.uint32))
+    np.testing.assert_array_equal(bits(rs.t), oracle.reduce_shard_bf16rs(host, N, A).view(np.uint32))
+    for a, b in zip(two + [p_two], fused + [p_fused]):
+        np.testing.assert_array_equal(bits(a.t), bits(b.t))
+    rt, rm, rv, rp = oracle.adamw_step(th.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy(), ref,
+                                       oracle.AdamWHparams(step=seed + 1))
+    gt, gm, gv = (x.t.cpu().numpy() for x in two)
+    assert np.all(np.abs(gt - rt) <= 1e-6 * np.maximum(np.abs(rt), np.abs(th.cpu().numpy())))
+    assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm))
+    assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv))
+    assert np.all(np.abs(bits(p_two.t).astype(np.int32) - rp.astype(np.int32)) <= 1)
