@@ -1024,6 +1024,21 @@ int check_device(const char *what, int dev_id) {
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
+// A plan's workspace holds the tables its kernels read, so it must be
+// device memory of the current device; *dev receives that device.
+int check_workspace(const char *what, const void *ws, int *dev) {
+    if (hipGetDevice(dev) != hipSuccess) return fsi::fail(FS_E_HIP, "%s: no current device", what);
+    hipPointerAttribute_t a;
+    memset(&a, 0, sizeof a);
+    if (hipPointerGetAttributes(&a, ws) != hipSuccess) {
+        (void)hipGetLastError();   // the query's error is not a launch error: do not leave it behind
+        return fsi::fail(FS_E_INVAL, "%s: workspace is not device memory", what);
+    }
+    if (a.type != hipMemoryTypeDevice || a.device != *dev)
+        return fsi::fail(FS_E_INVAL, "%s: workspace must be device memory of the current device (%d)", what, *dev);
+    return FS_OK;
+}
+
 int check_launch(const char *what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fsi::fail(FS_E_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
@@ -1045,6 +1060,8 @@ extern "C" int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hip
     if ((int64_t)bytes < w.total_bytes)
         return fsi::fail(FS_E_INVAL, "fs_plan_upload: workspace too small (%zu < %lld bytes)", bytes,
                          (long long)w.total_bytes);
+    int dev = -1;
+    if (int rc = check_workspace("fs_plan_upload", workspace, &dev)) return rc;
     char *ws = static_cast<char *>(workspace);
     struct Part { int64_t off; const void *src; int64_t bytes; };
     const Part parts[] = {
@@ -1062,8 +1079,6 @@ extern "C" int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hip
     }
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_plan_upload: sync failed: %s", hipGetErrorString(e));
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return fsi::fail(FS_E_HIP, "fs_plan_upload: no current device");
     plan->dev_ws = workspace;
     plan->dev_id = dev;
     return FS_OK;
@@ -1115,6 +1130,8 @@ extern "C" int fs_reshard_upload(fs_reshard_t r, void *workspace, size_t bytes, 
     if ((int64_t)bytes < r->ws_bytes)
         return fsi::fail(FS_E_INVAL, "fs_reshard_upload: workspace too small (%zu < %lld bytes)", bytes,
                          (long long)r->ws_bytes);
+    int dev = -1;
+    if (int rc = check_workspace("fs_reshard_upload", workspace, &dev)) return rc;
     char *ws = static_cast<char *>(workspace);
     if (!r->segs.empty()) {
         hipError_t e = hipMemcpyAsync(ws + r->ws_segs, r->segs.data(), r->segs.size() * sizeof(Segment),
@@ -1128,8 +1145,6 @@ extern "C" int fs_reshard_upload(fs_reshard_t r, void *workspace, size_t bytes, 
     }
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return fsi::fail(FS_E_HIP, "fs_reshard_upload: sync failed: %s", hipGetErrorString(e));
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return fsi::fail(FS_E_HIP, "fs_reshard_upload: no current device");
     r->dev_ws = workspace;
     r->dev_id = dev;
     return FS_OK;

@@ -181,10 +181,11 @@ int fs_plan_segments(fs_plan_t plan, fs_segment_t *out, int64_t cap, int64_t *n)
 
 /*
  * fs_plan_upload -- copy the plan's device tables (segments and tile index)
- * into `workspace` (device, at least info.workspace_bytes bytes, 16-byte
- * aligned) and bind that workspace to the plan for later fs_pack/fs_unpack
- * calls, which must then run with the same current device (FS_E_INVAL
- * otherwise).  Blocks until the copy has finished.  The workspace must stay
+ * into `workspace` (device memory of the current device, at least
+ * info.workspace_bytes bytes, 16-byte aligned; FS_E_INVAL for host or
+ * another device's memory) and bind that workspace to the plan for later
+ * fs_pack/fs_unpack calls, which must then run with the same current device
+ * (FS_E_INVAL otherwise).  Blocks until the copy has finished.  The workspace must stay
  * allocated and unmodified while the plan is used; calls that use one plan
  * on different streams at once are fine (the tables are read only).
  */

@@ -496,3 +496,22 @@ def test_reshard_bitexact(case, shift):
     dst.check()
     src.check()
     np.testing.assert_array_equal(bits(dst.t), ref)
+
+
+def test_upload_rejects_host_workspace():
+    """A plan's tables must live in device memory of the current device:
+    pinned or pageable host memory is refused before anything is copied."""
+    plan = fs.fs_plan(synth.mlp_tiny_shapes(), "bf16", 4, True, "fsdp1")
+    nb = plan.workspace_bytes
+    for host in (torch.empty(nb, dtype=torch.uint8, pin_memory=True), torch.empty(nb, dtype=torch.uint8)):
+        rc = fs.lib().fs_plan_upload(plan._h, host.data_ptr(), host.numel(), None)
+        assert rc == fs.FS_E_INVAL and b"device memory" in fs.lib().fs_last_error()
+    r = fs.fs_reshard_plan(plan, fs.fs_plan(synth.mlp_tiny_shapes(), "bf16", 2, True, "fsdp1"))
+    host = torch.empty(max(16, r.workspace_bytes), dtype=torch.uint8)
+    rc = fs.lib().fs_reshard_upload(r._h, host.data_ptr(), host.numel(), None)
+    assert rc == fs.FS_E_INVAL and b"device memory" in fs.lib().fs_last_error()
+    plan.upload()                        # a device workspace still works afterwards
+    out = torch.empty(plan.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    fs.fs_pack(plan, [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in synth.mlp_tiny_shapes()], out)
+    torch.cuda.synchronize()
+    assert (out.view(torch.int16) == 0).all()
