@@ -482,6 +482,9 @@ def main():
     ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-tiny", action="store_true",
+                    help="skip the tiny launch-bound step (its small launches would mix into a "
+                         "per-kernel profile of the 7B step)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this engine runs all N logical ranks on one GPU; "
@@ -538,7 +541,7 @@ def main():
     fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
     extra = extra_measurements(W, args.steps)
     ceiling = copy_ceiling(fs)
-    tiny = tiny_step_latency(fs)
+    tiny = None if args.no_tiny else tiny_step_latency(fs)
 
     kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
                                   "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
