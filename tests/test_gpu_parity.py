@@ -515,3 +515,48 @@ def test_upload_rejects_host_workspace():
     fs.fs_pack(plan, [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in synth.mlp_tiny_shapes()], out)
     torch.cuda.synchronize()
     assert (out.view(torch.int16) == 0).all()
+
+
+@pytest.mark.parametrize("n,shift,gbf", [(4096 * 2 + 37, 0, False), (4096 * 2 + 37, 0, True), (2999, 1, False)])
+def test_adamw_special_values(n, shift, gbf):
+    """Non-finite, signed-zero, subnormal and extreme inputs (gradient, theta,
+    moments): wherever the oracle's result is NaN the kernel's is NaN, every
+    other stored value is bit-identical to the oracle (both evaluate in fp64
+    and round once), and the bf16 copy is the RNE of the stored theta."""
+    say("adamw specials", n, shift, gbf)
+    rng = np.random.default_rng(n + shift)
+    g_sp = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-40, np.inf, -np.inf, np.nan, 3e38, -3e38, 1e-30, 1.0],
+                    np.float32)
+    th_sp = np.array([0.0, -0.0, 1e-45, 1e-40, 1e30, -1e30, np.nan, np.inf, 3.4e38, 1.0], np.float32)
+    v_sp = np.array([0.0, 1e-45, 1e-38, 1e30, np.inf, 1.0], np.float32)
+    g = rng.normal(0, 1e-3, n).astype(np.float32)
+    th = rng.normal(0, 0.02, n).astype(np.float32)
+    m = rng.normal(0, 1e-3, n).astype(np.float32)
+    v = (rng.normal(0, 1e-3, n) ** 2).astype(np.float32)
+    idx = rng.permutation(n)
+    g[idx[:600]] = g_sp[np.arange(600) % g_sp.size]
+    th[idx[300:900]] = th_sp[np.arange(600) % th_sp.size]
+    v[idx[500:1100]] = v_sp[np.arange(600) % v_sp.size]
+    m[idx[700:1000]] = -m[idx[700:1000]] * 1e30
+    gt_in = torch.from_numpy(g)
+    if gbf:
+        gt_in = gt_in.to(torch.bfloat16)
+    G = [Guarded(n, torch.float32, shift=shift, fill=torch.from_numpy(x).cuda()) for x in (th, m, v)]
+    Gg = Guarded(n, gt_in.dtype, shift=shift, fill=gt_in.cuda())
+    P = Guarded(n, torch.bfloat16, shift=shift)
+    for step in (1, 9):
+        th0, m0, v0 = (x.t.cpu().numpy().copy() for x in G)
+        g0 = bits(Gg.t) if gbf else Gg.t.cpu().numpy().copy()
+        fs.fs_adamw_step(G[0].t, G[1].t, G[2].t, Gg.t, P.t, step=step)
+        torch.cuda.synchronize()
+        for x in G + [Gg, P]:
+            x.check()
+        rt, rm, rv, rp = oracle.adamw_step(th0, m0, v0, g0, oracle.AdamWHparams(step=step))
+        for got, ref in zip((bits(x.t) for x in G), (rt, rm, rv)):
+            nan_ref = np.isnan(ref)
+            assert np.isnan(got.view(np.float32)[nan_ref]).all()
+            np.testing.assert_array_equal(got[~nan_ref], ref.view(np.uint32)[~nan_ref])
+        gp = bits(P.t)
+        nan_p = np.isnan(rt)
+        np.testing.assert_array_equal(gp[~nan_p], rp[~nan_p])
+        assert ((gp[nan_p] & 0x7F80) == 0x7F80).all() and ((gp[nan_p] & 0x7F) != 0).all()
