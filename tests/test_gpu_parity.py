@@ -560,3 +560,34 @@ def test_adamw_special_values(n, shift, gbf):
         nan_p = np.isnan(rt)
         np.testing.assert_array_equal(gp[~nan_p], rp[~nan_p])
         assert ((gp[nan_p] & 0x7F80) == 0x7F80).all() and ((gp[nan_p] & 0x7F) != 0).all()
+
+
+@pytest.mark.parametrize("n,N,A", [(16384 * 2 + 77, 8, 4), (3001, 3, 2)])
+def test_reduce_adamw_fused_special_values(n, N, A):
+    """The fused path on gradient slices holding NaN, infinities, signed zeros
+    and subnormals, and state with extreme values: same NaN positions as the
+    two-kernel path and bit-identical everywhere else."""
+    say("fused specials", n, N, A)
+    sl = _slices(n, N * A, seed=7, specials=True)
+    rng = np.random.default_rng(n)
+    th = rng.normal(0, 0.02, n).astype(np.float32)
+    th[rng.integers(0, n, 64)] = np.array([np.inf, -0.0, 1e-45, 3e38], np.float32)[np.arange(64) % 4]
+    m = rng.normal(0, 1e-3, n).astype(np.float32)
+    v = (rng.normal(0, 1e-3, n) ** 2).astype(np.float32)
+    v[rng.integers(0, n, 64)] = 0.0
+    two = [Guarded(n, torch.float32, fill=torch.from_numpy(x).cuda()) for x in (th, m, v)]
+    fused = [Guarded(n, torch.float32, fill=torch.from_numpy(x).cuda()) for x in (th, m, v)]
+    g32, p2, pf, gf = (Guarded(n, torch.float32), Guarded(n, torch.bfloat16), Guarded(n, torch.bfloat16),
+                       Guarded(n, torch.float32))
+    fs.fs_reduce_shard([s.t for s in sl], g32.t, N, A)
+    fs.fs_adamw_step(*[x.t for x in two], g32.t, p2.t, step=4)
+    fs.fs_reduce_adamw_step([s.t for s in sl], *[x.t for x in fused], pf.t, gf.t, world=N, grad_acc=A, step=4)
+    torch.cuda.synchronize()
+    for x in two + fused + [g32, p2, pf, gf] + sl:
+        x.check()
+    for a, b in zip(two + [g32], fused + [gf]):
+        ga, gb = bits(a.t), bits(b.t)
+        na, nb = np.isnan(ga.view(np.float32)), np.isnan(gb.view(np.float32))
+        np.testing.assert_array_equal(na, nb)
+        np.testing.assert_array_equal(ga[~na], gb[~na])
+    np.testing.assert_array_equal(bits(p2.t), bits(pf.t))
