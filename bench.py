@@ -172,7 +172,7 @@ def _timed(fn, reps):
     return sum(e[0].elapsed_time(e[1]) for e in evs) / reps
 
 
-def extra_measurements(W, reps) -> dict:
+def extra_measurements(W, reps, small: bool = True) -> dict:
     """The engine's other entry points on the same workload, outside the
     headline step: the bf16 reduce dtype over the same 32 slices, and the
     fp32 -> bf16 cast copy-in of every group from fp32 parameters."""
@@ -221,6 +221,20 @@ def extra_measurements(W, reps) -> dict:
                                   "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     del dst, rs, half
     torch.cuda.empty_cache()
+    if not small:
+        return out
+    # one transformer block's shard at a time, the granularity at which FSDP
+    # reduces a group: 8 gradient buffers (grad_acc = 1) of 25,297,920 elements
+    sb = 25_297_920
+    sl1 = [t[:sb] for t in W["slices"][:N]]
+    gb, th, m, v, pb = (W[k][:sb] for k in ("grad32", "master", "exp_avg", "exp_avg_sq", "p16"))
+    ms_r = _timed(lambda: fs.fs_reduce_shard(sl1, gb, N, 1), reps)
+    ms_a = _timed(lambda: fs.fs_adamw_step(th, m, v, gb, pb, lr=1e-3, step=2), reps)
+    br, ba = (2 * N + 4) * sb, 30 * sb
+    out["block_shard_grad_acc_1"] = {
+        "shard_numel": sb,
+        "reduce": {"us": round(ms_r * 1e3, 1), "GB": round(br / 1e9, 3), "GBps": round(br / (ms_r * 1e-3) / 1e9, 1)},
+        "adamw": {"us": round(ms_a * 1e3, 1), "GB": round(ba / 1e9, 3), "GBps": round(ba / (ms_a * 1e-3) / 1e9, 1)}}
     return out
 
 
@@ -357,7 +371,7 @@ def traffic_for(kernel: str, launch_bytes_alg: float):
 
 
 KERNELS = {  # rocprofv3 kernel-name fragment -> bench phase
-    "reduce_chunk_kernel": "reduce",
+    "reduce_chunk_kernel<16>": "reduce",
     "scatter_kernel<2, (anonymous namespace)::UnpackSrc": "reshard",
     "reduce_rs_chunk_kernel": "reduce_bf16_reduce_dtype",
     "pack_cast_kernel": "pack_cast",
@@ -410,7 +424,7 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     f_write = copy_bytes / (avg["copy_kernel"]["WRITE_SIZE"] * 1024)
     # algorithmic bytes per launch of the 7B shard step
     S, N, A = 842301440, 8, 4
-    alg = {"reduce_chunk_kernel": (2 * N * A + 4) * S, "adamw_wave_kernel": 30 * S,
+    alg = {"reduce_chunk_kernel<16>": (2 * N * A + 4) * S, "adamw_wave_kernel": 30 * S,
            "reduce_adamw_chunk_kernel": (2 * N * A + 26) * S,
            "reduce_rs_chunk_kernel": (2 * N * A + 4) * S,
            "copy_kernel": 2 * copy_bytes}
@@ -482,9 +496,9 @@ def main():
     ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-tiny", action="store_true",
-                    help="skip the tiny launch-bound step (its small launches would mix into a "
-                         "per-kernel profile of the 7B step)")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the tiny launch-bound step and the one-block measurement (their small "
+                         "launches would mix into a per-kernel profile of the 7B step)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this engine runs all N logical ranks on one GPU; "
@@ -539,9 +553,9 @@ def main():
     torch.cuda.synchronize()
     fused_ms = sum(e[0].elapsed_time(e[1]) for e in fz) / args.steps
     fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
-    extra = extra_measurements(W, args.steps)
+    extra = extra_measurements(W, args.steps, small=not args.no_small)
     ceiling = copy_ceiling(fs)
-    tiny = None if args.no_tiny else tiny_step_latency(fs)
+    tiny = None if args.no_small else tiny_step_latency(fs)
 
     kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
                                   "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
@@ -574,7 +588,7 @@ def main():
         "reduce_adamw_frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4),
         "copy_ceiling_GBps": round(ceiling, 1),
         "tiny_mlp_step": tiny,
-        "roofline": {"bound": "hbm", "kernel": "reduce_chunk_kernel", "achieved": round(red_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "reduce_chunk_kernel<16>", "achieved": round(red_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(red_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": alg["reduce"]},
         "cpu_baseline": None,

@@ -397,14 +397,17 @@ __global__ __launch_bounds__(kThreads) void pack_cast_kernel(const Segment *__re
 // is exactly the sequential one with no cross-lane traffic.
 //
 // Main kernel (16-byte-aligned slices and output): a workgroup owns a chunk
-// of kThreads*4*kRedGroups elements and walks the slices one after another,
-// reading kRedGroups groups of 4 bf16 (8 bytes) per lane from the current
-// slice -- 16 KB contiguous per slice per workgroup -- while the next slice's
-// loads are already in flight (two register slots).  The 4*kRedGroups fp32
-// accumulators live in registers; the chunk is written once, 16 bytes per
-// lane, every store instruction covering 1 KB contiguous.  Reading each
-// slice in long contiguous runs keeps the HBM row buffers busy on one stream
-// at a time, which measured faster than interleaving all slices per element.
+// of kThreads*4*G elements and walks the slices one after another, reading G
+// groups of 4 bf16 (8 bytes) per lane from the current slice -- 2*G KB
+// contiguous per slice per workgroup -- while the next slice's loads are
+// already in flight (two register slots).  The 4*G fp32 accumulators live in
+// registers; the chunk is written once, 16 bytes per lane, every store
+// instruction covering 1 KB contiguous.  Reading each slice in long
+// contiguous runs keeps the HBM row buffers busy on one stream at a time,
+// which measured faster than interleaving all slices per element.  G = 16
+// (32 KB per slice) for passes of more than 16 terms; fewer terms give each
+// workgroup little work, and G = 4 (more, shorter workgroups) measured 6-10%
+// faster there (8 terms) and no slower at 16.
 //
 // General kernel (misaligned slices or output, and the chunk remainder):
 // lane i owns 8 consecutive elements, one 16-byte (funnel-shifted when
@@ -509,23 +512,17 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nter
     }
 }
 
-#ifndef FS_RED_GROUPS
-#define FS_RED_GROUPS 16
-#endif
-constexpr int kRedGroups = FS_RED_GROUPS;
-constexpr int64_t kRedChunk = (int64_t)kThreads * 4 * kRedGroups;   // 16384 elements by default
+constexpr int kRedGroupsMany = 16;                                      // passes of > kRedFewTerms terms
+constexpr int kRedGroupsFew = 4;                                        // passes of <= kRedFewTerms terms
+constexpr int kRedFewTerms = 16;
+constexpr int64_t kRedChunk = (int64_t)kThreads * 4 * kRedGroupsMany;  // 16384 elements
+constexpr int64_t kRedChunkFew = (int64_t)kThreads * 4 * kRedGroupsFew; // 4096 elements
 
 __device__ __forceinline__ void add_bf16x4(float *acc, u32x2 v) {
     acc[0] = acc[0] + __uint_as_float(v.x << 16);
     acc[1] = acc[1] + __uint_as_float(v.x & 0xFFFF0000u);
     acc[2] = acc[2] + __uint_as_float(v.y << 16);
     acc[3] = acc[3] + __uint_as_float(v.y & 0xFFFF0000u);
-}
-
-__device__ __forceinline__ void load_groups(u32x2 (&x)[kRedGroups], const uint16_t *p, int64_t base) {
-#pragma unroll
-    for (int u = 0; u < kRedGroups; ++u)
-        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
 }
 
 template <int G>
@@ -535,17 +532,18 @@ __device__ __forceinline__ void load_groups_n(u32x2 (&x)[G], const uint16_t *p, 
         x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
 }
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
                                                                 int last_pass, float world,
                                                                 float *__restrict__ out) {
-    const int64_t base = (int64_t)blockIdx.x * kRedChunk + 4 * threadIdx.x;
-    float acc[4 * kRedGroups];
-    u32x2 xa[kRedGroups], xb[kRedGroups];
+    const int64_t base = (int64_t)blockIdx.x * ((int64_t)kThreads * 4 * G) + 4 * threadIdx.x;
+    float acc[4 * G];
+    u32x2 xa[G], xb[G];
     int t = 0;
     if (first_pass) {
-        load_groups(xa, sa.p[0], base);
+        load_groups_n<G>(xa, sa.p[0], base);
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) {
+        for (int u = 0; u < G; ++u) {
             acc[4 * u] = __uint_as_float(xa[u].x << 16);
             acc[4 * u + 1] = __uint_as_float(xa[u].x & 0xFFFF0000u);
             acc[4 * u + 2] = __uint_as_float(xa[u].y << 16);
@@ -554,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, in
         t = 1;
     } else {
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) {
+        for (int u = 0; u < G; ++u) {
             const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(out + base + u * kThreads * 4));
             acc[4 * u] = __uint_as_float(o.x);
             acc[4 * u + 1] = __uint_as_float(o.y);
@@ -563,23 +561,23 @@ __global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, in
         }
     }
     // two-slot pipeline: slice t is added while slice t+1 is loading
-    if (t < nterms) load_groups(xa, sa.p[t], base);
+    if (t < nterms) load_groups_n<G>(xa, sa.p[t], base);
     while (t < nterms) {
-        if (t + 1 < nterms) load_groups(xb, sa.p[t + 1], base);
+        if (t + 1 < nterms) load_groups_n<G>(xb, sa.p[t + 1], base);
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xa[u]);
+        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xa[u]);
         if (++t >= nterms) break;
-        if (t + 1 < nterms) load_groups(xa, sa.p[t + 1], base);
+        if (t + 1 < nterms) load_groups_n<G>(xa, sa.p[t + 1], base);
 #pragma unroll
-        for (int u = 0; u < kRedGroups; ++u) add_bf16x4(acc + 4 * u, xb[u]);
+        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xb[u]);
         ++t;
     }
     if (last_pass) {
 #pragma unroll
-        for (int e = 0; e < 4 * kRedGroups; ++e) acc[e] = acc[e] / world;
+        for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
     }
 #pragma unroll
-    for (int u = 0; u < kRedGroups; ++u)
+    for (int u = 0; u < G; ++u)
         st16(reinterpret_cast<char *>(out + base + u * kThreads * 4),
              u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
                    __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])});
@@ -1248,22 +1246,28 @@ extern "C" int fs_reduce_shard(int64_t n, int32_t world, int32_t grad_acc, const
     bool aligned = false, skip = false;
     if (int rc = check_reduce("fs_reduce_shard", n, world, grad_acc, slices, out, &terms, &aligned, &skip)) return rc;
     if (skip) return FS_OK;
-    const int64_t nchunks = aligned ? n / kRedChunk : 0;
-    const int64_t done = nchunks * kRedChunk;
-    const int64_t rest = n - done;
-    const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
-    if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
+    // the largest grids any pass can need: the small chunk, or everything element-wise
+    if ((aligned ? n / kRedChunkFew : 0) > INT32_MAX || ((n >> 3) + kThreads - 1) / kThreads > INT32_MAX)
         return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large for one launch");
     (void)hipGetLastError();
     for (int t0 = 0; t0 < terms; t0 += kTermsPerPass) {
         const int cnt = std::min(kTermsPerPass, terms - t0);
         const int first = t0 == 0, last = t0 + cnt == terms;
+        const bool few = cnt <= kRedFewTerms;
+        const int64_t chunk = few ? kRedChunkFew : kRedChunk;
+        const int64_t nchunks = aligned ? n / chunk : 0;
+        const int64_t done = nchunks * chunk;
+        const int64_t rest = n - done;
+        const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
         SliceArgs sa;
         memset(&sa, 0, sizeof sa);
         for (int k = 0; k < cnt; ++k) sa.p[k] = slices[t0 + k];
-        if (nchunks > 0)
-            hipLaunchKernelGGL(reduce_chunk_kernel, dim3((uint32_t)nchunks), dim3(kThreads), 0, stream, sa, cnt,
-                               first, last, (float)world, out);
+        if (nchunks > 0 && few)
+            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsFew>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
+                               stream, sa, cnt, first, last, (float)world, out);
+        else if (nchunks > 0)
+            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsMany>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
+                               stream, sa, cnt, first, last, (float)world, out);
         if (rest > 0) {   // the chunk remainder, or everything when misaligned
             SliceArgs sr;   // advanced by `done`, a multiple of 8 elements: alignment is kept
             memset(&sr, 0, sizeof sr);
@@ -1470,8 +1474,8 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
         for (int k = 0; k < kTermsPerPass; ++k) sa.p[k] = slices[t0 + k];
         const int64_t pre_chunks = done / kRedChunk, pre_done = pre_chunks * kRedChunk;
         if (pre_chunks > 0)
-            hipLaunchKernelGGL(reduce_chunk_kernel, dim3((uint32_t)pre_chunks), dim3(kThreads), 0, stream, sa,
-                               kTermsPerPass, (int)(t0 == 0), 0, (float)world, grad_out);
+            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsMany>, dim3((uint32_t)pre_chunks), dim3(kThreads), 0,
+                               stream, sa, kTermsPerPass, (int)(t0 == 0), 0, (float)world, grad_out);
         if (done > pre_done) {   // [pre_done, done): fused chunks smaller than the reduce chunk
             SliceArgs sm;
             memset(&sm, 0, sizeof sm);
