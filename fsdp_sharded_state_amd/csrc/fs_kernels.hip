@@ -594,22 +594,23 @@ __global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, in
 // running micro-step sum.  A pass holds whole micro-steps (floor(32/N) of
 // them); passes carry the fp32 accumulator through `out`.
 
-constexpr int kRsGroups = 8;
-constexpr int64_t kRsChunk = (int64_t)kThreads * 4 * kRsGroups;   // 8192 elements
+constexpr int kRsGroupsMany = 8;   // passes of more than kRedFewTerms terms: 8192-element chunks
+constexpr int kRsGroupsFew = 4;    // up to kRedFewTerms terms: 4096-element chunks (5% faster at 8 terms)
 
 __device__ __forceinline__ float bf16_round_f32(float f) {
     return __uint_as_float((uint32_t)bf16_rne_bits(__float_as_uint(f)) << 16);
 }
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void reduce_rs_chunk_kernel(SliceArgs sa, int nsteps, int world,
                                                                    int first_pass, float worldf,
                                                                    float *__restrict__ out) {
-    const int64_t base = (int64_t)blockIdx.x * kRsChunk + 4 * threadIdx.x;
-    float acc[4 * kRsGroups], sum[4 * kRsGroups];
-    u32x2 xa[kRsGroups], xb[kRsGroups];
+    const int64_t base = (int64_t)blockIdx.x * ((int64_t)kThreads * 4 * G) + 4 * threadIdx.x;
+    float acc[4 * G], sum[4 * G];
+    u32x2 xa[G], xb[G];
     if (!first_pass) {
 #pragma unroll
-        for (int u = 0; u < kRsGroups; ++u) {
+        for (int u = 0; u < G; ++u) {
             const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(out + base + u * kThreads * 4));
             acc[4 * u] = __uint_as_float(o.x);
             acc[4 * u + 1] = __uint_as_float(o.y);
@@ -619,10 +620,10 @@ __global__ __launch_bounds__(kThreads) void reduce_rs_chunk_kernel(SliceArgs sa,
     }
     const int total = nsteps * world;
     // add term t (held in x) into the micro-step sum; fold the finished micro-step into acc
-    auto consume = [&](const u32x2 (&x)[kRsGroups], int t) {
+    auto consume = [&](const u32x2 (&x)[G], int t) {
         const int k = t % world, j = t / world;
 #pragma unroll
-        for (int u = 0; u < kRsGroups; ++u) {
+        for (int u = 0; u < G; ++u) {
             const float w[4] = {__uint_as_float(x[u].x << 16), __uint_as_float(x[u].x & 0xFFFF0000u),
                                 __uint_as_float(x[u].y << 16), __uint_as_float(x[u].y & 0xFFFF0000u)};
 #pragma unroll
@@ -630,24 +631,24 @@ __global__ __launch_bounds__(kThreads) void reduce_rs_chunk_kernel(SliceArgs sa,
         }
         if (k == world - 1) {
 #pragma unroll
-            for (int e = 0; e < 4 * kRsGroups; ++e) {
+            for (int e = 0; e < 4 * G; ++e) {
                 const float d = bf16_round_f32(sum[e] / worldf);
                 acc[e] = (first_pass && j == 0) ? d : acc[e] + d;
             }
         }
     };
     int t = 0;
-    if (t < total) load_groups_n<kRsGroups>(xa, sa.p[t], base);
+    if (t < total) load_groups_n<G>(xa, sa.p[t], base);
     while (t < total) {
-        if (t + 1 < total) load_groups_n<kRsGroups>(xb, sa.p[t + 1], base);
+        if (t + 1 < total) load_groups_n<G>(xb, sa.p[t + 1], base);
         consume(xa, t);
         if (++t >= total) break;
-        if (t + 1 < total) load_groups_n<kRsGroups>(xa, sa.p[t + 1], base);
+        if (t + 1 < total) load_groups_n<G>(xa, sa.p[t + 1], base);
         consume(xb, t);
         ++t;
     }
 #pragma unroll
-    for (int u = 0; u < kRsGroups; ++u)
+    for (int u = 0; u < G; ++u)
         st16(reinterpret_cast<char *>(out + base + u * kThreads * 4),
              u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
                    __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])});
@@ -826,32 +827,30 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t begin, i
 // (unless the caller asks for it).  Traffic per element: 2*A*N + 26 bytes
 // instead of 2*A*N + 4 + 30.
 
-#ifndef FS_FUSED_GROUPS
-#define FS_FUSED_GROUPS 8
-#endif
-#ifndef FS_FUSED_BATCH
-#define FS_FUSED_BATCH 4
-#endif
-constexpr int kFusedGroups = FS_FUSED_GROUPS;
-constexpr int kFusedBatch = FS_FUSED_BATCH < FS_FUSED_GROUPS ? FS_FUSED_BATCH : FS_FUSED_GROUPS;
-constexpr int64_t kFusedChunk = (int64_t)kThreads * 4 * kFusedGroups;
+// G groups of 4 elements per lane: 8 (8192-element chunks) for a final pass of
+// more than kRedFewTerms terms, 4 for fewer (2-3% faster at 8 terms, as for
+// the plain reduce); AdamW runs in batches of kFusedBatch groups.
+constexpr int kFusedGroupsMany = 8;
+constexpr int kFusedGroupsFew = 4;
+constexpr int kFusedBatch = 4;
 
 
-template <bool HAS_P16, bool HAS_G>
+template <int G, bool HAS_P16, bool HAS_G>
 __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
                                                                       float world, float *__restrict__ th,
                                                                       float *__restrict__ m,
                                                                       float *__restrict__ v,
                                                                       uint16_t *__restrict__ p16,
                                                                       float *__restrict__ gout, AdamConsts c) {
-    const int64_t base = (int64_t)blockIdx.x * kFusedChunk + 4 * threadIdx.x;
-    float acc[4 * kFusedGroups];
-    u32x2 xa[kFusedGroups], xb[kFusedGroups];
+    const int64_t base = (int64_t)blockIdx.x * ((int64_t)kThreads * 4 * G) + 4 * threadIdx.x;
+    constexpr int KB = kFusedBatch < G ? kFusedBatch : G;
+    float acc[4 * G];
+    u32x2 xa[G], xb[G];
     int t = 0;
     if (first_pass) {
-        load_groups_n<kFusedGroups>(xa, sa.p[0], base);
+        load_groups_n<G>(xa, sa.p[0], base);
 #pragma unroll
-        for (int u = 0; u < kFusedGroups; ++u) {
+        for (int u = 0; u < G; ++u) {
             acc[4 * u] = __uint_as_float(xa[u].x << 16);
             acc[4 * u + 1] = __uint_as_float(xa[u].x & 0xFFFF0000u);
             acc[4 * u + 2] = __uint_as_float(xa[u].y << 16);
@@ -860,7 +859,7 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
         t = 1;
     } else {   // partial sums of the earlier terms, left in gout by the reduce passes
 #pragma unroll
-        for (int u = 0; u < kFusedGroups; ++u) {
+        for (int u = 0; u < G; ++u) {
             const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(gout + base + u * kThreads * 4));
             acc[4 * u] = __uint_as_float(o.x);
             acc[4 * u + 1] = __uint_as_float(o.y);
@@ -868,11 +867,11 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
             acc[4 * u + 3] = __uint_as_float(o.w);
         }
     }
-    constexpr int NB = kFusedGroups / kFusedBatch;
-    float T[2][4 * kFusedBatch], M[2][4 * kFusedBatch], V[2][4 * kFusedBatch];
+    constexpr int NB = G / KB;
+    float T[2][4 * KB], M[2][4 * KB], V[2][4 * KB];
     auto load_state = [&](int slot, int u0) {
 #pragma unroll
-        for (int q = 0; q < kFusedBatch; ++q) {
+        for (int q = 0; q < KB; ++q) {
             const int64_t e = base + (u0 + q) * kThreads * 4;
             f4(ld16(reinterpret_cast<const char *>(th + e)), T[slot] + 4 * q);
             f4(ld16(reinterpret_cast<const char *>(m + e)), M[slot] + 4 * q);
@@ -880,30 +879,30 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
         }
     };
     load_state(0, 0);   // independent of the reduce: in flight during the slice loop
-    if (t < nterms) load_groups_n<kFusedGroups>(xa, sa.p[t], base);
+    if (t < nterms) load_groups_n<G>(xa, sa.p[t], base);
     while (t < nterms) {
-        if (t + 1 < nterms) load_groups_n<kFusedGroups>(xb, sa.p[t + 1], base);
+        if (t + 1 < nterms) load_groups_n<G>(xb, sa.p[t + 1], base);
 #pragma unroll
-        for (int u = 0; u < kFusedGroups; ++u) add_bf16x4(acc + 4 * u, xa[u]);
+        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xa[u]);
         if (++t >= nterms) break;
-        if (t + 1 < nterms) load_groups_n<kFusedGroups>(xa, sa.p[t + 1], base);
+        if (t + 1 < nterms) load_groups_n<G>(xa, sa.p[t + 1], base);
 #pragma unroll
-        for (int u = 0; u < kFusedGroups; ++u) add_bf16x4(acc + 4 * u, xb[u]);
+        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xb[u]);
         ++t;
     }
 #pragma unroll
-    for (int e = 0; e < 4 * kFusedGroups; ++e) acc[e] = acc[e] / world;
-    // AdamW on the lane's groups, kFusedBatch groups (4*kFusedBatch elements)
-    // at a time; batch b+1's state loads are issued before batch b's update
-    // (batch 0's before the slice loop), so they overlap the arithmetic.
+    for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
+    // AdamW on the lane's groups, KB groups (4*KB elements) at a time; batch
+    // b+1's state loads are issued before batch b's update (batch 0's before
+    // the slice loop), so they overlap the arithmetic.
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
-        const int slot = bi & 1, u0 = bi * kFusedBatch;
-        if (bi + 1 < NB) load_state(slot ^ 1, u0 + kFusedBatch);
+        const int slot = bi & 1, u0 = bi * KB;
+        if (bi + 1 < NB) load_state(slot ^ 1, u0 + KB);
 #pragma unroll
-        for (int k = 0; k < 4 * kFusedBatch; ++k) adam_elem(c, acc[4 * u0 + k], T[slot][k], M[slot][k], V[slot][k]);
+        for (int k = 0; k < 4 * KB; ++k) adam_elem(c, acc[4 * u0 + k], T[slot][k], M[slot][k], V[slot][k]);
 #pragma unroll
-        for (int q = 0; q < kFusedBatch; ++q) {
+        for (int q = 0; q < KB; ++q) {
             const int64_t e = base + (u0 + q) * kThreads * 4;
             st16(reinterpret_cast<char *>(th + e), u4(T[slot] + 4 * q));
             st16(reinterpret_cast<char *>(m + e), u4(M[slot] + 4 * q));
@@ -1041,6 +1040,24 @@ int check_launch(const char *what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fsi::fail(FS_E_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
     return FS_OK;
+}
+
+template <int G>
+void launch_fused_chunks(int64_t nchunks, hipStream_t stream, const SliceArgs &sa, int cnt, int first, float world,
+                         float *th, float *m, float *v, uint16_t *p16, float *gout, const AdamConsts &c) {
+    const dim3 g((uint32_t)nchunks), b(kThreads);
+    if (p16 && gout)
+        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, true>), g, b, 0, stream, sa, cnt, first, world, th, m,
+                           v, p16, gout, c);
+    else if (p16)
+        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, false>), g, b, 0, stream, sa, cnt, first, world, th,
+                           m, v, p16, gout, c);
+    else if (gout)
+        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, true>), g, b, 0, stream, sa, cnt, first, world, th,
+                           m, v, p16, gout, c);
+    else
+        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, false>), g, b, 0, stream, sa, cnt, first, world, th,
+                           m, v, p16, gout, c);
 }
 
 bool ranges_overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
@@ -1298,16 +1315,19 @@ extern "C" int fs_reduce_shard_ex(int64_t n, int32_t world, int32_t grad_acc, fs
     if (world > kTermsPerPass)
         return fsi::fail(FS_E_UNSUPPORTED, "fs_reduce_shard_ex: bf16 reduce dtype supports world <= %d", kTermsPerPass);
     const int steps_per_pass = kTermsPerPass / world;
-    const int64_t nchunks = aligned ? n / kRsChunk : 0;
-    const int64_t done = nchunks * kRsChunk;
-    const int64_t rest = n - done;
-    const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
-    if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
+    if ((aligned ? n / ((int64_t)kThreads * 4 * kRsGroupsFew) : 0) > INT32_MAX ||
+        ((n >> 3) + kThreads - 1) / kThreads > INT32_MAX)
         return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard_ex: n too large for one launch");
     (void)hipGetLastError();
     for (int j0 = 0; j0 < grad_acc; j0 += steps_per_pass) {
         const int steps = std::min(steps_per_pass, grad_acc - j0);
         const int first = j0 == 0;
+        const bool few = steps * world <= kRedFewTerms;
+        const int64_t chunk = (int64_t)kThreads * 4 * (few ? kRsGroupsFew : kRsGroupsMany);
+        const int64_t nchunks = aligned ? n / chunk : 0;
+        const int64_t done = nchunks * chunk;
+        const int64_t rest = n - done;
+        const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
         SliceArgs sa, sr;
         memset(&sa, 0, sizeof sa);
         memset(&sr, 0, sizeof sr);
@@ -1315,9 +1335,12 @@ extern "C" int fs_reduce_shard_ex(int64_t n, int32_t world, int32_t grad_acc, fs
             sa.p[k] = slices[j0 * world + k];
             sr.p[k] = slices[j0 * world + k] + done;
         }
-        if (nchunks > 0)
-            hipLaunchKernelGGL(reduce_rs_chunk_kernel, dim3((uint32_t)nchunks), dim3(kThreads), 0, stream, sa, steps,
-                               (int)world, first, (float)world, out);
+        if (nchunks > 0 && few)
+            hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsFew>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
+                               stream, sa, steps, (int)world, first, (float)world, out);
+        else if (nchunks > 0)
+            hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsMany>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
+                               stream, sa, steps, (int)world, first, (float)world, out);
         if (rest > 0) {
             if (aligned)
                 hipLaunchKernelGGL(reduce_rs_general_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
@@ -1458,16 +1481,18 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
                 return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: an output overlaps slice %d", t);
     }
     const AdamConsts c = adam_consts(*hp);
-    const int64_t nchunks = aligned ? n / kFusedChunk : 0;
-    const int64_t done = nchunks * kFusedChunk;
+    // terms beyond the last kTermsPerPass: plain reduce passes leave partial sums in grad_out
+    const int last_cnt = terms - (terms - 1) / kTermsPerPass * kTermsPerPass;
+    const int t_last = terms - last_cnt;
+    const bool few = last_cnt <= kRedFewTerms;
+    const int64_t chunk = (int64_t)kThreads * 4 * (few ? kFusedGroupsFew : kFusedGroupsMany);
+    const int64_t nchunks = aligned ? n / chunk : 0;
+    const int64_t done = nchunks * chunk;
     const int64_t rest = n - done;
     const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
     if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
         return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: n too large for one launch");
     (void)hipGetLastError();
-    // terms beyond the last kTermsPerPass: plain reduce passes leave partial sums in grad_out
-    const int last_cnt = terms - (terms - 1) / kTermsPerPass * kTermsPerPass;
-    const int t_last = terms - last_cnt;
     for (int t0 = 0; t0 < t_last; t0 += kTermsPerPass) {
         SliceArgs sa;
         memset(&sa, 0, sizeof sa);
@@ -1502,19 +1527,12 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
     for (int k = 0; k < last_cnt; ++k) sa.p[k] = slices[t_last + k];
     const int first = t_last == 0;
     if (nchunks > 0) {
-        const dim3 g((uint32_t)nchunks), b(kThreads);
-        if (param_bf16 && grad_out)
-            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<true, true>), g, b, 0, stream, sa, last_cnt, first,
-                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
-        else if (param_bf16)
-            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<true, false>), g, b, 0, stream, sa, last_cnt, first,
-                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
-        else if (grad_out)
-            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<false, true>), g, b, 0, stream, sa, last_cnt, first,
-                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
+        if (few)
+            launch_fused_chunks<kFusedGroupsFew>(nchunks, stream, sa, last_cnt, first, (float)world, master, exp_avg,
+                                                 exp_avg_sq, param_bf16, grad_out, c);
         else
-            hipLaunchKernelGGL((reduce_adamw_chunk_kernel<false, false>), g, b, 0, stream, sa, last_cnt, first,
-                               (float)world, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
+            launch_fused_chunks<kFusedGroupsMany>(nchunks, stream, sa, last_cnt, first, (float)world, master,
+                                                  exp_avg, exp_avg_sq, param_bf16, grad_out, c);
     }
     if (rest > 0) {
         SliceArgs sr;
