@@ -294,6 +294,74 @@ def tiny_step_latency(fs, reps=200) -> dict:
             "launches_per_step": 4, "shard_numel": S}
 
 
+def stream_ceilings(fs, nbytes=8 << 30, reps=5) -> dict:
+    """Achieved GB/s of a plain read-only stream and a plain write-only
+    stream of nbytes (median of reps), the two ends between which every
+    kernel's read/write mix falls."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    fs.fs_stream_fill(a, 0x01010101)
+    out = {}
+    for name, fn in (("read", lambda: fs.fs_stream_read(a, sink)), ("write", lambda: fs.fs_stream_fill(a, 0x01010101))):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(reps):
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            times.append(s.elapsed_time(e))
+        out[name] = nbytes / (sorted(times)[len(times) // 2] * 1e-3) / 1e9
+    del a, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def own_buffer_ceilings(W, reps=3) -> dict:
+    """The reduce's and AdamW's bytes streamed over their own buffers, reads
+    and writes apart: read-only passes over every input buffer and write-only
+    passes over every output buffer, timed with events around each pass (median
+    of reps).  Same buffers, so the same physical placement as the kernels.
+    Overwrites the shard state: run it last."""
+    import torch
+    fs = W["fs"]
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+
+    def med(fn):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            s.record()
+            fn()
+            e.record()
+            e.synchronize()
+            ts.append(s.elapsed_time(e))
+        return sorted(ts)[len(ts) // 2]
+
+    out = {}
+    for name, reads, writes in (("reduce", W["slices"], [W["grad32"]]),
+                                ("adamw", [W["grad32"], W["master"], W["exp_avg"], W["exp_avg_sq"]],
+                                 [W["master"], W["exp_avg"], W["exp_avg_sq"], W["p16"]])):
+        t_r = sum(med(lambda t=t: fs.fs_stream_read(t, sink)) for t in reads)
+        t_w = sum(med(lambda t=t: fs.fs_stream_fill(t, 0)) for t in writes)
+        rb = sum(t.numel() * t.element_size() for t in reads)
+        wb = sum(t.numel() * t.element_size() for t in writes)
+        out[name] = {"read_GBps": round(rb / (t_r * 1e-3) / 1e9, 1), "write_GBps": round(wb / (t_w * 1e-3) / 1e9, 1),
+                     "ceiling_GBps": round((rb + wb) / ((t_r + t_w) * 1e-3) / 1e9, 1)}
+    return out
+
+
+def mix_ceiling(read_bytes: float, write_bytes: float, ceil: dict) -> float:
+    """GB/s a kernel moving these bytes would reach if its reads ran at the
+    read-only stream rate and its writes at the write-only rate, one after
+    the other."""
+    t = read_bytes / ceil["read"] + write_bytes / ceil["write"]
+    return (read_bytes + write_bytes) / t
+
+
 def copy_ceiling(fs, nbytes=1 << 32, reps=5):
     """Achieved GB/s of a plain dwordx4 copy (read + write) of nbytes."""
     import torch
@@ -555,6 +623,7 @@ def main():
     fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
     extra = extra_measurements(W, args.steps, small=not args.no_small)
     ceiling = copy_ceiling(fs)
+    streams = stream_ceilings(fs)
     tiny = None if args.no_small else tiny_step_latency(fs)
 
     kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
@@ -562,6 +631,20 @@ def main():
                                   "frac_hbm_peak": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                   "step_ms_with_fused": round(ms["pack"] + ms["unpack"] + fused_ms, 4)}
     kern.update(extra)
+    # each kernel against the streaming rate of its own read/write mix
+    P, S, N, A = W["P"], W["S"], W["world"], W["grad_acc"]
+    gath = sum(p.gathered_numel for p in W["plans"])
+    rw = {"pack": (2 * P, 2 * gath), "unpack": (2 * P, 2 * P), "reduce": (2 * N * A * S, 4 * S),
+          "adamw": (16 * S, 14 * S), "reduce_adamw_fused": ((2 * N * A + 12) * S, 14 * S),
+          "reduce_bf16_reduce_dtype": (2 * N * A * S, 4 * S), "pack_cast_fp32_to_bf16": (4 * P, 2 * gath),
+          "reshard_n_to_half_n": (2 * P, kern["reshard_n_to_half_n"]["GB"] * 1e9 - 2 * P)}
+    for k, (r, w) in rw.items():
+        c = mix_ceiling(r, w, streams)
+        kern[k]["mix_ceiling_GBps"] = round(c, 1)
+        kern[k]["frac_of_mix_ceiling"] = round(kern[k]["GBps"] / c, 4)
+    own = own_buffer_ceilings(W)      # last: it overwrites the shard state
+    for k, v in own.items():
+        kern[k]["own_buffers"] = dict(v, frac=round(kern[k]["GBps"] / v["ceiling_GBps"], 4))
     red_gbps = alg["reduce"] / (ms["reduce"] * 1e-3) / 1e9
     traffic = traffic_for("reduce", alg["reduce"])
     out = {
@@ -587,6 +670,7 @@ def main():
         "reduce_adamw_GBps": round(ra_gbps, 1),
         "reduce_adamw_frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4),
         "copy_ceiling_GBps": round(ceiling, 1),
+        "stream_ceilings_GBps": {k: round(v, 1) for k, v in streams.items()},
         "tiny_mlp_step": tiny,
         "roofline": {"bound": "hbm", "kernel": "reduce_chunk_kernel<16>", "achieved": round(red_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(red_gbps / HBM_PEAK_GBPS, 4),

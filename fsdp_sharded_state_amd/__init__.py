@@ -101,13 +101,15 @@ def lib() -> ctypes.CDLL:
     L.fs_pack_cast.argtypes = [vp, vp, i32, vp, i32, vp]
     L.fs_reduce_adamw_step.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamWHparams), vp]
     L.fs_copy_bytes.argtypes = [vp, vp, i64, vp]
+    L.fs_stream_read.argtypes = [vp, i64, vp, vp]
+    L.fs_stream_fill.argtypes = [vp, i64, ctypes.c_uint32, vp]
     L.fs_last_error.argtypes = []
     L.fs_last_error.restype = ctypes.c_char_p
     for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
                  "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_reduce_adamw_step",
                  "fs_reduce_shard_ex", "fs_pack_cast", "fs_reshard_plan", "fs_reshard_info",
                  "fs_reshard_upload", "fs_reshard",
-                 "fs_copy_bytes"):
+                 "fs_copy_bytes", "fs_stream_read", "fs_stream_fill"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -470,3 +472,18 @@ def fs_copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None):
     if dst.numel() * dst.element_size() != nb:
         raise ValueError("fs_copy_bytes: size mismatch")
     _check(lib().fs_copy_bytes(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), nb, _stream(stream)))
+
+
+def fs_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Read-only stream over src's bytes (measurement aid); sink: a device
+    tensor of at least 4 bytes that may receive an unspecified value."""
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("fs_stream_read: sink needs 4 bytes")
+    _check(lib().fs_stream_read(_dev_ptr(src, "src"), src.numel() * src.element_size(), _dev_ptr(sink, "sink"),
+                                _stream(stream)))
+
+
+def fs_stream_fill(dst: torch.Tensor, value: int, stream=None):
+    """Write-only stream: every 32-bit word of dst becomes `value` (measurement aid)."""
+    _check(lib().fs_stream_fill(_dev_ptr(dst, "dst"), dst.numel() * dst.element_size(), int(value) & 0xFFFFFFFF,
+                                _stream(stream)))

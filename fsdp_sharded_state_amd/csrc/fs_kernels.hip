@@ -977,6 +977,36 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArg
 
 // ------------------------------------------------------------------ copy --
 
+// Read-only and write-only streams (measurement aids), dwordx4 accesses with
+// every instruction covering 4 KB of the workgroup's contiguous range: the
+// read stream keeps 16 loads per lane in flight (64 KB per workgroup; 4 per
+// lane measured 3% slower), the write stream 4 stores per lane.
+constexpr int kReadVecs = 16;
+__global__ __launch_bounds__(kThreads) void read_kernel(const char *__restrict__ src, int64_t nvec,
+                                                        uint32_t *__restrict__ sink) {
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kReadVecs + threadIdx.x;
+    uint32_t x = 0;
+#pragma unroll
+    for (int u = 0; u < kReadVecs; ++u) {
+        const int64_t i = i0 + u * kThreads;
+        if (i < nvec) {
+            const u32x4 v = ld16(src + 16 * i);
+            x ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+    if (x == 0x9E3779B9u) sink[0] = x;   // data-dependent, so the loads stay; rarely taken
+}
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(char *__restrict__ dst, int64_t nvec, uint32_t value) {
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads * 4 + threadIdx.x;
+    const u32x4 v = {value, value, value, value};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u * kThreads;
+        if (i < nvec) st16(dst + 16 * i, v);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void copy_kernel(char *__restrict__ dst,
                                                         const char *__restrict__ src, int64_t nvec) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -1550,6 +1580,36 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
                                exp_avg_sq + done, p16r, gr, c);
     }
     return check_launch("fs_reduce_adamw_step");
+}
+
+extern "C" int fs_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream) {
+    fsi::clear_error();
+    if (bytes < 0 || (bytes & 15)) return fsi::fail(FS_E_INVAL, "fs_stream_read: bytes must be a multiple of 16");
+    if (bytes == 0) return FS_OK;
+    if (!src || !sink) return fsi::fail(FS_E_INVAL, "fs_stream_read: NULL pointer");
+    if (misaligned(src, 16) || misaligned(sink, 4)) return fsi::fail(FS_E_ALIGN, "fs_stream_read: misaligned pointer");
+    const int64_t nvec = bytes / 16;
+    const int64_t grid = (nvec + kReadVecs * kThreads - 1) / (kReadVecs * kThreads);
+    if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_stream_read: too large for one launch");
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(read_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, static_cast<const char *>(src),
+                       nvec, sink);
+    return check_launch("fs_stream_read");
+}
+
+extern "C" int fs_stream_fill(void *dst, int64_t bytes, uint32_t value, hipStream_t stream) {
+    fsi::clear_error();
+    if (bytes < 0 || (bytes & 15)) return fsi::fail(FS_E_INVAL, "fs_stream_fill: bytes must be a multiple of 16");
+    if (bytes == 0) return FS_OK;
+    if (!dst) return fsi::fail(FS_E_INVAL, "fs_stream_fill: NULL pointer");
+    if (misaligned(dst, 16)) return fsi::fail(FS_E_ALIGN, "fs_stream_fill: dst must be 16-byte aligned");
+    const int64_t nvec = bytes / 16;
+    const int64_t grid = (nvec + 4 * kThreads - 1) / (4 * kThreads);
+    if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_stream_fill: too large for one launch");
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fill_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, static_cast<char *>(dst), nvec,
+                       value);
+    return check_launch("fs_stream_fill");
 }
 
 extern "C" int fs_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t stream) {

@@ -378,6 +378,19 @@ int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc,
  */
 int fs_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t stream);
 
+/*
+ * fs_stream_read / fs_stream_fill -- measurement aids beside fs_copy_bytes,
+ * not part of the method: the HBM read-only and write-only streaming rates
+ * that, with the copy rate, bound each kernel's read/write mix.
+ * fs_stream_read reads `bytes` bytes at src and discards them; sink (device,
+ * 4 bytes) may receive an unspecified value.  fs_stream_fill writes the
+ * 32-bit `value` over `bytes` bytes at dst.  Pointers 16-byte aligned (sink
+ * 4-byte), bytes a multiple of 16.  Errors: FS_E_INVAL, FS_E_ALIGN,
+ * FS_E_OVERFLOW, FS_E_HIP.
+ */
+int fs_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
+int fs_stream_fill(void *dst, int64_t bytes, uint32_t value, hipStream_t stream);
+
 /* fs_last_error -- message for the calling thread's last failed call
  * (empty string if none).  The pointer stays valid until the next call. */
 const char *fs_last_error(void);

@@ -210,6 +210,12 @@ def test_call_validation_before_gpu():
     assert L.fs_adamw_step(8, ctypes.c_void_p(258), f, f, f, 1, None, ctypes.byref(hp), None) == fs.FS_E_ALIGN
     assert L.fs_copy_bytes(ctypes.c_void_p(256), ctypes.c_void_p(512), 15, None) == fs.FS_E_INVAL
     assert L.fs_copy_bytes(ctypes.c_void_p(264), ctypes.c_void_p(512), 16, None) == fs.FS_E_ALIGN
+    assert L.fs_stream_read(ctypes.c_void_p(256), 15, ctypes.c_void_p(512), None) == fs.FS_E_INVAL
+    assert L.fs_stream_read(ctypes.c_void_p(264), 16, ctypes.c_void_p(512), None) == fs.FS_E_ALIGN
+    assert L.fs_stream_read(ctypes.c_void_p(256), 16, None, None) == fs.FS_E_INVAL
+    assert L.fs_stream_fill(ctypes.c_void_p(256), -16, 0, None) == fs.FS_E_INVAL
+    assert L.fs_stream_fill(ctypes.c_void_p(260), 16, 0, None) == fs.FS_E_ALIGN
+    assert L.fs_stream_fill(ctypes.c_void_p(256), 0, 0, None) == fs.FS_OK           # nothing to do
 
 
 def test_fused_call_validation_before_gpu():

@@ -591,3 +591,21 @@ def test_reduce_adamw_fused_special_values(n, N, A):
         np.testing.assert_array_equal(na, nb)
         np.testing.assert_array_equal(ga[~na], gb[~na])
     np.testing.assert_array_equal(bits(p2.t), bits(pf.t))
+
+
+def test_stream_read_and_fill():
+    """The measurement aids: fill writes its word everywhere (and only inside
+    the buffer); read leaves its source untouched."""
+    n = (1 << 20) + 4 * 256 * 3 + 4    # not a whole number of workgroups
+    g = Guarded(n, torch.float32)
+    fs.fs_stream_fill(g.t, 0x3F800000)
+    torch.cuda.synchronize()
+    g.check()
+    assert (g.t == 1.0).all()
+    src = Guarded(n, torch.float32, fill=synth.normal_f32(3, 2, n, 1.0, device="cuda"))
+    before = bits(src.t)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fs.fs_stream_read(src.t, sink)
+    torch.cuda.synchronize()
+    src.check()
+    np.testing.assert_array_equal(bits(src.t), before)
