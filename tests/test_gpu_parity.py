@@ -609,3 +609,36 @@ def test_stream_read_and_fill():
     torch.cuda.synchronize()
     src.check()
     np.testing.assert_array_equal(bits(src.t), before)
+
+
+def test_deterministic_across_runs_and_streams():
+    """The fixed summation order makes every result reproducible: three runs,
+    one on a side stream, give identical bits for the reduce, the bf16 reduce
+    dtype, AdamW and the fused step."""
+    n, N, A = 16384 * 5 + 123, 8, 4
+    say("determinism", n, N, A)
+    sl = _slices(n, N * A, seed=61)
+    th0 = synth.normal_f32(61, synth.STREAM_MASTER, n, 0.02, device="cuda")
+    m0 = synth.normal_f32(61, synth.STREAM_EXP_AVG, n, 1e-3, device="cuda")
+    v0 = synth.normal_f32(61, synth.STREAM_EXP_AVG_SQ, n, 1e-3, device="cuda") ** 2
+    side = torch.cuda.Stream()
+    runs = []
+    for r in range(3):
+        st = side if r == 2 else torch.cuda.current_stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            g = torch.empty(n, device="cuda")
+            g_rs = torch.empty(n, device="cuda")
+            th, m, v = th0.clone(), m0.clone(), v0.clone()
+            thf, mf, vf = th0.clone(), m0.clone(), v0.clone()
+            p, pf = (torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+            fs.fs_reduce_shard([s.t for s in sl], g, N, A)
+            fs.fs_reduce_shard_ex([s.t for s in sl], g_rs, N, A, reduce_dtype="bf16")
+            fs.fs_adamw_step(th, m, v, g, p, step=5)
+            fs.fs_reduce_adamw_step([s.t for s in sl], thf, mf, vf, pf, None, world=N, grad_acc=A, step=5)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        runs.append([bits(x) for x in (g, g_rs, th, m, v, p, thf, mf, vf, pf)])
+    for r in (1, 2):
+        for a, b in zip(runs[0], runs[r]):
+            np.testing.assert_array_equal(a, b)
