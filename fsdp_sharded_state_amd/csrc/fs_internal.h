@@ -64,7 +64,7 @@ struct BufInfo {        // unpack destinations: 16 bytes per parameter
 struct WorkspaceLayout {
     int64_t pack_segs, n_pack_segs;
     int64_t unpack_segs, n_unpack_segs;
-    int64_t pack_tiles_all, n_pack_tiles_all;      // grid over [0, N*shard), anchored at 0
+    int64_t pack_tiles_all, n_pack_tiles_all;      // grid over [0, N*shard), anchored at 0 (may alias pack_tiles_rank)
     int64_t pack_tiles_rank, n_pack_tiles_rank;    // N grids over [r*shard, (r+1)*shard), anchored at r*shard
     int64_t unpack_tiles, n_unpack_tiles;
     int64_t bufinfo, n_bufinfo;

@@ -1115,7 +1115,8 @@ extern "C" int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hip
     const Part parts[] = {
         {w.pack_segs, plan->pack_segs.data(), w.n_pack_segs * (int64_t)sizeof(Segment)},
         {w.unpack_segs, plan->unpack_segs.data(), w.n_unpack_segs * (int64_t)sizeof(Segment)},
-        {w.pack_tiles_all, plan->pack_tiles_all.data(), w.n_pack_tiles_all * (int64_t)sizeof(Tile)},
+        // (empty when the all-ranks launch shares the per-rank table)
+        {w.pack_tiles_all, plan->pack_tiles_all.data(), (int64_t)plan->pack_tiles_all.size() * (int64_t)sizeof(Tile)},
         {w.pack_tiles_rank, plan->pack_tiles_rank.data(), w.n_pack_tiles_rank * (int64_t)sizeof(Tile)},
         {w.unpack_tiles, plan->unpack_tiles.data(), w.n_unpack_tiles * (int64_t)sizeof(Tile)},
         {w.bufinfo, plan->bufinfo.data(), w.n_bufinfo * (int64_t)sizeof(BufInfo)},

@@ -263,13 +263,22 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
                   [](const Segment &a, const Segment &b) { return a.vx < b.vx; });
 
         // ---- tiles
-        fsi::build_tiles(ps, 0, gathered, vec, fsi::kPackTileBlocks, p->pack_tiles_all);
+        // Per-rank grids (anchored at each shard's start).  When every shard
+        // starts on a 16-byte block of the gathered buffer, their concatenation
+        // is also a grid anchored at 0 and serves the all-ranks pack: one table.
         p->rank_tile_off.push_back(0);
+        p->pack_tiles_rank.reserve((size_t)world * (size_t)(ceil_div(ceil_div(shard, vec), fsi::kPackTileBlocks) + 1));
         for (int32_t r = 0; r < world; ++r) {
             fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, fsi::kPackTileBlocks,
                              p->pack_tiles_rank);
             p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
         }
+        const bool shared_grid = world == 1 || shard % vec == 0;
+        if (!shared_grid) {
+            p->pack_tiles_all.reserve((size_t)(ceil_div(ceil_div(gathered, vec), fsi::kPackTileBlocks) + 1));
+            fsi::build_tiles(ps, 0, gathered, vec, fsi::kPackTileBlocks, p->pack_tiles_all);
+        }
+        p->unpack_tiles.reserve((size_t)(ceil_div(ceil_div(vb, vec), fsi::kTileBlocks) + 1));
         fsi::build_tiles(p->unpack_segs, 0, vb, vec, fsi::kTileBlocks, p->unpack_tiles);
         for (Tile &t : p->unpack_tiles)
             if (t.run_buf >= 0) t.run_dst = t.x_begin - p->bufinfo[t.run_buf].vbase;
@@ -286,6 +295,10 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
         place((int64_t)p->unpack_segs.size(), sizeof(Segment), &w.unpack_segs, &w.n_unpack_segs);
         place((int64_t)p->pack_tiles_all.size(), sizeof(Tile), &w.pack_tiles_all, &w.n_pack_tiles_all);
         place((int64_t)p->pack_tiles_rank.size(), sizeof(Tile), &w.pack_tiles_rank, &w.n_pack_tiles_rank);
+        if (shared_grid) {   // the all-ranks launch reads the per-rank table
+            w.pack_tiles_all = w.pack_tiles_rank;
+            w.n_pack_tiles_all = w.n_pack_tiles_rank;
+        }
         place((int64_t)p->unpack_tiles.size(), sizeof(Tile), &w.unpack_tiles, &w.n_unpack_tiles);
         place((int64_t)p->bufinfo.size(), sizeof(fsi::BufInfo), &w.bufinfo, &w.n_bufinfo);
         w.total_bytes = std::max<int64_t>(off, 256);
