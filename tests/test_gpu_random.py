@@ -172,3 +172,43 @@ def test_random_reduce_family(seed):
     assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm))
     assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv))
     assert np.all(np.abs(bits(p_two.t).astype(np.int32) - rp.astype(np.int32)) <= 1)
+
+
+@pytest.mark.parametrize("mode,dt,uo", [("fsdp1", "bf16", True), ("fsdp1", "fp32", False), ("fsdp2", "bf16", False)])
+def test_many_tiny_parameters(mode, dt, uo):
+    """20,000 parameters of 1-40 elements (tens of segments per 16-byte block
+    range, so tiles are cut at the LDS segment cap): pack, unpack and re-shard
+    to N = 3 bit-exact."""
+    rng = np.random.default_rng(77)
+    shapes = [(int(x),) for x in rng.integers(1, 41, size=20000)]
+    if mode == "fsdp2":
+        shapes = [(int(x), 2) for x in rng.integers(1, 21, size=20000)]
+    N = 8
+    say("many tiny parameters", mode, dt, uo)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    plan = fs.fs_plan(shapes, dt, N, uo, mode).upload()
+    L = _olayout(mode, shapes, dt, N, uo)
+    gen = synth.bits16 if dt == "bf16" else synth.bits32
+    total = int(L.numel.sum())
+    flat = gen(5, synth.STREAM_PARAMS, total, device="cuda").view(tdt)
+    offs = np.concatenate([[0], np.cumsum(L.numel)]).astype(np.int64)
+    params = [flat[offs[i]:offs[i + 1]] for i in range(len(shapes))]
+    host_flat = bits(flat)
+    host = [host_flat[offs[i]:offs[i + 1]] for i in range(len(shapes))]
+    ref = oracle.pack(L, host)
+    G = Guarded(plan.gathered_numel, tdt)
+    fs.fs_pack(plan, params, G.t)
+    torch.cuda.synchronize()
+    G.check()
+    np.testing.assert_array_equal(bits(G.t), ref)
+    out_flat = torch.empty(total, dtype=tdt, device="cuda")
+    outs = [out_flat[offs[i]:offs[i + 1]] for i in range(len(shapes))]
+    fs.fs_unpack(plan, G.t, outs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(out_flat), host_flat)
+    plan3 = fs.fs_plan(shapes, dt, 3, uo, mode).upload()
+    D = Guarded(plan3.gathered_numel, tdt)
+    fs.fs_reshard(fs.fs_reshard_plan(plan, plan3).upload(), G.t, D.t)
+    torch.cuda.synchronize()
+    D.check()
+    np.testing.assert_array_equal(bits(D.t), oracle.reshard(L, _olayout(mode, shapes, dt, 3, uo), ref))
