@@ -172,6 +172,28 @@ def _timed(fn, reps):
     return sum(e[0].elapsed_time(e[1]) for e in evs) / reps
 
 
+def _timed_graph(fn, reps):
+    """GPU time per call of fn for launches too short to hide the Python
+    call: fn is captured once into a HIP graph and the graph replayed
+    back to back."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        g.replay()
+    e.record()
+    e.synchronize()
+    del g
+    return s.elapsed_time(e) / reps
+
+
 def extra_measurements(W, reps, small: bool = True) -> dict:
     """The engine's other entry points on the same workload, outside the
     headline step: the bf16 reduce dtype over the same 32 slices, and the
@@ -228,9 +250,24 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
     sb = 25_297_920
     sl1 = [t[:sb] for t in W["slices"][:N]]
     gb, th, m, v, pb = (W[k][:sb] for k in ("grad32", "master", "exp_avg", "exp_avg_sq", "p16"))
-    ms_r = _timed(lambda: fs.fs_reduce_shard(sl1, gb, N, 1), reps)
-    ms_a = _timed(lambda: fs.fs_adamw_step(th, m, v, gb, pb, lr=1e-3, step=2), reps)
+    ms_r = _timed_graph(lambda: fs.fs_reduce_shard(sl1, gb, N, 1), 4 * reps)
+    ms_a = _timed_graph(lambda: fs.fs_adamw_step(th, m, v, gb, pb, lr=1e-3, step=2), 4 * reps)
     br, ba = (2 * N + 4) * sb, 30 * sb
+    # the padding-stress parameter list (97 parameters, 21,444,378 elements, FSDP1
+    # with use_orig_params, N = 8): alignment and world pads, short segments
+    st = [(n,) for n in synth.padding_stress_numels()]
+    pst = fs.fs_plan(st, "bf16", N, True, "fsdp1", 1).upload()
+    prm = [synth.normal_bf16(3, synth.STREAM_PARAMS, n[0], 0.02, device="cuda") for n in st]
+    gst = torch.empty(pst.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    ost = [torch.empty_like(t) for t in prm]
+    ms_p = _timed_graph(lambda: fs.fs_pack(pst, prm, gst), 4 * reps)
+    ms_u = _timed_graph(lambda: fs.fs_unpack(pst, gst, ost), 4 * reps)
+    bp, bu = 2 * pst.total_numel + 2 * pst.gathered_numel, 4 * pst.total_numel
+    out["padding_stress_fsdp1"] = {
+        "params": len(st), "numel": pst.total_numel, "gathered_numel": pst.gathered_numel,
+        "pack": {"us": round(ms_p * 1e3, 1), "GBps": round(bp / (ms_p * 1e-3) / 1e9, 1)},
+        "unpack": {"us": round(ms_u * 1e3, 1), "GBps": round(bu / (ms_u * 1e-3) / 1e9, 1)}}
+    del prm, gst, ost
     out["block_shard_grad_acc_1"] = {
         "shard_numel": sb,
         "reduce": {"us": round(ms_r * 1e3, 1), "GB": round(br / 1e9, 3), "GBps": round(br / (ms_r * 1e-3) / 1e9, 1)},
