@@ -251,15 +251,17 @@ class Plan:
         self.workspace = ws
         return self
 
-    def ptr_table(self, tensors: Sequence[torch.Tensor], what: str) -> torch.Tensor:
-        """Device array of the tensors' data pointers (cached per pointer set)."""
+    def ptr_table(self, tensors: Sequence[torch.Tensor], what: str, elem_bytes: Optional[int] = None) -> torch.Tensor:
+        """Device array of the tensors' data pointers (cached per pointer set).
+        Every tensor must hold its parameter's element count, with elements of
+        `elem_bytes` bytes (default: the plan's)."""
         if len(tensors) != self.info.n_params:
             raise ValueError(f"{what}: expected {self.info.n_params} tensors, got {len(tensors)}")
-        esz = self.info.elem_bytes
+        esz = self.info.elem_bytes if elem_bytes is None else elem_bytes
         ptrs = []
         for i, t in enumerate(tensors):
             if t.element_size() != esz:
-                raise ValueError(f"{what}[{i}]: element size {t.element_size()} != plan's {esz}")
+                raise ValueError(f"{what}[{i}]: element size {t.element_size()} != {esz}")
             if t.numel() != self.numels[i]:
                 raise ValueError(f"{what}[{i}]: numel {t.numel()} != {self.numels[i]}")
             ptrs.append(_dev_ptr(t, f"{what}[{i}]") if t.numel() else 0)
@@ -352,18 +354,7 @@ def fs_pack_cast(plan: Plan, params: Sequence[torch.Tensor], out: torch.Tensor, 
     dt = params[0].dtype
     if any(p.dtype != dt for p in params):
         raise ValueError("fs_pack_cast: parameters must share one dtype")
-    ptrs = []
-    for i, t in enumerate(params):
-        if t.numel() != plan.numels[i]:
-            raise ValueError(f"params[{i}]: numel {t.numel()} != {plan.numels[i]}")
-        ptrs.append(_dev_ptr(t, f"params[{i}]") if t.numel() else 0)
-    key = ("cast", tuple(ptrs))
-    tab = plan._ptr_cache.get(key)
-    if tab is None:
-        tab = torch.tensor(ptrs, dtype=torch.int64, device=params[0].device)
-        if len(plan._ptr_cache) >= 8:
-            plan._ptr_cache.pop(next(iter(plan._ptr_cache)))
-        plan._ptr_cache[key] = tab
+    tab = plan.ptr_table(params, "params", elem_bytes=params[0].element_size())
     _check(lib().fs_pack_cast(plan._h, tab.data_ptr(), _dtype_code(dt), _dev_ptr(out, "out") if want else 0,
                               int(rank), _stream(stream)))
 
