@@ -677,6 +677,7 @@ def main():
           "reshard_n_to_half_n": (2 * P, kern["reshard_n_to_half_n"]["GB"] * 1e9 - 2 * P)}
     for k, (r, w) in rw.items():
         c = mix_ceiling(r, w, streams)
+        kern[k]["frac_of_copy_ceiling"] = round(kern[k]["GBps"] / ceiling, 4)
         kern[k]["mix_ceiling_GBps"] = round(c, 1)
         kern[k]["frac_of_mix_ceiling"] = round(kern[k]["GBps"] / c, 4)
     own = own_buffer_ceilings(W)      # last: it overwrites the shard state
