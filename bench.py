@@ -243,6 +243,17 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
                                   "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     del dst, rs, half
     torch.cuda.empty_cache()
+    # the same groups under the FSDP1 FlatParameter layout (use_orig_params):
+    # 16-byte-aligned parameter starts, flat chunked into N equal shards
+    f1 = [fs.fs_plan(g, "bf16", N, True, "fsdp1", A).upload() for g in groups]
+    if all(p.gathered_numel == g.numel() for p, g in zip(f1, W["gathered"])):
+        ms_p = _timed(lambda: [fs.fs_pack(p, ps, g) for p, ps, g in zip(f1, W["params"], W["gathered"])], reps)
+        ms_u = _timed(lambda: [fs.fs_unpack(p, g, o) for p, g, o in zip(f1, W["gathered"], W["outs"])], reps)
+        bp = 2 * W["P"] + 2 * sum(p.gathered_numel for p in f1)
+        bu = 4 * W["P"]
+        out["fsdp1_flat_pack"] = {"ms": round(ms_p, 4), "GB": round(bp / 1e9, 3), "GBps": round(bp / (ms_p * 1e-3) / 1e9, 1)}
+        out["fsdp1_flat_unpack"] = {"ms": round(ms_u, 4), "GB": round(bu / 1e9, 3), "GBps": round(bu / (ms_u * 1e-3) / 1e9, 1)}
+    del f1
     if not small:
         return out
     # one transformer block's shard at a time, the granularity at which FSDP
