@@ -198,6 +198,7 @@ REDUCE_CASES = [
     (16384 * 3, 8, 4, 0, 0),     # whole chunks only
     (4097, 8, 4, 1, 0), (4097, 8, 4, 3, 1), (4096, 4, 2, 0, 2),   # misaligned slices / out
     (70001, 8, 4, 1, 0),         # misaligned, large
+    (30011, 5, 7, 0, 0),         # 35 terms: a 32-term pass (long chunks), then 3 terms (short chunks)
     (25_297_920, 8, 1, 0, 0),    # one Llama-7B block shard, 8-buffer average
 ]
 
@@ -332,6 +333,7 @@ FUSED_CASES = [
     (4097, 3, 2, 1, True, True, 2),
     (40000, 8, 5, 0, True, True, 5),      # 40 terms: partial sums pass through grad_out
     (20007, 2, 33, 0, False, True, 2),    # 66 terms
+    (30011, 5, 7, 0, True, True, 3),      # 35 terms: one reduce pass, then a fused pass of 3 terms
     (25_297_920, 8, 1, 0, True, False, 1000),
 ]
 
@@ -391,6 +393,8 @@ RS_CASES = [
     (20007, 2, 33, 0, 0),     # 66 terms: passes of 16 micro-steps
     (4097, 8, 4, 1, 0), (9000, 3, 3, 3, 1),
     (100003, 32, 1, 0, 0),    # N = 32
+    (30011, 5, 7, 0, 0),      # 35 terms: a pass of 6 micro-steps (30 terms), then one of 1 (5 terms)
+    (12345, 17, 3, 0, 0),     # one micro-step (17 terms) per pass
     (25_297_920, 8, 4, 0, 0),
 ]
 
