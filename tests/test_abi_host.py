@@ -361,7 +361,7 @@ _shape = st.one_of(st.tuples(), st.tuples(_dims), st.tuples(_dims, st.integers(1
                    st.tuples(_dims, st.integers(1, 5), st.integers(1, 3)))
 
 
-@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=300, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
 @given(shapes=st.lists(_shape, min_size=0, max_size=12), N=st.integers(1, 64),
        eb=st.sampled_from([2, 4]), uo=st.booleans(), mode=st.sampled_from(["fsdp1", "fsdp2"]))
 def test_planner_matches_oracle_randomized(shapes, N, eb, uo, mode):
