@@ -245,8 +245,8 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
     torch.cuda.empty_cache()
     # the same groups under the FSDP1 FlatParameter layout (use_orig_params):
     # 16-byte-aligned parameter starts, flat chunked into N equal shards
-    f1 = [fs.fs_plan(g, "bf16", N, True, "fsdp1", A).upload() for g in groups]
-    if all(p.gathered_numel == g.numel() for p, g in zip(f1, W["gathered"])):
+    f1 = [fs.fs_plan(g, "bf16", N, True, "fsdp1", A).upload() for g in groups] if small else []
+    if f1 and all(p.gathered_numel == g.numel() for p, g in zip(f1, W["gathered"])):
         ms_p = _timed(lambda: [fs.fs_pack(p, ps, g) for p, ps, g in zip(f1, W["params"], W["gathered"])], reps)
         ms_u = _timed(lambda: [fs.fs_unpack(p, g, o) for p, g, o in zip(f1, W["gathered"], W["outs"])], reps)
         bp = 2 * W["P"] + 2 * sum(p.gathered_numel for p in f1)
@@ -613,8 +613,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-small", action="store_true",
-                    help="skip the tiny launch-bound step and the one-block measurement (their small "
-                         "launches would mix into a per-kernel profile of the 7B step)")
+                    help="skip the tiny launch-bound step, the one-block, padding-stress and FSDP1 "
+                         "measurements (their launches would mix into a per-kernel profile of the 7B step)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this engine runs all N logical ranks on one GPU; "
