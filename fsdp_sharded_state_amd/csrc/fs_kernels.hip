@@ -766,12 +766,13 @@ __device__ __forceinline__ u32x4 u4(const float o[4]) {
 // Main AdamW kernel (all buffers 16-byte aligned): a wave owns 64*4*kAdamGroups
 // consecutive elements; lane l holds groups of 4 at offsets q*256 + 4l, so
 // every load and store instruction of the wave covers 1 KB (fp32) or 512 B
-// (bf16) contiguous -- no instruction leaves holes in a cache line.
+// (bf16) contiguous -- no instruction leaves holes in a cache line.  Eight
+// groups per lane (32 elements) measured 0.5-1% faster than four.
 #ifndef FS_ADAM_GROUPS
-#define FS_ADAM_GROUPS 4
+#define FS_ADAM_GROUPS 8
 #endif
 constexpr int kAdamGroups = FS_ADAM_GROUPS;
-constexpr int64_t kAdamChunk = (int64_t)kThreads * 4 * kAdamGroups;   // 4096 elements per workgroup
+constexpr int64_t kAdamChunk = (int64_t)kThreads * 4 * kAdamGroups;   // 8192 elements per workgroup
 
 template <bool GRAD_BF16, bool HAS_P16>
 __global__ __launch_bounds__(kThreads) void adamw_wave_kernel(float *__restrict__ th, float *__restrict__ m,
