@@ -475,10 +475,12 @@ __device__ __forceinline__ u32x4 ld_slice16(const uint16_t *p, int64_t off) {
     return funnel16(lo, hi, sh);
 }
 
-template <bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nterms, int first_pass,
-                                                          int last_pass, float world,
-                                                          int64_t n, float *__restrict__ out) {
+// Misaligned slices or output: lane i owns 8 consecutive elements, one
+// funnel-shifted 16-byte load per term, element stores; the last n % 8
+// elements go one per lane of the first wave.
+__global__ __launch_bounds__(kThreads) void reduce_general_kernel(SliceArgs sa, int nterms, int first_pass,
+                                                                  int last_pass, float world, int64_t n,
+                                                                  float *__restrict__ out) {
     const int64_t nvec = n >> 3;
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i < nvec) {
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nter
         float acc[8];
         int t = 0;
         if (first_pass) {
-            set_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[0], off));
+            set_bf16x8(acc, ld_slice16<false>(sa.p[0], off));
             t = 1;
         } else {
 #pragma unroll
@@ -495,28 +497,18 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nter
         for (; t + 8 <= nterms; t += 8) {
             u32x4 v[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = ld_slice16<ALIGNED>(sa.p[t + k], off);
+            for (int k = 0; k < 8; ++k) v[k] = ld_slice16<false>(sa.p[t + k], off);
 #pragma unroll
             for (int k = 0; k < 8; ++k) add_bf16x8(acc, v[k]);
         }
-        for (; t < nterms; ++t) add_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[t], off));
+        for (; t < nterms; ++t) add_bf16x8(acc, ld_slice16<false>(sa.p[t], off));
         if (last_pass) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = acc[e] / world;
         }
-        if (ALIGNED) {
-            st16(reinterpret_cast<char *>(out + 8 * i),
-                 u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                       __float_as_uint(acc[3])});
-            st16(reinterpret_cast<char *>(out + 8 * i + 4),
-                 u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
-                       __float_as_uint(acc[7])});
-        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) out[8 * i + e] = acc[e];
-        }
+        for (int e = 0; e < 8; ++e) out[8 * i + e] = acc[e];
     }
-    // ragged tail: the last n % 8 elements, one per lane of the first wave
     const int64_t tail = n - nvec * 8;
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < tail) {
         const int64_t e = nvec * 8 + threadIdx.x;
@@ -536,8 +528,19 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(SliceArgs sa, int nter
 constexpr int kRedGroupsMany = 16;                                      // passes of > kRedFewTerms terms
 constexpr int kRedGroupsFew = 4;                                        // passes of <= kRedFewTerms terms
 constexpr int kRedFewTerms = 16;
-constexpr int64_t kRedChunk = (int64_t)kThreads * 4 * kRedGroupsMany;  // 16384 elements
-constexpr int64_t kRedChunkFew = (int64_t)kThreads * 4 * kRedGroupsFew; // 4096 elements
+constexpr int64_t kWgRow = (int64_t)kThreads * 4;                       // elements of one group index across a workgroup
+constexpr int64_t kRedChunk = kWgRow * kRedGroupsMany;                  // 16384 elements
+constexpr int64_t kRedChunkFew = kWgRow * kRedGroupsFew;                // 4096 elements
+
+__device__ __forceinline__ void f4(u32x4 v, float o[4]) {
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ u32x4 u4(const float o[4]) {
+    return u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+}
 
 __device__ __forceinline__ void add_bf16x4(float *acc, u32x2 v) {
     acc[0] = acc[0] + __uint_as_float(v.x << 16);
@@ -545,63 +548,138 @@ __device__ __forceinline__ void add_bf16x4(float *acc, u32x2 v) {
     acc[2] = acc[2] + __uint_as_float(v.y << 16);
     acc[3] = acc[3] + __uint_as_float(v.y & 0xFFFF0000u);
 }
-
-template <int G>
-__device__ __forceinline__ void load_groups_n(u32x2 (&x)[G], const uint16_t *p, int64_t base) {
-#pragma unroll
-    for (int u = 0; u < G; ++u)
-        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kThreads * 4));
+__device__ __forceinline__ void set_bf16x4(float *acc, u32x2 v) {
+    acc[0] = __uint_as_float(v.x << 16);
+    acc[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    acc[2] = __uint_as_float(v.y << 16);
+    acc[3] = __uint_as_float(v.y & 0xFFFF0000u);
 }
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
-                                                                int last_pass, float world,
-                                                                float *__restrict__ out) {
-    const int64_t base = (int64_t)blockIdx.x * ((int64_t)kThreads * 4 * G) + 4 * threadIdx.x;
+// Chunked kernels: a workgroup owns kWgRow*G consecutive elements and lane i
+// the groups of 4 starting at base + u*kWgRow (base = chunk start + 4i), so
+// every wave-wide access of one group index is contiguous.  A launch covers n
+// with ceil(n / chunk) workgroups.  The last one, when its chunk runs past n,
+// walks it in sub-chunks of kTailGroups groups with bounds (TAIL): a group is
+// live when its first element lies below n, and full when all four do.  A
+// live group's aligned 8- or 16-byte block still holds its first element, so
+// the block lies inside a page of the buffer and is read whole; only the
+// elements below n are stored.  The tail code is instantiated at the small
+// group count, so it never needs more registers than the main path.
+constexpr int kTailGroups = 4;
+
+template <int G, bool TAIL>
+struct Bounds {
+    int nlive = G, nfull = G;   // groups of the lane with e < n, with e + 4 <= n
+    int64_t n = 0;
+    __device__ __forceinline__ Bounds(int64_t base, int64_t n_) : n(n_) {
+        if (TAIL) {
+            const int64_t rem = n_ - base;
+            nlive = rem <= 0 ? 0 : (int)imin(G, (rem + kWgRow - 1) / kWgRow);
+            nfull = rem < 4 ? 0 : (int)imin(G, (rem - 4) / kWgRow + 1);
+        }
+    }
+    __device__ __forceinline__ bool live(int u) const { return !TAIL || u < nlive; }
+    __device__ __forceinline__ bool full(int u) const { return !TAIL || u < nfull; }
+};
+
+template <int G, bool TAIL>
+__device__ __forceinline__ void load_groups(u32x2 (&x)[G], const uint16_t *p, int64_t base, const Bounds<G, TAIL> &B) {
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+        x[u] = B.live(u) ? __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p + base + u * kWgRow))
+                         : u32x2{0u, 0u};
+}
+
+template <int G, int GB, bool TAIL>
+__device__ __forceinline__ void load_f32_groups(float *o, const float *p, int64_t base, const Bounds<GB, TAIL> &B,
+                                                int u0 = 0) {
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+        f4(B.live(u0 + u) ? ld16(reinterpret_cast<const char *>(p + base + (u0 + u) * kWgRow)) : u32x4{0u, 0u, 0u, 0u},
+           o + 4 * u);
+}
+
+// Store group u's four values (those below n, in a straddling group).
+template <int G, bool TAIL>
+__device__ __forceinline__ void store_f32_group(float *p, int64_t base, int u, const float *v, const Bounds<G, TAIL> &B) {
+    const int64_t e = base + u * kWgRow;
+    if (B.full(u)) {
+        st16(reinterpret_cast<char *>(p + e), u4(v));
+    } else if (B.live(u)) {
+        for (int k = 0; k < 4; ++k)
+            if (e + k < B.n) p[e + k] = v[k];
+    }
+}
+
+// Sum the lane's G groups over slices 0..nterms-1 in slice order, into acc
+// (init: acc starts as slice 0 itself, so -0 survives; else slice 0 is added
+// to acc).  SL slices are in flight: slot k % SL holds slice k, refilled with
+// slice k + SL once added.  Reading one slice at a time per workgroup keeps
+// each HBM stream in long contiguous runs.
+template <int G, int SL, bool TAIL>
+__device__ __forceinline__ void sum_slices(const SliceArgs &sa, int nterms, bool init, float *acc, int64_t base,
+                                           const Bounds<G, TAIL> &B) {
+    u32x2 x[SL][G];
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+        if (s < nterms) load_groups<G, TAIL>(x[s], sa.p[s], base, B);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        if (init) set_bf16x4(acc + 4 * u, x[0][u]);
+        else add_bf16x4(acc + 4 * u, x[0][u]);
+    }
+    if (SL < nterms) load_groups<G, TAIL>(x[0], sa.p[SL], base, B);
+    for (int r = 0;; ++r) {
+#pragma unroll
+        for (int k = 1; k <= SL; ++k) {
+            const int t = r * SL + k;
+            if (t >= nterms) return;
+#pragma unroll
+            for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, x[k % SL][u]);
+            if (t + SL < nterms) load_groups<G, TAIL>(x[k % SL], sa.p[t + SL], base, B);
+        }
+    }
+}
+
+template <int G, bool TAIL>
+__device__ __forceinline__ void reduce_chunk(const SliceArgs &sa, int nterms, int first_pass, int last_pass,
+                                             float world, float *__restrict__ out, int64_t base, int64_t n) {
+    const Bounds<G, TAIL> B(base, n);
     float acc[4 * G];
-    u32x2 xa[G], xb[G];
-    int t = 0;
-    if (first_pass) {
-        load_groups_n<G>(xa, sa.p[0], base);
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            acc[4 * u] = __uint_as_float(xa[u].x << 16);
-            acc[4 * u + 1] = __uint_as_float(xa[u].x & 0xFFFF0000u);
-            acc[4 * u + 2] = __uint_as_float(xa[u].y << 16);
-            acc[4 * u + 3] = __uint_as_float(xa[u].y & 0xFFFF0000u);
-        }
-        t = 1;
-    } else {
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(out + base + u * kThreads * 4));
-            acc[4 * u] = __uint_as_float(o.x);
-            acc[4 * u + 1] = __uint_as_float(o.y);
-            acc[4 * u + 2] = __uint_as_float(o.z);
-            acc[4 * u + 3] = __uint_as_float(o.w);
-        }
-    }
-    // two-slot pipeline: slice t is added while slice t+1 is loading
-    if (t < nterms) load_groups_n<G>(xa, sa.p[t], base);
-    while (t < nterms) {
-        if (t + 1 < nterms) load_groups_n<G>(xb, sa.p[t + 1], base);
-#pragma unroll
-        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xa[u]);
-        if (++t >= nterms) break;
-        if (t + 1 < nterms) load_groups_n<G>(xa, sa.p[t + 1], base);
-#pragma unroll
-        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xb[u]);
-        ++t;
-    }
+    if (!first_pass) load_f32_groups<G, G, TAIL>(acc, out, base, B);   // partial sums of the earlier passes
+    sum_slices<G, 2, TAIL>(sa, nterms, first_pass, acc, base, B);
     if (last_pass) {
 #pragma unroll
         for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
     }
 #pragma unroll
-    for (int u = 0; u < G; ++u)
-        st16(reinterpret_cast<char *>(out + base + u * kThreads * 4),
-             u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
-                   __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])});
+    for (int u = 0; u < G; ++u) store_f32_group<G, TAIL>(out, base, u, acc + 4 * u, B);
+}
+
+// The chunk of workgroup blockIdx.x: whole, or the last one cut by n (walked
+// in sub-chunks of kTailGroups groups).  `body(groups_tag, base, tail)` runs
+// one (sub-)chunk.
+#define FS_CHUNK_DISPATCH(G, FULL_CALL, TAIL_CALL)                                               \
+    do {                                                                                        \
+        const int64_t chunk_lo = (int64_t)blockIdx.x * (kWgRow * (G));                         \
+        if (chunk_lo + kWgRow * (G) <= n) {                                                     \
+            const int64_t base = chunk_lo + 4 * threadIdx.x;                                    \
+            FULL_CALL;                                                                          \
+        } else {                                                                                \
+            for (int64_t sub = chunk_lo; sub < n; sub += kWgRow * kTailGroups) {                \
+                const int64_t base = sub + 4 * threadIdx.x;                                     \
+                TAIL_CALL;                                                                      \
+            }                                                                                   \
+        }                                                                                       \
+    } while (0)
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void reduce_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
+                                                                int last_pass, float world,
+                                                                float *__restrict__ out, int64_t n) {
+    static_assert(G % kTailGroups == 0, "the tail walks whole sub-chunks");
+    FS_CHUNK_DISPATCH(G, (reduce_chunk<G, false>(sa, nterms, first_pass, last_pass, world, out, base, n)),
+                      (reduce_chunk<kTailGroups, true>(sa, nterms, first_pass, last_pass, world, out, base, n)));
 }
 
 // ------------------------------------------------- bf16 reduce dtype --
@@ -622,23 +700,13 @@ __device__ __forceinline__ float bf16_round_f32(float f) {
     return __uint_as_float((uint32_t)bf16_rne_bits(__float_as_uint(f)) << 16);
 }
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void reduce_rs_chunk_kernel(SliceArgs sa, int nsteps, int world,
-                                                                   int first_pass, float worldf,
-                                                                   float *__restrict__ out) {
-    const int64_t base = (int64_t)blockIdx.x * ((int64_t)kThreads * 4 * G) + 4 * threadIdx.x;
+template <int G, bool TAIL>
+__device__ __forceinline__ void reduce_rs_chunk(const SliceArgs &sa, int nsteps, int world, int first_pass,
+                                                float worldf, float *__restrict__ out, int64_t base, int64_t n) {
+    const Bounds<G, TAIL> B(base, n);
     float acc[4 * G], sum[4 * G];
     u32x2 xa[G], xb[G];
-    if (!first_pass) {
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(out + base + u * kThreads * 4));
-            acc[4 * u] = __uint_as_float(o.x);
-            acc[4 * u + 1] = __uint_as_float(o.y);
-            acc[4 * u + 2] = __uint_as_float(o.z);
-            acc[4 * u + 3] = __uint_as_float(o.w);
-        }
-    }
+    if (!first_pass) load_f32_groups<G, G, TAIL>(acc, out, base, B);
     const int total = nsteps * world;
     // add term t (held in x) into the micro-step sum; fold the finished micro-step into acc
     auto consume = [&](const u32x2 (&x)[G], int t) {
@@ -659,24 +727,29 @@ __global__ __launch_bounds__(kThreads) void reduce_rs_chunk_kernel(SliceArgs sa,
         }
     };
     int t = 0;
-    if (t < total) load_groups_n<G>(xa, sa.p[t], base);
+    if (t < total) load_groups<G, TAIL>(xa, sa.p[t], base, B);
     while (t < total) {
-        if (t + 1 < total) load_groups_n<G>(xb, sa.p[t + 1], base);
+        if (t + 1 < total) load_groups<G, TAIL>(xb, sa.p[t + 1], base, B);
         consume(xa, t);
         if (++t >= total) break;
-        if (t + 1 < total) load_groups_n<G>(xa, sa.p[t + 1], base);
+        if (t + 1 < total) load_groups<G, TAIL>(xa, sa.p[t + 1], base, B);
         consume(xb, t);
         ++t;
     }
 #pragma unroll
-    for (int u = 0; u < G; ++u)
-        st16(reinterpret_cast<char *>(out + base + u * kThreads * 4),
-             u32x4{__float_as_uint(acc[4 * u]), __float_as_uint(acc[4 * u + 1]),
-                   __float_as_uint(acc[4 * u + 2]), __float_as_uint(acc[4 * u + 3])});
+    for (int u = 0; u < G; ++u) store_f32_group<G, TAIL>(out, base, u, acc + 4 * u, B);
 }
 
-// Remainder / misaligned variant: 8 elements per lane, element tail.
-template <bool ALIGNED>
+template <int G>
+__global__ __launch_bounds__(kThreads) void reduce_rs_chunk_kernel(SliceArgs sa, int nsteps, int world,
+                                                                   int first_pass, float worldf,
+                                                                   float *__restrict__ out, int64_t n) {
+    static_assert(G % kTailGroups == 0, "the tail walks whole sub-chunks");
+    FS_CHUNK_DISPATCH(G, (reduce_rs_chunk<G, false>(sa, nsteps, world, first_pass, worldf, out, base, n)),
+                      (reduce_rs_chunk<kTailGroups, true>(sa, nsteps, world, first_pass, worldf, out, base, n)));
+}
+
+// Misaligned variant: 8 elements per lane, element tail.
 __global__ __launch_bounds__(kThreads) void reduce_rs_general_kernel(SliceArgs sa, int nsteps, int world,
                                                                      int first_pass, float worldf, int64_t n,
                                                                      float *__restrict__ out) {
@@ -690,23 +763,16 @@ __global__ __launch_bounds__(kThreads) void reduce_rs_general_kernel(SliceArgs s
             for (int e = 0; e < 8; ++e) acc[e] = out[8 * i + e];
         }
         for (int j = 0; j < nsteps; ++j) {
-            set_bf16x8(sum, ld_slice16<ALIGNED>(sa.p[j * world], off));
-            for (int k = 1; k < world; ++k) add_bf16x8(sum, ld_slice16<ALIGNED>(sa.p[j * world + k], off));
+            set_bf16x8(sum, ld_slice16<false>(sa.p[j * world], off));
+            for (int k = 1; k < world; ++k) add_bf16x8(sum, ld_slice16<false>(sa.p[j * world + k], off));
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float d = bf16_round_f32(sum[e] / worldf);
                 acc[e] = (first_pass && j == 0) ? d : acc[e] + d;
             }
         }
-        if (ALIGNED) {
-            st16(reinterpret_cast<char *>(out + 8 * i),
-                 u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])});
-            st16(reinterpret_cast<char *>(out + 8 * i + 4),
-                 u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]), __float_as_uint(acc[7])});
-        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) out[8 * i + e] = acc[e];
-        }
+        for (int e = 0; e < 8; ++e) out[8 * i + e] = acc[e];
     }
     const int64_t tail = n - nvec * 8;
     if (blockIdx.x == 0 && (int64_t)threadIdx.x < tail) {
@@ -733,12 +799,7 @@ struct AdamConsts {
     double b1, b2, omb1, omb2, bc1, bc2, lr, eps, decay;
 };
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return bf16_rne_bits(__float_as_uint(f)); }
 
 __device__ __forceinline__ void adam_elem(const AdamConsts &c, float g32, float &th32, float &m32,
                                           float &v32) {
@@ -753,81 +814,68 @@ __device__ __forceinline__ void adam_elem(const AdamConsts &c, float g32, float 
     v32 = (float)v_new;
 }
 
-__device__ __forceinline__ void f4(u32x4 v, float o[4]) {
-    o[0] = __uint_as_float(v.x);
-    o[1] = __uint_as_float(v.y);
-    o[2] = __uint_as_float(v.z);
-    o[3] = __uint_as_float(v.w);
-}
-__device__ __forceinline__ u32x4 u4(const float o[4]) {
-    return u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+template <int G, bool TAIL>
+__device__ __forceinline__ void store_bf16_group(uint16_t *p, int64_t base, int u, const float *v,
+                                                 const Bounds<G, TAIL> &B) {
+    const int64_t e = base + u * kWgRow;
+    if (B.full(u)) {
+        const u32x2 w = {(uint32_t)bf16_rne(v[0]) | ((uint32_t)bf16_rne(v[1]) << 16),
+                         (uint32_t)bf16_rne(v[2]) | ((uint32_t)bf16_rne(v[3]) << 16)};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p + e));
+    } else if (B.live(u)) {
+        for (int k = 0; k < 4; ++k)
+            if (e + k < B.n) p[e + k] = bf16_rne(v[k]);
+    }
 }
 
-// Main AdamW kernel (all buffers 16-byte aligned): a wave owns 64*4*kAdamGroups
-// consecutive elements; lane l holds groups of 4 at offsets q*256 + 4l, so
-// every load and store instruction of the wave covers 1 KB (fp32) or 512 B
-// (bf16) contiguous -- no instruction leaves holes in a cache line.  Eight
-// groups per lane (32 elements) measured 0.5-1% faster than four.
-#ifndef FS_ADAM_GROUPS
-#define FS_ADAM_GROUPS 8
-#endif
-constexpr int kAdamGroups = FS_ADAM_GROUPS;
-constexpr int64_t kAdamChunk = (int64_t)kThreads * 4 * kAdamGroups;   // 8192 elements per workgroup
+// Main AdamW kernel (all buffers 16-byte aligned): one group of 4 elements per
+// lane, 1024 elements per workgroup, so each wave's load or store of an array
+// covers 1 KB (fp32) or 512 B (bf16) contiguous.  At about 50 registers the
+// kernel runs 8 waves per SIMD; small workgroups keep the last round of a
+// launch short (one Llama-7B block's shard, 25.3M elements: 117 us against
+// 143 us for 8192-element workgroups with a separate remainder launch) and
+// measured equal on the 842M-element shard.
+template <bool GRAD_BF16, bool HAS_P16, bool TAIL>
+__device__ __forceinline__ void adamw_group(float *__restrict__ th, float *__restrict__ m, float *__restrict__ v,
+                                            const void *__restrict__ grad, uint16_t *__restrict__ p16,
+                                            const AdamConsts &c, int64_t e, int64_t n) {
+    const Bounds<1, TAIL> B(e, n);
+    if (!B.live(0)) return;
+    float G[4], T[4], M[4], V[4];
+    if (GRAD_BF16) {
+        const u32x2 gb = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(
+            reinterpret_cast<const uint16_t *>(grad) + e));
+        set_bf16x4(G, gb);
+    } else {
+        f4(ld16(reinterpret_cast<const char *>(reinterpret_cast<const float *>(grad) + e)), G);
+    }
+    f4(ld16(reinterpret_cast<const char *>(th + e)), T);
+    f4(ld16(reinterpret_cast<const char *>(m + e)), M);
+    f4(ld16(reinterpret_cast<const char *>(v + e)), V);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) adam_elem(c, G[k], T[k], M[k], V[k]);
+    store_f32_group<1, TAIL>(th, e, 0, T, B);
+    store_f32_group<1, TAIL>(m, e, 0, M, B);
+    store_f32_group<1, TAIL>(v, e, 0, V, B);
+    if (HAS_P16) store_bf16_group<1, TAIL>(p16, e, 0, T, B);
+}
 
 template <bool GRAD_BF16, bool HAS_P16>
-__global__ __launch_bounds__(kThreads) void adamw_wave_kernel(float *__restrict__ th, float *__restrict__ m,
-                                                              float *__restrict__ v,
-                                                              const void *__restrict__ grad,
-                                                              uint16_t *__restrict__ p16, AdamConsts c) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t base = (int64_t)blockIdx.x * kAdamChunk + (int64_t)wave * 256 * kAdamGroups + 4 * lane;
-    float G[4 * kAdamGroups], T[4 * kAdamGroups], M[4 * kAdamGroups], V[4 * kAdamGroups];
-    // loads and stores are issued array by array (all of g, then theta, m,
-    // v), so each wave's 4 KB of one array go out back to back
-#pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) {
-        const int64_t e = base + q * 256;
-        if (GRAD_BF16) {
-            const u32x2 gb = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(
-                reinterpret_cast<const uint16_t *>(grad) + e));
-            G[4 * q] = __uint_as_float(gb.x << 16);
-            G[4 * q + 1] = __uint_as_float(gb.x & 0xFFFF0000u);
-            G[4 * q + 2] = __uint_as_float(gb.y << 16);
-            G[4 * q + 3] = __uint_as_float(gb.y & 0xFFFF0000u);
-        } else {
-            f4(ld16(reinterpret_cast<const char *>(reinterpret_cast<const float *>(grad) + e)), G + 4 * q);
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) f4(ld16(reinterpret_cast<const char *>(th + base + q * 256)), T + 4 * q);
-#pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) f4(ld16(reinterpret_cast<const char *>(m + base + q * 256)), M + 4 * q);
-#pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) f4(ld16(reinterpret_cast<const char *>(v + base + q * 256)), V + 4 * q);
-#pragma unroll
-    for (int k = 0; k < 4 * kAdamGroups; ++k) adam_elem(c, G[k], T[k], M[k], V[k]);
-#pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) st16(reinterpret_cast<char *>(th + base + q * 256), u4(T + 4 * q));
-#pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) st16(reinterpret_cast<char *>(m + base + q * 256), u4(M + 4 * q));
-#pragma unroll
-    for (int q = 0; q < kAdamGroups; ++q) st16(reinterpret_cast<char *>(v + base + q * 256), u4(V + 4 * q));
-    if (HAS_P16) {
-#pragma unroll
-        for (int q = 0; q < kAdamGroups; ++q) {
-            const u32x2 w = {(uint32_t)bf16_rne(T[4 * q]) | ((uint32_t)bf16_rne(T[4 * q + 1]) << 16),
-                             (uint32_t)bf16_rne(T[4 * q + 2]) | ((uint32_t)bf16_rne(T[4 * q + 3]) << 16)};
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p16 + base + q * 256));
-        }
-    }
+__global__ __launch_bounds__(kThreads) void adamw_kernel(float *__restrict__ th, float *__restrict__ m,
+                                                         float *__restrict__ v, const void *__restrict__ grad,
+                                                         uint16_t *__restrict__ p16, AdamConsts c, int64_t n) {
+    const int64_t e = (int64_t)blockIdx.x * kWgRow + 4 * threadIdx.x;
+    if ((int64_t)(blockIdx.x + 1) * kWgRow <= n)
+        adamw_group<GRAD_BF16, HAS_P16, false>(th, m, v, grad, p16, c, e, n);
+    else
+        adamw_group<GRAD_BF16, HAS_P16, true>(th, m, v, grad, p16, c, e, n);
 }
 
-// Element-wise variant for misaligned buffers and the ragged tail.
-__global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t begin, int64_t n, float *th,
-                                                                float *m, float *v,
+// Element-wise variant for misaligned buffers.
+__global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t n, float *th, float *m, float *v,
                                                                 const void *grad, int grad_bf16,
                                                                 uint16_t *p16, AdamConsts c) {
-    const int64_t e = begin + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (e >= n) return;
     const float g = grad_bf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(grad)[e] << 16)
                               : reinterpret_cast<const float *>(grad)[e];
@@ -848,78 +896,42 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t begin, i
 // two-kernel path, while the gradient shard is never written and re-read
 // (unless the caller asks for it).  Traffic per element: 2*A*N + 26 bytes
 // instead of 2*A*N + 4 + 30.
-
-// G groups of 4 elements per lane: 16 (16384-element chunks) for a final
-// pass of more than kRedFewTerms terms, 4 for fewer (2-3% faster at 8
-// terms, as for the plain reduce).  AdamW runs in batches of kFusedBatch
-// groups.  With 16 groups and batches of 8 the kernel holds one wave per
-// SIMD (all 512 registers of a lane in use, none spilled to memory); that
-// measured 1-2% faster than 8 groups in batches of 4 at two waves per SIMD.
+//
+// A workgroup sums its chunk over the slices (the reduce's loop), then loads
+// theta, m, v after the slice loop -- not before it, where they would hold
+// registers through the whole loop -- and updates them in batches of KB
+// groups, the next batch's loads in flight during the current batch's
+// arithmetic, storing array by array (all of theta, then m, v, the bf16 copy).
+// With 16 groups per lane (the chunk of passes of more than kRedFewTerms
+// terms) that measured 5% faster than loading the first batch before the
+// slice loop and storing group by group.  The kernel is bound by HBM's mixed
+// read/write rate, not by its double-precision arithmetic: a cheaper update
+// formula and variants at two to four waves per SIMD measured no faster.
 constexpr int kFusedGroupsMany = 16;
 constexpr int kFusedGroupsFew = 4;
 constexpr int kFusedBatch = 8;
 
-
-template <int G, bool HAS_P16, bool HAS_G>
-__global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
-                                                                      float world, float *__restrict__ th,
-                                                                      float *__restrict__ m,
-                                                                      float *__restrict__ v,
-                                                                      uint16_t *__restrict__ p16,
-                                                                      float *__restrict__ gout, AdamConsts c) {
-    const int64_t base = (int64_t)blockIdx.x * ((int64_t)kThreads * 4 * G) + 4 * threadIdx.x;
+template <int G, bool HAS_P16, bool HAS_G, bool TAIL>
+__device__ __forceinline__ void reduce_adamw_chunk(const SliceArgs &sa, int nterms, int first_pass, float world,
+                                                   float *__restrict__ th, float *__restrict__ m,
+                                                   float *__restrict__ v, uint16_t *__restrict__ p16,
+                                                   float *__restrict__ gout, const AdamConsts &c, int64_t base,
+                                                   int64_t n) {
     constexpr int KB = kFusedBatch < G ? kFusedBatch : G;
-    float acc[4 * G];
-    u32x2 xa[G], xb[G];
-    int t = 0;
-    if (first_pass) {
-        load_groups_n<G>(xa, sa.p[0], base);
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            acc[4 * u] = __uint_as_float(xa[u].x << 16);
-            acc[4 * u + 1] = __uint_as_float(xa[u].x & 0xFFFF0000u);
-            acc[4 * u + 2] = __uint_as_float(xa[u].y << 16);
-            acc[4 * u + 3] = __uint_as_float(xa[u].y & 0xFFFF0000u);
-        }
-        t = 1;
-    } else {   // partial sums of the earlier terms, left in gout by the reduce passes
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-            const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(gout + base + u * kThreads * 4));
-            acc[4 * u] = __uint_as_float(o.x);
-            acc[4 * u + 1] = __uint_as_float(o.y);
-            acc[4 * u + 2] = __uint_as_float(o.z);
-            acc[4 * u + 3] = __uint_as_float(o.w);
-        }
-    }
     constexpr int NB = G / KB;
-    float T[2][4 * KB], M[2][4 * KB], V[2][4 * KB];
-    auto load_state = [&](int slot, int u0) {
-#pragma unroll
-        for (int q = 0; q < KB; ++q) {
-            const int64_t e = base + (u0 + q) * kThreads * 4;
-            f4(ld16(reinterpret_cast<const char *>(th + e)), T[slot] + 4 * q);
-            f4(ld16(reinterpret_cast<const char *>(m + e)), M[slot] + 4 * q);
-            f4(ld16(reinterpret_cast<const char *>(v + e)), V[slot] + 4 * q);
-        }
-    };
-    load_state(0, 0);   // independent of the reduce: in flight during the slice loop
-    if (t < nterms) load_groups_n<G>(xa, sa.p[t], base);
-    while (t < nterms) {
-        if (t + 1 < nterms) load_groups_n<G>(xb, sa.p[t + 1], base);
-#pragma unroll
-        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xa[u]);
-        if (++t >= nterms) break;
-        if (t + 1 < nterms) load_groups_n<G>(xa, sa.p[t + 1], base);
-#pragma unroll
-        for (int u = 0; u < G; ++u) add_bf16x4(acc + 4 * u, xb[u]);
-        ++t;
-    }
+    const Bounds<G, TAIL> B(base, n);
+    float acc[4 * G];
+    if (!first_pass) load_f32_groups<G, G, TAIL>(acc, gout, base, B);   // partial sums left by the reduce passes
+    sum_slices<G, 2, TAIL>(sa, nterms, first_pass, acc, base, B);
 #pragma unroll
     for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
-    // AdamW on the lane's groups, KB groups (4*KB elements) at a time; batch
-    // b+1's state loads are issued before batch b's update (batch 0's before
-    // the slice loop), so they overlap the arithmetic.
+    float T[2][4 * KB], M[2][4 * KB], V[2][4 * KB];
+    auto load_state = [&](int slot, int u0) {
+        load_f32_groups<KB, G, TAIL>(T[slot], th, base, B, u0);
+        load_f32_groups<KB, G, TAIL>(M[slot], m, base, B, u0);
+        load_f32_groups<KB, G, TAIL>(V[slot], v, base, B, u0);
+    };
+    load_state(0, 0);
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
         const int slot = bi & 1, u0 = bi * KB;
@@ -927,25 +939,41 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
 #pragma unroll
         for (int k = 0; k < 4 * KB; ++k) adam_elem(c, acc[4 * u0 + k], T[slot][k], M[slot][k], V[slot][k]);
 #pragma unroll
-        for (int q = 0; q < KB; ++q) {
-            const int64_t e = base + (u0 + q) * kThreads * 4;
-            st16(reinterpret_cast<char *>(th + e), u4(T[slot] + 4 * q));
-            st16(reinterpret_cast<char *>(m + e), u4(M[slot] + 4 * q));
-            st16(reinterpret_cast<char *>(v + e), u4(V[slot] + 4 * q));
-            if (HAS_P16) {
-                const u32x2 w = {(uint32_t)bf16_rne(T[slot][4 * q]) | ((uint32_t)bf16_rne(T[slot][4 * q + 1]) << 16),
-                                 (uint32_t)bf16_rne(T[slot][4 * q + 2]) | ((uint32_t)bf16_rne(T[slot][4 * q + 3]) << 16)};
-                __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p16 + e));
-            }
-            if (HAS_G) st16(reinterpret_cast<char *>(gout + e), u4(acc + 4 * (u0 + q)));
+        for (int q = 0; q < KB; ++q) store_f32_group<G, TAIL>(th, base, u0 + q, T[slot] + 4 * q, B);
+#pragma unroll
+        for (int q = 0; q < KB; ++q) store_f32_group<G, TAIL>(m, base, u0 + q, M[slot] + 4 * q, B);
+#pragma unroll
+        for (int q = 0; q < KB; ++q) store_f32_group<G, TAIL>(v, base, u0 + q, V[slot] + 4 * q, B);
+        if (HAS_P16) {
+#pragma unroll
+            for (int q = 0; q < KB; ++q) store_bf16_group<G, TAIL>(p16, base, u0 + q, T[slot] + 4 * q, B);
+        }
+        if (HAS_G) {
+#pragma unroll
+            for (int q = 0; q < KB; ++q) store_f32_group<G, TAIL>(gout, base, u0 + q, acc + 4 * (u0 + q), B);
         }
     }
 }
 
-// Remainder / misaligned variant: lane i owns 8 consecutive elements (the
-// general reduce's loads), then updates them element by element; the last
-// n % 8 elements go one per lane of the first wave.
-template <bool ALIGNED>
+template <int G, bool HAS_P16, bool HAS_G>
+__global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
+                                                                      float world, float *__restrict__ th,
+                                                                      float *__restrict__ m,
+                                                                      float *__restrict__ v,
+                                                                      uint16_t *__restrict__ p16,
+                                                                      float *__restrict__ gout, AdamConsts c,
+                                                                      int64_t n) {
+    static_assert(G % kTailGroups == 0, "the tail walks whole sub-chunks");
+    FS_CHUNK_DISPATCH(G,
+                      (reduce_adamw_chunk<G, HAS_P16, HAS_G, false>(sa, nterms, first_pass, world, th, m, v, p16,
+                                                                    gout, c, base, n)),
+                      (reduce_adamw_chunk<kTailGroups, HAS_P16, HAS_G, true>(sa, nterms, first_pass, world, th, m,
+                                                                             v, p16, gout, c, base, n)));
+}
+
+// Misaligned variant: lane i owns 8 consecutive elements (the general
+// reduce's loads), then updates them element by element; the last n % 8
+// elements go one per lane of the first wave.
 __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArgs sa, int nterms, int first_pass,
                                                                         float world, int64_t n, float *th,
                                                                         float *m, float *v, uint16_t *p16,
@@ -957,13 +985,13 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArg
         float acc[8];
         int t = 0;
         if (first_pass) {
-            set_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[0], off));
+            set_bf16x8(acc, ld_slice16<false>(sa.p[0], off));
             t = 1;
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = gout[8 * i + e];
         }
-        for (; t < nterms; ++t) add_bf16x8(acc, ld_slice16<ALIGNED>(sa.p[t], off));
+        for (; t < nterms; ++t) add_bf16x8(acc, ld_slice16<false>(sa.p[t], off));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int64_t k = 8 * i + e;
@@ -1098,21 +1126,53 @@ int check_launch(const char *what) {
 }
 
 template <int G>
-void launch_fused_chunks(int64_t nchunks, hipStream_t stream, const SliceArgs &sa, int cnt, int first, float world,
-                         float *th, float *m, float *v, uint16_t *p16, float *gout, const AdamConsts &c) {
-    const dim3 g((uint32_t)nchunks), b(kThreads);
+void launch_fused(int64_t n, hipStream_t stream, const SliceArgs &sa, int cnt, int first, float world, float *th,
+                  float *m, float *v, uint16_t *p16, float *gout, const AdamConsts &c) {
+    const dim3 g((uint32_t)((n + kWgRow * G - 1) / (kWgRow * G))), b(kThreads);
     if (p16 && gout)
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, true>), g, b, 0, stream, sa, cnt, first, world, th, m,
-                           v, p16, gout, c);
+                           v, p16, gout, c, n);
     else if (p16)
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, false>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, gout, c);
+                           m, v, p16, gout, c, n);
     else if (gout)
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, true>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, gout, c);
+                           m, v, p16, gout, c, n);
     else
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, false>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, gout, c);
+                           m, v, p16, gout, c, n);
+}
+
+// One pass of the fp32 reduce over terms [t0, t0 + cnt): chunked when every
+// pointer is 16-byte aligned (one launch, the last chunk partial), else the
+// general kernel.
+void launch_reduce_pass(int64_t n, hipStream_t stream, const uint16_t *const *slices, int t0, int cnt, int first,
+                        int last, float world, bool aligned, float *out) {
+    SliceArgs sa;
+    memset(&sa, 0, sizeof sa);
+    for (int k = 0; k < cnt; ++k) sa.p[k] = slices[t0 + k];
+    if (aligned) {
+        const bool few = cnt <= kRedFewTerms;
+        const int64_t chunk = few ? kRedChunkFew : kRedChunk;
+        const dim3 g((uint32_t)((n + chunk - 1) / chunk));
+        if (few)
+            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsFew>, g, dim3(kThreads), 0, stream, sa, cnt, first, last,
+                               world, out, n);
+        else
+            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsMany>, g, dim3(kThreads), 0, stream, sa, cnt, first,
+                               last, world, out, n);
+    } else {
+        const int64_t grid = std::max<int64_t>(1, ((n >> 3) + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(reduce_general_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, cnt, first,
+                           last, world, n, out);
+    }
+}
+
+// Largest grid any launch over n elements needs: one workgroup per kWgRow
+// elements (AdamW) bounds every chunked kernel; the general kernels use one
+// lane per 8 elements.
+bool grid_fits(int64_t n) {
+    return (n + kWgRow - 1) / kWgRow <= INT32_MAX && ((n >> 3) + kThreads - 1) / kThreads <= INT32_MAX;
 }
 
 bool ranges_overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
@@ -1319,39 +1379,11 @@ extern "C" int fs_reduce_shard(int64_t n, int32_t world, int32_t grad_acc, const
     bool aligned = false, skip = false;
     if (int rc = check_reduce("fs_reduce_shard", n, world, grad_acc, slices, out, &terms, &aligned, &skip)) return rc;
     if (skip) return FS_OK;
-    // the largest grids any pass can need: the small chunk, or everything element-wise
-    if ((aligned ? n / kRedChunkFew : 0) > INT32_MAX || ((n >> 3) + kThreads - 1) / kThreads > INT32_MAX)
-        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large for one launch");
+    if (!grid_fits(n)) return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard: n too large for one launch");
     (void)hipGetLastError();
     for (int t0 = 0; t0 < terms; t0 += kTermsPerPass) {
         const int cnt = std::min(kTermsPerPass, terms - t0);
-        const int first = t0 == 0, last = t0 + cnt == terms;
-        const bool few = cnt <= kRedFewTerms;
-        const int64_t chunk = few ? kRedChunkFew : kRedChunk;
-        const int64_t nchunks = aligned ? n / chunk : 0;
-        const int64_t done = nchunks * chunk;
-        const int64_t rest = n - done;
-        const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
-        SliceArgs sa;
-        memset(&sa, 0, sizeof sa);
-        for (int k = 0; k < cnt; ++k) sa.p[k] = slices[t0 + k];
-        if (nchunks > 0 && few)
-            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsFew>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
-                               stream, sa, cnt, first, last, (float)world, out);
-        else if (nchunks > 0)
-            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsMany>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
-                               stream, sa, cnt, first, last, (float)world, out);
-        if (rest > 0) {   // the chunk remainder, or everything when misaligned
-            SliceArgs sr;   // advanced by `done`, a multiple of 8 elements: alignment is kept
-            memset(&sr, 0, sizeof sr);
-            for (int k = 0; k < cnt; ++k) sr.p[k] = slices[t0 + k] + done;
-            if (aligned)
-                hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
-                                   cnt, first, last, (float)world, rest, out + done);
-            else
-                hipLaunchKernelGGL(reduce_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
-                                   cnt, first, last, (float)world, rest, out + done);
-        }
+        launch_reduce_pass(n, stream, slices, t0, cnt, t0 == 0, t0 + cnt == terms, (float)world, aligned, out);
         int rc = check_launch("fs_reduce_shard");
         if (rc != FS_OK) return rc;
     }
@@ -1371,39 +1403,28 @@ extern "C" int fs_reduce_shard_ex(int64_t n, int32_t world, int32_t grad_acc, fs
     if (world > kTermsPerPass)
         return fsi::fail(FS_E_UNSUPPORTED, "fs_reduce_shard_ex: bf16 reduce dtype supports world <= %d", kTermsPerPass);
     const int steps_per_pass = kTermsPerPass / world;
-    if ((aligned ? n / ((int64_t)kThreads * 4 * kRsGroupsFew) : 0) > INT32_MAX ||
-        ((n >> 3) + kThreads - 1) / kThreads > INT32_MAX)
-        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard_ex: n too large for one launch");
+    if (!grid_fits(n)) return fsi::fail(FS_E_OVERFLOW, "fs_reduce_shard_ex: n too large for one launch");
     (void)hipGetLastError();
     for (int j0 = 0; j0 < grad_acc; j0 += steps_per_pass) {
         const int steps = std::min(steps_per_pass, grad_acc - j0);
         const int first = j0 == 0;
-        const bool few = steps * world <= kRedFewTerms;
-        const int64_t chunk = (int64_t)kThreads * 4 * (few ? kRsGroupsFew : kRsGroupsMany);
-        const int64_t nchunks = aligned ? n / chunk : 0;
-        const int64_t done = nchunks * chunk;
-        const int64_t rest = n - done;
-        const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
-        SliceArgs sa, sr;
+        SliceArgs sa;
         memset(&sa, 0, sizeof sa);
-        memset(&sr, 0, sizeof sr);
-        for (int k = 0; k < steps * world; ++k) {
-            sa.p[k] = slices[j0 * world + k];
-            sr.p[k] = slices[j0 * world + k] + done;
-        }
-        if (nchunks > 0 && few)
-            hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsFew>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
-                               stream, sa, steps, (int)world, first, (float)world, out);
-        else if (nchunks > 0)
-            hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsMany>, dim3((uint32_t)nchunks), dim3(kThreads), 0,
-                               stream, sa, steps, (int)world, first, (float)world, out);
-        if (rest > 0) {
-            if (aligned)
-                hipLaunchKernelGGL(reduce_rs_general_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
-                                   stream, sr, steps, (int)world, first, (float)world, rest, out + done);
+        for (int k = 0; k < steps * world; ++k) sa.p[k] = slices[j0 * world + k];
+        if (aligned) {
+            const bool few = steps * world <= kRedFewTerms;
+            const int64_t chunk = kWgRow * (few ? kRsGroupsFew : kRsGroupsMany);
+            const dim3 g((uint32_t)((n + chunk - 1) / chunk));
+            if (few)
+                hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsFew>, g, dim3(kThreads), 0, stream, sa, steps,
+                                   (int)world, first, (float)world, out, n);
             else
-                hipLaunchKernelGGL(reduce_rs_general_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
-                                   stream, sr, steps, (int)world, first, (float)world, rest, out + done);
+                hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsMany>, g, dim3(kThreads), 0, stream, sa, steps,
+                                   (int)world, first, (float)world, out, n);
+        } else {
+            const int64_t grid = std::max<int64_t>(1, ((n >> 3) + kThreads - 1) / kThreads);
+            hipLaunchKernelGGL(reduce_rs_general_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, steps,
+                               (int)world, first, (float)world, n, out);
         }
         int rc = check_launch("fs_reduce_shard_ex");
         if (rc != FS_OK) return rc;
@@ -1466,35 +1487,29 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
     const AdamConsts c = adam_consts(*hp);
     const bool aligned = !misaligned(master, 16) && !misaligned(exp_avg, 16) && !misaligned(exp_avg_sq, 16) &&
                          !misaligned(grad, 16) && !(param_bf16 && misaligned(param_bf16, 16));
+    if (!grid_fits(n)) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
     (void)hipGetLastError();
-    int64_t done = 0;
-    if (aligned && n >= kAdamChunk) {
-        const int64_t nchunks = n / kAdamChunk;
-        if (nchunks > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
-        const dim3 g((uint32_t)nchunks), b(kThreads);
+    if (aligned) {
+        const dim3 g((uint32_t)((n + kWgRow - 1) / kWgRow)), b(kThreads);
         if (grad_dtype == FS_BF16) {
             if (param_bf16)
-                hipLaunchKernelGGL((adamw_wave_kernel<true, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
-                                   grad, param_bf16, c);
+                hipLaunchKernelGGL((adamw_kernel<true, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                                   param_bf16, c, n);
             else
-                hipLaunchKernelGGL((adamw_wave_kernel<true, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
-                                   grad, param_bf16, c);
+                hipLaunchKernelGGL((adamw_kernel<true, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                                   param_bf16, c, n);
         } else {
             if (param_bf16)
-                hipLaunchKernelGGL((adamw_wave_kernel<false, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
-                                   grad, param_bf16, c);
+                hipLaunchKernelGGL((adamw_kernel<false, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                                   param_bf16, c, n);
             else
-                hipLaunchKernelGGL((adamw_wave_kernel<false, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq,
-                                   grad, param_bf16, c);
+                hipLaunchKernelGGL((adamw_kernel<false, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                                   param_bf16, c, n);
         }
-        done = nchunks * kAdamChunk;
-    }
-    if (done < n) {
-        const int64_t rest = n - done;
-        const int64_t grid = (rest + kThreads - 1) / kThreads;
-        if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
-        hipLaunchKernelGGL(adamw_scalar_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, done, n, master,
-                           exp_avg, exp_avg_sq, grad, (int)(grad_dtype == FS_BF16), param_bf16, c);
+    } else {
+        hipLaunchKernelGGL(adamw_scalar_kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                           stream, n, master, exp_avg, exp_avg_sq, grad, (int)(grad_dtype == FS_BF16), param_bf16,
+                           c);
     }
     return check_launch("fs_adamw_step");
 }
@@ -1537,73 +1552,28 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
                 return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: an output overlaps slice %d", t);
     }
     const AdamConsts c = adam_consts(*hp);
-    // terms beyond the last kTermsPerPass: plain reduce passes leave partial sums in grad_out
+    if (!grid_fits(n)) return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: n too large for one launch");
+    // terms before the last kTermsPerPass: plain reduce passes leave partial sums in grad_out
     const int last_cnt = terms - (terms - 1) / kTermsPerPass * kTermsPerPass;
     const int t_last = terms - last_cnt;
-    const bool few = last_cnt <= kRedFewTerms;
-    const int64_t chunk = (int64_t)kThreads * 4 * (few ? kFusedGroupsFew : kFusedGroupsMany);
-    const int64_t nchunks = aligned ? n / chunk : 0;
-    const int64_t done = nchunks * chunk;
-    const int64_t rest = n - done;
-    const int64_t rest_grid = std::max<int64_t>(1, ((rest >> 3) + kThreads - 1) / kThreads);
-    if (nchunks > INT32_MAX || rest_grid > INT32_MAX)
-        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: n too large for one launch");
     (void)hipGetLastError();
-    for (int t0 = 0; t0 < t_last; t0 += kTermsPerPass) {
-        SliceArgs sa;
-        memset(&sa, 0, sizeof sa);
-        for (int k = 0; k < kTermsPerPass; ++k) sa.p[k] = slices[t0 + k];
-        const int64_t pre_chunks = done / kRedChunk, pre_done = pre_chunks * kRedChunk;
-        if (pre_chunks > 0)
-            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsMany>, dim3((uint32_t)pre_chunks), dim3(kThreads), 0,
-                               stream, sa, kTermsPerPass, (int)(t0 == 0), 0, (float)world, grad_out);
-        if (done > pre_done) {   // [pre_done, done): fused chunks smaller than the reduce chunk
-            SliceArgs sm;
-            memset(&sm, 0, sizeof sm);
-            for (int k = 0; k < kTermsPerPass; ++k) sm.p[k] = slices[t0 + k] + pre_done;
-            const int64_t mid = done - pre_done;
-            hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)(((mid >> 3) + kThreads - 1) / kThreads)),
-                               dim3(kThreads), 0, stream, sm, kTermsPerPass, (int)(t0 == 0), 0, (float)world, mid,
-                               grad_out + pre_done);
-        }
-        if (rest > 0) {
-            SliceArgs sr;
-            memset(&sr, 0, sizeof sr);
-            for (int k = 0; k < kTermsPerPass; ++k) sr.p[k] = slices[t0 + k] + done;
-            if (aligned)
-                hipLaunchKernelGGL(reduce_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
-                                   kTermsPerPass, (int)(t0 == 0), 0, (float)world, rest, grad_out + done);
-            else
-                hipLaunchKernelGGL(reduce_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0, stream, sr,
-                                   kTermsPerPass, (int)(t0 == 0), 0, (float)world, rest, grad_out + done);
-        }
-    }
+    for (int t0 = 0; t0 < t_last; t0 += kTermsPerPass)
+        launch_reduce_pass(n, stream, slices, t0, kTermsPerPass, t0 == 0, 0, (float)world, aligned, grad_out);
     SliceArgs sa;
     memset(&sa, 0, sizeof sa);
     for (int k = 0; k < last_cnt; ++k) sa.p[k] = slices[t_last + k];
     const int first = t_last == 0;
-    if (nchunks > 0) {
-        if (few)
-            launch_fused_chunks<kFusedGroupsFew>(nchunks, stream, sa, last_cnt, first, (float)world, master, exp_avg,
-                                                 exp_avg_sq, param_bf16, grad_out, c);
+    if (aligned) {
+        if (last_cnt <= kRedFewTerms)
+            launch_fused<kFusedGroupsFew>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg, exp_avg_sq,
+                                          param_bf16, grad_out, c);
         else
-            launch_fused_chunks<kFusedGroupsMany>(nchunks, stream, sa, last_cnt, first, (float)world, master,
-                                                  exp_avg, exp_avg_sq, param_bf16, grad_out, c);
-    }
-    if (rest > 0) {
-        SliceArgs sr;
-        memset(&sr, 0, sizeof sr);
-        for (int k = 0; k < last_cnt; ++k) sr.p[k] = slices[t_last + k] + done;
-        uint16_t *p16r = param_bf16 ? param_bf16 + done : nullptr;
-        float *gr = grad_out ? grad_out + done : nullptr;
-        if (aligned)
-            hipLaunchKernelGGL(reduce_adamw_general_kernel<true>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
-                               stream, sr, last_cnt, first, (float)world, rest, master + done, exp_avg + done,
-                               exp_avg_sq + done, p16r, gr, c);
-        else
-            hipLaunchKernelGGL(reduce_adamw_general_kernel<false>, dim3((uint32_t)rest_grid), dim3(kThreads), 0,
-                               stream, sr, last_cnt, first, (float)world, rest, master + done, exp_avg + done,
-                               exp_avg_sq + done, p16r, gr, c);
+            launch_fused<kFusedGroupsMany>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg, exp_avg_sq,
+                                           param_bf16, grad_out, c);
+    } else {
+        const int64_t grid = std::max<int64_t>(1, ((n >> 3) + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(reduce_adamw_general_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, last_cnt,
+                           first, (float)world, n, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
     }
     return check_launch("fs_reduce_adamw_step");
 }

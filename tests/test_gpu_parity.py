@@ -199,6 +199,10 @@ REDUCE_CASES = [
     (4097, 8, 4, 1, 0), (4097, 8, 4, 3, 1), (4096, 4, 2, 0, 2),   # misaligned slices / out
     (70001, 8, 4, 1, 0),         # misaligned, large
     (30011, 5, 7, 0, 0),         # 35 terms: a 32-term pass (long chunks), then 3 terms (short chunks)
+    (16384 * 2 + 4096 * 3 + 5, 8, 4, 0, 0),   # last chunk cut into four sub-chunks, the fourth holding 5 elements
+    (16384 + 4095, 4, 8, 0, 0),  # last chunk: four sub-chunks, a straddling group of 3 elements
+    (4096 * 5 + 1027, 8, 1, 0, 0),   # few terms: last chunk of 1027 elements
+    (1025, 8, 1, 0, 0), (4095, 16, 1, 0, 0), (4097, 17, 1, 0, 0),   # 16 / 17 terms: the chunk switch
     (25_297_920, 8, 1, 0, 0),    # one Llama-7B block shard, 8-buffer average
 ]
 
@@ -283,10 +287,14 @@ def _adam_inputs(n, seed, step, grad_bf16, shift=0):
 
 
 ADAM_CASES = [
-    # (n, step, grad_bf16, with p16, shift)
+    # (n, step, grad_bf16, with p16, shift); the aligned kernel works in
+    # 1024-element workgroups, the last one cut by n
     (1, 1, False, True, 0), (7, 1, False, True, 0), (8, 2, True, True, 0), (1003, 1000, False, True, 0),
+    (1023, 3, False, False, 0), (1024, 1, False, False, 0), (1025, 2, True, False, 0),
     (1 << 20, 1, False, True, 0), (1 << 20, 1000, True, False, 0), (4101, 7, False, True, 1),
-    (4096 * 3 + 5, 3, True, True, 0), (4096, 1, False, False, 0), (4095, 2, False, True, 0),
+    # every <bf16 grad, bf16 copy> build over whole workgroups plus a ragged last one
+    (1024 * 13 + 3, 3, True, True, 0), (1024 * 7 + 2, 5, False, False, 0),
+    (1024 * 9 + 1, 4, True, False, 0), (1024 * 11 + 3, 6, False, True, 0),
     (50003, 9, True, True, 2),
     (25_297_920, 1000, False, True, 0),
 ]
@@ -334,6 +342,9 @@ FUSED_CASES = [
     (40000, 8, 5, 0, True, True, 5),      # 40 terms: partial sums pass through grad_out
     (20007, 2, 33, 0, False, True, 2),    # 66 terms
     (30011, 5, 7, 0, True, True, 3),      # 35 terms: one reduce pass, then a fused pass of 3 terms
+    (16384 * 2 + 4096 * 3 + 5, 8, 4, 0, True, True, 2),   # last chunk in four sub-chunks, 5 elements in the fourth
+    (4096 * 6 + 1029, 8, 1, 0, True, False, 1),           # few terms: a last chunk of 1029 elements
+    (16384 + 4095, 4, 8, 0, False, True, 4),              # straddling group of 3 elements, no bf16 copy
     (25_297_920, 8, 1, 0, True, False, 1000),
 ]
 
@@ -395,6 +406,8 @@ RS_CASES = [
     (100003, 32, 1, 0, 0),    # N = 32
     (30011, 5, 7, 0, 0),      # 35 terms: a pass of 6 micro-steps (30 terms), then one of 1 (5 terms)
     (12345, 17, 3, 0, 0),     # one micro-step (17 terms) per pass
+    (8192 * 3 + 4096 + 7, 8, 4, 0, 0),   # last chunk in two sub-chunks
+    (4096 * 3 + 2051, 8, 2, 0, 0),       # few terms: last chunk of 2051 elements
     (25_297_920, 8, 4, 0, 0),
 ]
 
