@@ -8,11 +8,15 @@ gcc, no fast-math, no FMA contraction); this module only marshals numpy arrays
 into those loops, plus the memory ledger, which is plain arithmetic.
 
 Sources, cited by page title and section:
-  [P1] "FSDP1 vs FSDP2" -- section 01 (per-rank ledger), section 03 (layouts),
-       the strategy ledger table (FULL_SHARD / SHARD_GRAD_OP / NO_SHARD),
-       Table 3 (worked example).
-  [P2] "Data parallelism, ZeRO and FSDP" -- sections 1, 2.1, 5, 9 and 9.4.
-  [P3] "ZeRO/FSDP explainer (AI infra KB M036)" -- section 03 (7B, 8 cards).
+  "FSDP1 vs FSDP2" -- section 01 (per-rank ledger), section 03 (layouts),
+      the strategy ledger table (FULL_SHARD / SHARD_GRAD_OP / NO_SHARD),
+      Table 3 (worked example).
+  "Data parallelism, ZeRO and FSDP" -- sections 1, 2.1, 5, 9 and 9.4.
+  "ZeRO/FSDP explainer" (AI infra KB M036) -- sections 03 (7B, 8 cards), 04.
+
+The C source builds twice: liboracle.so (single-threaded, what every check
+uses) and liboracle_omp.so (the same loops under OpenMP, used only to time
+the oracle on all host cores; pass parallel=True).
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fs_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
 
 # gcc flags: each C operator is one IEEE operation (no contraction into FMA,
 # no fast-math reassociation), so the loops compute exactly what they say.
@@ -35,23 +40,26 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
 
 
 def build(force: bool = True) -> str:
-    """Compile fs_oracle.c into liboracle.so with gcc (host only)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
+    """Compile fs_oracle.c with gcc (host only) into liboracle.so and, with
+    -fopenmp, into liboracle_omp.so."""
+    for path, extra in ((_LIB, []), (_LIB_OMP, ["-fopenmp"])):
+        if force or not os.path.exists(path):
+            tmp = path + ".tmp"
+            subprocess.run(["gcc", *CFLAGS, *extra, _SRC, "-o", tmp, "-lm"], check=True)
+            os.replace(tmp, path)
     return _LIB
 
 
-_lib: Optional[ctypes.CDLL] = None
+_libs = {}
 
 
-def lib() -> ctypes.CDLL:
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB):
+def lib(parallel: bool = False) -> ctypes.CDLL:
+    """The single-threaded oracle library, or (parallel=True) its OpenMP build."""
+    if parallel not in _libs:
+        path = _LIB_OMP if parallel else _LIB
+        if not os.path.exists(path):
             build(force=False)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         f32 = ctypes.c_float
         L.oracle_fsdp1_layout.argtypes = [i32, vp, i32, i32, i32, vp, vp, vp]
@@ -81,8 +89,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_adamw.argtypes = [i64, vp, vp, vp, vp, i32, vp,
                                    f32, f32, f32, f32, f32, i64]
         L.oracle_adamw.restype = None
-        _lib = L
-    return _lib
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = ctypes.c_int
+        _libs[parallel] = L
+    return _libs[parallel]
+
+
+def threads(parallel: bool = False) -> int:
+    """Threads the element loops of that build use."""
+    return int(lib(parallel).oracle_threads())
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -170,7 +185,7 @@ class Layout:
 
 def fsdp1_layout(shapes: Sequence[Sequence[int]], elem_bytes: int, world: int,
                  use_orig_params: bool) -> Layout:
-    """FSDP1 FlatParameter layout [P1 section 03; Table 3]."""
+    """FSDP1 FlatParameter layout ["FSDP1 vs FSDP2", section 03 and Table 3]."""
     numel = np.array([_numel(s) for s in shapes], np.int64)
     n = len(numel)
     start = np.zeros(max(1, n), np.int64)
@@ -187,7 +202,7 @@ def fsdp1_layout(shapes: Sequence[Sequence[int]], elem_bytes: int, world: int,
 
 def fsdp2_layout(shapes: Sequence[Sequence[int]], elem_bytes: int,
                  world: int) -> Layout:
-    """FSDP2 per-parameter dim-0 layout [P1 section 03; Table 3].
+    """FSDP2 per-parameter dim-0 layout ["FSDP1 vs FSDP2", section 03 and Table 3].
 
     A 0-d parameter is taken as shape [1]; row = product of dims 1.."""
     d0 = np.array([int(s[0]) if len(s) else 1 for s in shapes], np.int64)
@@ -206,7 +221,7 @@ def fsdp2_layout(shapes: Sequence[Sequence[int]], elem_bytes: int,
                   chunk_rows=cr[:n], row=row, pre=pre[:n])
 
 
-def pack(layout: Layout, params: Sequence[np.ndarray], rank: int = -1) -> np.ndarray:
+def pack(layout: Layout, params: Sequence[np.ndarray], rank: int = -1, parallel: bool = False) -> np.ndarray:
     """All-gather copy-in.  params: 1-D arrays of the layout's element size
     (uint16 for bf16 bits, uint32/float32 for fp32).  Returns the gathered
     buffer (rank < 0) or rank's shard, same dtype as the params."""
@@ -218,7 +233,7 @@ def pack(layout: Layout, params: Sequence[np.ndarray], rank: int = -1) -> np.nda
     out = np.empty(max(1, size), dt)
     ptrs = (ctypes.c_void_p * max(1, len(ps)))(*[_ptr(p) for p in ps])
     c = layout._c()
-    lib().oracle_pack(ctypes.byref(c), ptrs, _ptr(out), int(rank))
+    lib(parallel).oracle_pack(ctypes.byref(c), ptrs, _ptr(out), int(rank))
     return out[:size]
 
 
@@ -253,7 +268,7 @@ def reshard(src_layout: Layout, dst_layout: Layout, gathered: np.ndarray) -> np.
     return out[:dst_layout.gathered_numel]
 
 
-def unpack(layout: Layout, gathered: np.ndarray) -> List[np.ndarray]:
+def unpack(layout: Layout, gathered: np.ndarray, parallel: bool = False) -> List[np.ndarray]:
     """All-gather copy-out: per-parameter 1-D arrays from a gathered buffer."""
     dt = np.uint16 if layout.elem_bytes == 2 else np.uint32
     g = np.ascontiguousarray(gathered).view(dt).reshape(-1)
@@ -261,7 +276,7 @@ def unpack(layout: Layout, gathered: np.ndarray) -> List[np.ndarray]:
     outs = [np.empty(max(1, int(n)), dt) for n in layout.numel]
     ptrs = (ctypes.c_void_p * max(1, len(outs)))(*[_ptr(o) for o in outs])
     c = layout._c()
-    lib().oracle_unpack(ctypes.byref(c), _ptr(g) if g.size else _ptr(np.zeros(1, dt)), ptrs)
+    lib(parallel).oracle_unpack(ctypes.byref(c), _ptr(g) if g.size else _ptr(np.zeros(1, dt)), ptrs)
     return [o[:int(n)] for o, n in zip(outs, layout.numel)]
 
 
@@ -283,22 +298,23 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32)
 
 
-def reduce_shard(slices: Sequence[np.ndarray], world: int, grad_acc: int) -> np.ndarray:
+def reduce_shard(slices: Sequence[np.ndarray], world: int, grad_acc: int, parallel: bool = False) -> np.ndarray:
     """Average slices[j*world + k] (bf16 bits, uint16) into an fp32 shard
-    [P2 sections 2.1, 5, 9.2]."""
+    ["Data parallelism, ZeRO and FSDP", sections 2.1, 5 and 9.2]."""
     assert len(slices) == world * grad_acc
     ss = [np.ascontiguousarray(s, np.uint16).reshape(-1) for s in slices]
     n = ss[0].size
     assert all(s.size == n for s in ss)
     out = np.empty(max(1, n), np.float32)
     ptrs = (ctypes.c_void_p * len(ss))(*[_ptr(s) for s in ss])
-    lib().oracle_reduce(n, world, grad_acc, ptrs, _ptr(out))
+    lib(parallel).oracle_reduce(n, world, grad_acc, ptrs, _ptr(out))
     return out[:n]
 
 
 def reduce_shard_bf16rs(slices: Sequence[np.ndarray], world: int, grad_acc: int) -> np.ndarray:
     """Average with a bf16 reduce dtype: each micro-step's N-way average is
-    delivered as bf16, then accumulated in fp32 [P1 mixed precision; P2 9.2]."""
+    delivered as bf16, then accumulated in fp32 ["FSDP1 vs FSDP2", mixed
+    precision; "Data parallelism, ZeRO and FSDP", section 9.2]."""
     assert len(slices) == world * grad_acc
     ss = [np.ascontiguousarray(s, np.uint16).reshape(-1) for s in slices]
     n = ss[0].size
@@ -320,8 +336,9 @@ class AdamWHparams:
 
 
 def adamw_step(master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
-               grad: np.ndarray, hp: AdamWHparams, want_bf16: bool = True):
-    """One AdamW step [P2 sections 1 and 9.1; P3 section 04].
+               grad: np.ndarray, hp: AdamWHparams, want_bf16: bool = True, parallel: bool = False):
+    """One AdamW step ["Data parallelism, ZeRO and FSDP", sections 1 and 9.1;
+    "ZeRO/FSDP explainer", section 04].
 
     Returns new copies (master, exp_avg, exp_avg_sq, param_bf16 or None); the
     inputs are not modified.  grad: float32 array, or uint16 bf16 bits."""
@@ -336,7 +353,7 @@ def adamw_step(master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
     assert m.size == n and v.size == n and g.size == n
     p16 = np.empty(max(1, n), np.uint16) if want_bf16 else None
     dummy = np.zeros(1, np.float32)
-    lib().oracle_adamw(n, _ptr(th) if n else _ptr(dummy), _ptr(m) if n else _ptr(dummy),
+    lib(parallel).oracle_adamw(n, _ptr(th) if n else _ptr(dummy), _ptr(m) if n else _ptr(dummy),
                        _ptr(v) if n else _ptr(dummy), _ptr(g) if n else _ptr(dummy),
                        int(is_bf16), _ptr(p16) if want_bf16 else None,
                        hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
@@ -348,17 +365,19 @@ def adamw_step(master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
 # Memory ledger (plain arithmetic)
 # --------------------------------------------------------------------------
 
-GB = 1e9  # the pages count decimal GB [P1 section 01 calculator]
+GB = 1e9  # the pages count decimal GB ("FSDP1 vs FSDP2", section 01 calculator)
 
 
 def ledger(P: float, N: int, b: float, bopt: float, fp32_grad_acc: bool = False) -> dict:
-    """Per-rank resident bytes of each scheme [P1 section 01 table; P2
-    section 9; P3 section 03].
+    """Per-rank resident bytes of each scheme ["FSDP1 vs FSDP2", section 01
+    table; "Data parallelism, ZeRO and FSDP", section 9; "ZeRO/FSDP
+    explainer", section 03].
 
     P parameters, N data-parallel ranks, b bytes per parameter and per
     gradient, bopt optimizer bytes per parameter.  With fp32 gradient
     accumulation the gradient term grows by 4 bytes per parameter on the
-    part each scheme keeps of the gradient (P2 section 9)."""
+    part each scheme keeps of the gradient ("Data parallelism, ZeRO and FSDP",
+    section 9)."""
     acc = 4.0 if fp32_grad_acc else 0.0
     return {
         "ddp": P * (2 * b + bopt) + acc * P,
@@ -369,7 +388,7 @@ def ledger(P: float, N: int, b: float, bopt: float, fp32_grad_acc: bool = False)
 
 
 def strategy_ledger(P: float, N: int, b: float, bopt: float) -> dict:
-    """FSDP1 strategy table [P1 strategy ledger]: resident, worst-case peak
+    """FSDP1 strategy table ["FSDP1 vs FSDP2", strategy ledger]: resident, worst-case peak
     (resident plus one full parameter copy while it is gathered) and
     communication bytes per iteration per card (3P(N-1)/N elements for
     FULL_SHARD, 2P(N-1)/N for SHARD_GRAD_OP and NO_SHARD)."""

@@ -9,12 +9,12 @@
  * Everything here is a plain, slow, element-by-element loop that follows the
  * pages' definitions in their own order.  Sources (page title, then section):
  *
- *   [P1] "FSDP1 vs FSDP2" (visual reading, blog.vllbc.top)
+ *   "FSDP1 vs FSDP2" (visual reading, blog.vllbc.top)
  *        -- section 03 (the two representations): FlatParameter alignment
  *           padding, world-size padding, flatten().chunk(N); FSDP2 dim-0
  *           ceil(s_i/N) chunks and group concatenation.
  *        -- Table 3 (worked example: parameters of 3 and 5 elements, N=4).
- *   [P2] "Data parallelism, ZeRO and FSDP" (hs-black.github.io)
+ *   "Data parallelism, ZeRO and FSDP" (hs-black.github.io)
  *        -- section 1 (16 B/param mixed-precision recipe; fp32 gradient
  *           accumulation; Adam updates the moments first, then the params),
  *        -- section 2.1 (gradients are summed, then divided by N_d),
@@ -44,6 +44,31 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/*
+ * The same source also builds with -fopenmp (liboracle_omp.so, used only to
+ * time the oracle on every host core): ELEMENT_LOOP marks loops whose
+ * iterations write disjoint outputs and share no accumulator, so running them
+ * on several threads changes no arithmetic and no result.
+ */
+#ifdef _OPENMP
+#define ELEMENT_LOOP _Pragma("omp parallel for schedule(static)")
+#else
+#define ELEMENT_LOOP
+#endif
+
+/* Threads the element loops use (1 in the single-threaded build). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 uint16_t oracle_bf16_round(float f); /* defined with the number formats below */
 
@@ -52,7 +77,7 @@ uint16_t oracle_bf16_round(float f); /* defined with the number formats below */
 /* ------------------------------------------------------------------------ */
 
 /*
- * FSDP1 FlatParameter layout [P1 section 03; Table 3].
+ * FSDP1 FlatParameter layout ["FSDP1 vs FSDP2", section 03 and Table 3].
  * Parameters are flattened and concatenated in order.  With use_orig_params
  * the start of every parameter after the first is padded up to a multiple of
  * a = 16 / elem_bytes elements (16-byte boundary, at most a-1 pad elements).
@@ -89,7 +114,7 @@ int oracle_fsdp1_layout(int32_t n_params, const int64_t *numel,
 }
 
 /*
- * FSDP2 per-parameter layout [P1 section 03: each parameter is chunked on
+ * FSDP2 per-parameter layout ["FSDP1 vs FSDP2", section 03: each parameter is chunked on
  * dim 0 into ceil(s_i/N) rows per rank, padding belongs to that parameter
  * alone, an empty parameter gets empty chunks; the group's shards are
  * concatenated into one all-gather input].
@@ -187,7 +212,8 @@ void oracle_index_at(const oracle_layout *L, int64_t n, const int32_t *param,
 }
 
 /*
- * All-gather copy-in [P1 section 03 and the FSDP2 group concatenation]:
+ * All-gather copy-in ["FSDP1 vs FSDP2", section 03, and the FSDP2 group
+ * concatenation]:
  * start from a zero-filled output and copy every parameter element to its
  * place.  rank < 0 writes the whole gathered buffer (N * shard elements);
  * rank r writes only shard r, into an output of `shard` elements.
@@ -205,6 +231,7 @@ void oracle_pack(const oracle_layout *L, const void *const *params, void *out,
     memset(out, 0, (size_t)((hi - lo) * w));
     for (int32_t i = 0; i < L->n_params; ++i) {
         const unsigned char *p = (const unsigned char *)params[i];
+        ELEMENT_LOOP
         for (int64_t e = 0; e < L->numel[i]; ++e) {
             int64_t x = gathered_index(L, i, e);
             if (x >= lo && x < hi)
@@ -215,8 +242,8 @@ void oracle_pack(const oracle_layout *L, const void *const *params, void *out,
 }
 
 /*
- * Copy-in with the parameter-dtype cast at the all-gather boundary [P1
- * section on mixed precision: the all-gather casts the parameters to
+ * Copy-in with the parameter-dtype cast at the all-gather boundary ["FSDP1 vs
+ * FSDP2", section on mixed precision: the all-gather casts the parameters to
  * param_dtype while the optimizer keeps the original dtype].  The layout is
  * the bf16 one (elem_bytes 2); the parameters are fp32 and every element is
  * written as the round-to-nearest-even bf16 of its value; pads are zero.
@@ -250,6 +277,7 @@ void oracle_unpack(const oracle_layout *L, const void *gathered,
     const int64_t w = L->elem_bytes;
     for (int32_t i = 0; i < L->n_params; ++i) {
         unsigned char *p = (unsigned char *)params[i];
+        ELEMENT_LOOP
         for (int64_t e = 0; e < L->numel[i]; ++e) {
             int64_t x = gathered_index(L, i, e);
             memcpy(p + e * w, (const unsigned char *)gathered + x * w,
@@ -320,9 +348,10 @@ void oracle_bf16_round_array(int64_t n, const float *in, uint16_t *out)
 /* ------------------------------------------------------------------------ */
 
 /*
- * This rank's averaged gradient shard [P2 section 2.1: sum the ranks'
- * gradients, then divide by N_d; P2 sections 1 and 9.2: accumulate in fp32
- * over the micro-steps on the own 1/N_d; P2 section 5: the 1/grad_acc factor
+ * This rank's averaged gradient shard ["Data parallelism, ZeRO and FSDP",
+ * section 2.1: sum the ranks' gradients, then divide by N_d; sections 1 and
+ * 9.2: accumulate in fp32 over the micro-steps on the own 1/N_d; section 5:
+ * the 1/grad_acc factor
  * is already in each micro-step's loss, so the engine only sums over them].
  *
  * slices[j*world + k] is rank k's gradient at micro-step j, restricted to
@@ -334,6 +363,7 @@ void oracle_reduce(int64_t n, int32_t world, int32_t grad_acc,
                    const uint16_t *const *slices, float *out)
 {
     const int32_t terms = world * grad_acc;
+    ELEMENT_LOOP
     for (int64_t e = 0; e < n; ++e) {
         float acc = bf16_to_float(slices[0][e]);
         for (int32_t t = 1; t < terms; ++t) {
@@ -345,9 +375,9 @@ void oracle_reduce(int64_t n, int32_t world, int32_t grad_acc,
 }
 
 /*
- * The same averaging with a bf16 reduce dtype [P1 section on mixed
- * precision: reduce_dtype sets the precision of the gradient reduction; P2
- * section 9.2: the own 1/N_d fp32 buffer accumulates the bf16 gradients the
+ * The same averaging with a bf16 reduce dtype ["FSDP1 vs FSDP2", section on
+ * mixed precision: reduce_dtype sets the precision of the gradient reduction;
+ * "Data parallelism, ZeRO and FSDP", section 9.2: the own 1/N_d fp32 buffer accumulates the bf16 gradients the
  * reduce-scatter delivers].  Per micro-step j the N ranks' terms are added in
  * fp32 in rank order and divided once by N -- the reduce-scatter's average --
  * and that average is delivered as bf16 (round to nearest even); the
@@ -356,6 +386,7 @@ void oracle_reduce(int64_t n, int32_t world, int32_t grad_acc,
 void oracle_reduce_bf16rs(int64_t n, int32_t world, int32_t grad_acc,
                           const uint16_t *const *slices, float *out)
 {
+    ELEMENT_LOOP
     for (int64_t e = 0; e < n; ++e) {
         float acc = 0.0f;
         for (int32_t j = 0; j < grad_acc; ++j) {
@@ -374,10 +405,10 @@ void oracle_reduce_bf16rs(int64_t n, int32_t world, int32_t grad_acc,
 /* ------------------------------------------------------------------------ */
 
 /*
- * One AdamW step over this rank's shard [P2 section 1: Adam updates the
- * first and second moments, then the parameter; P2 section 9.1: the rank
- * updates its own fp32 parameters and then turns them into bf16; P3
- * section 04: optimizer_step over the local sharded states, AdamW built on
+ * One AdamW step over this rank's shard ["Data parallelism, ZeRO and FSDP",
+ * section 1: Adam updates the first and second moments, then the parameter;
+ * section 9.1: the rank updates its own fp32 parameters and then turns them
+ * into bf16; "ZeRO/FSDP explainer", section 04: optimizer_step over the local sharded states, AdamW built on
  * the sharded parameters].
  *
  * Update (decoupled weight decay scaled by lr), all in double:
@@ -400,6 +431,7 @@ void oracle_adamw(int64_t n, float *master, float *exp_avg, float *exp_avg_sq,
     const double bias1 = 1.0 - pow(b1, (double)step);
     const double bias2 = 1.0 - pow(b2, (double)step);
     const double lr_d = lr, eps_d = eps, wd_d = weight_decay;
+    ELEMENT_LOOP
     for (int64_t e = 0; e < n; ++e) {
         double g = grad_is_bf16 ? (double)bf16_to_float(((const uint16_t *)grad)[e])
                                 : (double)((const float *)grad)[e];

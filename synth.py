@@ -153,6 +153,16 @@ def normal_bf16(seed: int, stream: int, count: int, sigma: float, device="cpu",
     return _fill(out, start, lambda i: normal_bf16_at(seed, stream, i, sigma))
 
 
+def fill_normal(out: torch.Tensor, seed: int, stream: int, sigma: float, start: int = 0) -> torch.Tensor:
+    """Fill `out` (fp32 or bf16, any device, contiguous) in place with the
+    same values normal_f32 / normal_bf16 would return for this range."""
+    if out.dtype == torch.float32:
+        return _fill(out, start, lambda i: normal_f32_at(seed, stream, i, sigma))
+    if out.dtype == torch.bfloat16:
+        return _fill(out, start, lambda i: normal_bf16_at(seed, stream, i, sigma))
+    raise ValueError(f"fill_normal: unsupported dtype {out.dtype}")
+
+
 def to_numpy_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bits of a CPU tensor as numpy uint16 (2-byte) or uint32 (4-byte)."""
     t = t.detach().contiguous().cpu()
