@@ -13,8 +13,22 @@ in HBM before timing starts:
 The layout plans are built and uploaded once, before timing (a plan is made
 once per group).  Throughput is algorithmic bytes (what the method must read
 and write) per second; per-kernel durations come from HIP events recorded on
-the stream the kernels run on.  The CPU baseline is the plain C oracle on a
-bounded sample of the same workload, single-threaded.
+the stream the kernels run on.
+
+Where the buffers land in HBM moves the rates by several percent, and the
+process's allocation order decides it.  So the step is set up and timed once
+per allocation order (parameters first, shard state first, plan tables
+first), each from a freshly emptied allocator; the headline figures are those
+of the order with the median step time, and every order's figures (and the
+worst) are in the line too.  The 32 gradient slices live in one buffer, and
+theta, m, v and the fp32 gradient in another (the engine's shard state as
+one allocation).
+
+After the 7B buffers are freed, the 70B model's rank-0 shard (80 blocks,
+grad_acc = 2) is measured: the per-group reduce over a reused slice pool,
+the whole-shard AdamW, and the per-group fused reduce + AdamW.  The CPU
+baseline is the plain C oracle on a bounded sample of the 7B workload,
+single-threaded and on every host core.
 
 Prints one JSON line.  `--gpus N` with N > 1 is refused: this engine runs all
 logical ranks on one GPU.
@@ -25,6 +39,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -39,9 +54,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7b_shard_step.json")
 WORKLOADS = {
     # name: (n_blocks, d, f, kv, vocab, world, grad_acc)
     "7b": (32, 4096, 11008, None, 32000, 8, 4),
+    "70b": (80, 8192, 28672, 1024, 32000, 8, 2),
 }
 # llama_model_groups(n_blocks, d, f, vocab, kv) arguments per workload
 _WL_SHAPES = {k: (v[0], v[1], v[2], v[4], v[3]) for k, v in WORKLOADS.items()}
+ORDERS = ("params_first", "state_first", "plans_first")
 
 
 def log(*a):
@@ -61,13 +78,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def setup(workload: str, seed: int = 4, order: str = "params_first"):
-    """Allocate and fill every input in HBM.  By default the parameters and
-    gathered buffers come first, then the gradient slices and the fp32 shard
-    state, then the small plan tables.  The order fixes where the big buffers
-    land physically, and that moves HBM efficiency by several percent: on one
-    MI355X, AdamW ran at 6.45 TB/s with this order and at 5.7 TB/s with the
-    state allocated first ("state_first"); "plans_first" is in between."""
+def setup(workload: str = "7b", seed: int = 4, order: str = "params_first", pooled: bool = True):
+    """Allocate and fill every input in HBM, in the given order of the three
+    allocation families: parameters, gathered buffers and copy-out targets
+    ("params"); the gradient-slice pool, the fp32 shard state pool and the
+    bf16 parameter copy ("state"); the plans' device tables ("plans")."""
     import torch
 
     import fsdp_sharded_state_amd as fs
@@ -80,23 +95,33 @@ def setup(workload: str, seed: int = 4, order: str = "params_first"):
     P = sum(p.total_numel for p in probe)
     gathered_numels = [p.gathered_numel for p in probe]
     del probe
-    log(f"workload {workload}: {len(groups)} groups, P={P}, shard S={S}, N={world}, A={grad_acc}")
+    log(f"workload {workload}, order {order}: {len(groups)} groups, P={P}, shard S={S}, N={world}, A={grad_acc}")
 
     t0 = time.time()
-    W = dict(fs=fs, S=S, P=P, world=world, grad_acc=grad_acc, groups=len(groups), workload=workload)
+    W = dict(fs=fs, S=S, P=P, world=world, grad_acc=grad_acc, groups=len(groups), workload=workload, order=order)
 
     def alloc_state():
+        T = world * grad_acc
+        if pooled:
+            pool = torch.empty(T * S, dtype=torch.bfloat16, device="cuda")
+            bufs = [pool[t * S:(t + 1) * S] for t in range(T)]
+            st = torch.empty(4 * S, dtype=torch.float32, device="cuda")
+            master, exp_avg, exp_avg_sq, grad32 = (st[i * S:(i + 1) * S] for i in range(4))
+        else:
+            bufs = [torch.empty(S, dtype=torch.bfloat16, device="cuda") for _ in range(T)]
+            master, exp_avg, exp_avg_sq, grad32 = (torch.empty(S, dtype=torch.float32, device="cuda")
+                                                   for _ in range(4))
         slices = []
         for j in range(grad_acc):
             for k in range(world):
-                slices.append(synth.normal_bf16(seed, synth.stream_grad(j, k, world), S, 1e-3, device="cuda"))
-            log(f"gradient slices of micro-step {j} generated ({time.time() - t0:.1f}s)")
-        W.update(slices=slices,
-                 master=synth.normal_f32(seed, synth.STREAM_MASTER, S, 0.02, device="cuda"),
-                 exp_avg=torch.zeros(S, dtype=torch.float32, device="cuda"),
-                 exp_avg_sq=torch.zeros(S, dtype=torch.float32, device="cuda"),
-                 grad32=torch.empty(S, dtype=torch.float32, device="cuda"),
+                t = j * world + k
+                slices.append(synth.fill_normal(bufs[t], seed, synth.stream_grad(j, k, world), 1e-3))
+        synth.fill_normal(master, seed, synth.STREAM_MASTER, 0.02)
+        exp_avg.zero_()
+        exp_avg_sq.zero_()
+        W.update(slices=slices, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, grad32=grad32,
                  p16=torch.empty(S, dtype=torch.bfloat16, device="cuda"))
+        log(f"gradient slices and shard state generated ({time.time() - t0:.1f}s)")
 
     def alloc_params():
         params, gathered, outs = [], [], []
@@ -125,6 +150,17 @@ def setup(workload: str, seed: int = 4, order: str = "params_first"):
     log(f"inputs generated on the GPU in {time.time() - t0:.1f}s; "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
     return W
+
+
+def release(W):
+    """Drop every buffer of a setup and return the memory to the device."""
+    import gc
+
+    import torch
+    W.clear()
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def algorithmic_bytes(W) -> dict:
@@ -158,6 +194,71 @@ def run_step(W, step_t, ev=None):
                      lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=step_t)
     if ev:
         ev[4].record()
+
+
+PHASES = ["pack", "unpack", "reduce", "adamw"]
+
+
+def measure_order(W, steps: int, warmup: int) -> dict:
+    """Warm-up steps, then exactly `steps` timed steps (wall time between two
+    device synchronizations, per-phase HIP events on the launch stream), then
+    the fused reduce + AdamW entry point on the same shard."""
+    import torch
+    fs = W["fs"]
+    alg = algorithmic_bytes(W)
+    t = 1
+    for _ in range(warmup):
+        run_step(W, t)
+        t += 1
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        run_step(W, t, evs[k])
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / steps
+    ms = {ph: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i, ph in enumerate(PHASES)}
+    med = {ph: sorted(e[i].elapsed_time(e[i + 1]) for e in evs)[steps // 2] for i, ph in enumerate(PHASES)}
+    kern = {ph: {"ms": round(ms[ph], 4), "ms_median": round(med[ph], 4), "GB": round(alg[ph] / 1e9, 3),
+                 "GBps": round(alg[ph] / (ms[ph] * 1e-3) / 1e9, 1),
+                 "frac_hbm_peak": round(alg[ph] / (ms[ph] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            for ph in PHASES}
+    ra_ms = ms["reduce"] + ms["adamw"]
+    ra_gbps = (alg["reduce"] + alg["adamw"]) / (ra_ms * 1e-3) / 1e9
+    kern["reduce_adamw"] = {"ms": round(ra_ms, 4), "GBps": round(ra_gbps, 1),
+                            "frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4)}
+    fz = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(steps):
+        fz[k][0].record()
+        fs.fs_reduce_adamw_step(W["slices"], W["master"], W["exp_avg"], W["exp_avg_sq"], W["p16"], None,
+                                world=W["world"], grad_acc=W["grad_acc"], lr=1e-3, beta1=0.9, beta2=0.999,
+                                eps=1e-8, weight_decay=0.01, step=t)
+        fz[k][1].record()
+        t += 1
+    torch.cuda.synchronize()
+    fused_ms = sum(e[0].elapsed_time(e[1]) for e in fz) / steps
+    fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
+    kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
+                                  "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                  "step_ms_with_fused": round(ms["pack"] + ms["unpack"] + fused_ms, 4)}
+    step_bytes = sum(alg.values())
+    return {"order": W["order"], "ms_per_step": ms_step, "value": step_bytes / (ms_step * 1e-3) / 1e9,
+            "step_bytes": step_bytes, "alg": alg, "ms": ms, "kernels": kern, "next_t": t}
+
+
+def placement_summary(r: dict) -> dict:
+    k = r["kernels"]
+    return {"ms_per_step": round(r["ms_per_step"], 4), "value_GBps": round(r["value"], 1),
+            "frac_hbm_peak": round(r["value"] / HBM_PEAK_GBPS, 4),
+            "reduce_GBps": k["reduce"]["GBps"], "adamw_GBps": k["adamw"]["GBps"],
+            "pack_GBps": k["pack"]["GBps"], "unpack_GBps": k["unpack"]["GBps"],
+            "reduce_adamw_ms": k["reduce_adamw"]["ms"], "reduce_adamw_frac_hbm_peak": k["reduce_adamw"]["frac_hbm_peak"],
+            "reduce_adamw_fused_ms": k["reduce_adamw_fused"]["ms"],
+            "reduce_adamw_fused_frac_hbm_peak": k["reduce_adamw_fused"]["frac_hbm_peak"]}
 
 
 def _timed(fn, reps):
@@ -263,7 +364,9 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
     gb, th, m, v, pb = (W[k][:sb] for k in ("grad32", "master", "exp_avg", "exp_avg_sq", "p16"))
     ms_r = _timed_graph(lambda: fs.fs_reduce_shard(sl1, gb, N, 1), 4 * reps)
     ms_a = _timed_graph(lambda: fs.fs_adamw_step(th, m, v, gb, pb, lr=1e-3, step=2), 4 * reps)
-    br, ba = (2 * N + 4) * sb, 30 * sb
+    ms_f = _timed_graph(lambda: fs.fs_reduce_adamw_step(sl1, th, m, v, pb, None, world=N, grad_acc=1, step=3),
+                        4 * reps)
+    br, ba, bfz = (2 * N + 4) * sb, 30 * sb, (2 * N + 26) * sb
     # the padding-stress parameter list (97 parameters, 21,444,378 elements, FSDP1
     # with use_orig_params, N = 8): alignment and world pads, short segments
     st = [(n,) for n in synth.padding_stress_numels()]
@@ -282,7 +385,9 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
     out["block_shard_grad_acc_1"] = {
         "shard_numel": sb,
         "reduce": {"us": round(ms_r * 1e3, 1), "GB": round(br / 1e9, 3), "GBps": round(br / (ms_r * 1e-3) / 1e9, 1)},
-        "adamw": {"us": round(ms_a * 1e3, 1), "GB": round(ba / 1e9, 3), "GBps": round(ba / (ms_a * 1e-3) / 1e9, 1)}}
+        "adamw": {"us": round(ms_a * 1e3, 1), "GB": round(ba / 1e9, 3), "GBps": round(ba / (ms_a * 1e-3) / 1e9, 1)},
+        "reduce_adamw_fused": {"us": round(ms_f * 1e3, 1), "GB": round(bfz / 1e9, 3),
+                               "GBps": round(bfz / (ms_f * 1e-3) / 1e9, 1)}}
     return out
 
 
@@ -431,17 +536,105 @@ def copy_ceiling(fs, nbytes=1 << 32, reps=5):
     return 2 * nbytes / (t * 1e-3) / 1e9
 
 
-def cpu_baseline(workload: str, target_s: float = 12.0, seed: int = 4) -> dict:
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    reduce + AdamW over the first n_s shard elements and pack + unpack of one
-    transformer block group, single-threaded, timed with a monotonic clock."""
-    import numpy as np
+
+def measure_70b(reps: int = 3, seed: int = 5) -> dict:
+    """The 70B Llama-style model's rank-0 FSDP2 shard (80 blocks with grouped
+    k/v, N = 8, grad_acc = 2): 8,622,080,000 elements of fp32 theta, m, v and
+    gradient plus the bf16 copy, resident at once (155 GB).  The reduce runs
+    group by group, as FSDP reduces a group at a time, over a slice pool that
+    holds one block group's 16 slices and is reused by every group (each
+    launch still streams its slices from HBM: 3.4 GB against a 256 MB cache);
+    AdamW runs once over the whole shard; the fused reduce + AdamW runs group
+    by group.  Median of `reps` passes each."""
     import torch
+
+    import fsdp_sharded_state_amd as fs
+    import synth
+
+    n_blocks, d, f, kv, vocab, N, A = WORKLOADS["70b"]
+    blk = fs.fs_plan(synth.llama_block_shapes(d, f, kv), "bf16", N, False, "fsdp2", A)
+    root = fs.fs_plan([(vocab, d), (vocab, d)], "bf16", N, False, "fsdp2", A)
+    sizes = [blk.shard_numel] * n_blocks + [root.shard_numel]
+    S, T, Sb = sum(sizes), N * A, max(sizes)
+    t0 = time.time()
+    st = torch.empty(4 * S, dtype=torch.float32, device="cuda")
+    master, m, v, g32 = (st[i * S:(i + 1) * S] for i in range(4))
+    synth.fill_normal(master, seed, synth.STREAM_MASTER, 0.02)
+    m.zero_()
+    v.zero_()
+    p16 = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    pool = torch.empty(T * Sb, dtype=torch.bfloat16, device="cuda")
+    for j in range(A):
+        for k in range(N):
+            t = j * N + k
+            synth.fill_normal(pool[t * Sb:(t + 1) * Sb], seed, synth.stream_grad(j, k, N), 1e-3)
+    torch.cuda.synchronize()
+    log(f"70B shard state ({S} elements) and slice pool generated in {time.time() - t0:.1f}s; "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+    offs = [0]
+    for n in sizes:
+        offs.append(offs[-1] + n)
+    sl = [[pool[t * Sb:t * Sb + n] for t in range(T)] for n in sizes[-2:]]   # block and root views
+    views = [sl[0] if i < n_blocks else sl[1] for i in range(len(sizes))]
+
+    def reduce_all():
+        for i, n in enumerate(sizes):
+            fs.fs_reduce_shard(views[i], g32[offs[i]:offs[i + 1]], N, A)
+
+    def fused_all(step):
+        for i, n in enumerate(sizes):
+            a, b = offs[i], offs[i + 1]
+            fs.fs_reduce_adamw_step(views[i], master[a:b], m[a:b], v[a:b], p16[a:b], None, world=N, grad_acc=A,
+                                    step=step)
+
+    def med(fn):
+        fn(1)
+        torch.cuda.synchronize()
+        ts = []
+        for r in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn(r + 2)
+            e.record()
+            e.synchronize()
+            ts.append(s.elapsed_time(e))
+        return sorted(ts)[len(ts) // 2]
+
+    ms_r = med(lambda step: reduce_all())
+    ms_a = med(lambda step: fs.fs_adamw_step(master, m, v, g32, p16, step=step))
+    ms_f = med(fused_all)
+    br, ba, bf = (2 * N * A + 4) * S, 30 * S, (2 * N * A + 26) * S
+
+    def ent(ms, b, target_ms=None):
+        e = {"ms": round(ms, 3), "GB": round(b / 1e9, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+             "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        if target_ms:
+            e["target_ms_at_80pct"] = target_ms
+        return e
+    out = {"workload": "70B Llama-style model (80 blocks, d 8192, f 28672, k/v 8192x1024, vocab 32000), "
+                       "rank 0's FSDP2 1/8 shard, grad_acc 2",
+           "shard_numel": S, "groups": len(sizes), "launches_per_reduce": len(sizes),
+           "reduce": ent(ms_r, br, round(br / (0.8 * HBM_PEAK_GBPS) / 1e6, 1)),
+           "adamw": ent(ms_a, ba, round(ba / (0.8 * HBM_PEAK_GBPS) / 1e6, 1)),
+           "reduce_adamw": ent(ms_r + ms_a, br + ba),
+           "reduce_adamw_fused": ent(ms_f, bf)}
+    del st, master, m, v, g32, p16, pool, sl, views
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(workload: str = "7b", seed: int = 4, reps: int = 5) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    reduce (32 bf16 slices) + AdamW over the first n_s shard elements, and
+    pack + unpack of one transformer block group.  Timed single-threaded (the
+    build every check uses) and with its OpenMP build on every host core the
+    process may use: one warm-up pass, then `reps` passes, median."""
+    import numpy as np
 
     import oracle
     import synth
 
-    torch.set_num_threads(min(16, os.cpu_count() or 1))
     n_blocks, d, f, kv, vocab, world, grad_acc = WORKLOADS[workload]
     n_s = 1 << 22
     # same generator and streams as the GPU run, evaluated on the GPU for speed
@@ -454,22 +647,31 @@ def cpu_baseline(workload: str, target_s: float = 12.0, seed: int = 4) -> dict:
     nb = int(L.numel.sum())
     prm = [np.frombuffer(np.random.default_rng(k).bytes(2 * int(n)), np.uint16) for k, n in enumerate(L.numel)]
     hp = oracle.AdamWHparams(step=1)
+    sample_bytes = ((2 * world * grad_acc + 4) * n_s + 30 * n_s + (2 * nb + 2 * L.gathered_numel) + 4 * nb)
 
-    total_bytes, total_t, reps = 0, 0.0, 0
-    while total_t < target_s and reps < 20:
+    def one_pass(par):
         t0 = time.perf_counter()
-        g = oracle.reduce_shard(sl, world, grad_acc)
-        oracle.adamw_step(th, z, z, g, hp)
-        gath = oracle.pack(L, prm)
-        oracle.unpack(L, gath)
-        total_t += time.perf_counter() - t0
-        total_bytes += (2 * world * grad_acc + 4) * n_s + 30 * n_s + (2 * nb + 2 * L.gathered_numel) + 4 * nb
-        reps += 1
+        g = oracle.reduce_shard(sl, world, grad_acc, parallel=par)
+        oracle.adamw_step(th, z, z, g, hp, parallel=par)
+        gath = oracle.pack(L, prm, parallel=par)
+        oracle.unpack(L, gath, parallel=par)
+        return time.perf_counter() - t0
+
+    res = {}
+    for par in (False, True):
+        one_pass(par)
+        ts = sorted(one_pass(par) for _ in range(reps))
+        res[par] = (sample_bytes / ts[len(ts) // 2] / 1e9, ts[len(ts) // 2])
+    threads = oracle.threads(True)
     return {
-        "value": total_bytes / total_t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{reps} passes of: reduce ({world * grad_acc} bf16 slices) + AdamW over {n_s} of the "
-                   f"rank-0 shard's elements, pack + unpack of one block group ({nb} params); "
-                   f"{total_t:.1f}s of single-threaded CPU work"),
+        "value": res[True][0], "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "value_1t": res[False][0], "value_all_cores": res[True][0],
+        "host_cpu_count": os.cpu_count(),
+        "sample": (f"reduce ({world * grad_acc} bf16 slices) + AdamW over {n_s} of the rank-0 shard's elements, "
+                   f"pack + unpack of one block group ({nb} params): {sample_bytes / 1e9:.2f} GB of algorithmic "
+                   f"traffic per pass; median of {reps} passes after one warm-up: "
+                   f"{res[False][1]:.2f} s single-threaded, {res[True][1]:.3f} s on {threads} threads "
+                   f"(OpenMP build of the same source)"),
     }
 
 
@@ -492,7 +694,7 @@ KERNELS = {  # rocprofv3 kernel-name fragment -> bench phase
     "reduce_rs_chunk_kernel": "reduce_bf16_reduce_dtype",
     "pack_cast_kernel": "pack_cast",
     "reduce_adamw_chunk_kernel": "reduce_adamw_fused",
-    "adamw_wave_kernel": "adamw",
+    "adamw_kernel": "adamw",
     "scatter_kernel<2, (anonymous namespace)::PackSrc": "pack",
     "unpack_kernel": "unpack",
     "copy_kernel": "copy",
@@ -540,11 +742,10 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     f_write = copy_bytes / (avg["copy_kernel"]["WRITE_SIZE"] * 1024)
     # algorithmic bytes per launch of the 7B shard step
     S, N, A = 842301440, 8, 4
-    alg = {"reduce_chunk_kernel<16>": (2 * N * A + 4) * S, "adamw_wave_kernel": 30 * S,
+    alg = {"reduce_chunk_kernel<16>": (2 * N * A + 4) * S, "adamw_kernel": 30 * S,
            "reduce_adamw_chunk_kernel": (2 * N * A + 26) * S,
            "reduce_rs_chunk_kernel": (2 * N * A + 4) * S,
            "copy_kernel": 2 * copy_bytes}
-    P_blk = 202383360
     for k in KERNELS:
         alg.setdefault(k, None)   # pack / unpack / reshard: per group, reported as means below
     rec = {"kernel_source_sha256_16": kernel_source_hash(), "fetch_scale": f_fetch, "write_scale": f_write,
@@ -573,9 +774,9 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     md += ["", "then `python bench.py --rocprof-summary <trace dir> <FETCH_SIZE dir> <WRITE_SIZE dir>`.", "",
            f"Counter scale (bytes per counted byte, from the 4 GiB copy kernel): FETCH_SIZE x{f_fetch:.4f}, "
            f"WRITE_SIZE x{f_write:.4f}.", "",
-           "Kernel rates move by up to about 8% between processes running the same code, with the",
+           "Kernel rates move by up to about 10% between allocations running the same code, with the",
            "physical placement of the buffers; compare the trace with the bench line of the same run",
-           "(at the end), not with another run's.", "",
+           "(at the end, one allocation order), not with another run's.", "",
            "| kernel | calls | avg duration | HBM read / launch | HBM write / launch | algorithmic / launch | HBM / alg | alg GB/s (trace) |",
            "|---|---|---|---|---|---|---|---|"]
     for k, st, fe, wr, a in rows:
@@ -609,9 +810,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--orders", default=",".join(ORDERS),
+                    help="comma-separated allocation orders to set up and time, each from an emptied allocator "
+                         f"(default: all of {', '.join(ORDERS)})")
+    ap.add_argument("--separate", action="store_true",
+                    help="allocate every gradient slice and every shard-state array on its own instead of "
+                         "one buffer for the slices and one for theta, m, v and the gradient")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-70b", action="store_true", help="skip the 70B shard measurement")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the tiny launch-bound step, the one-block, padding-stress and FSDP1 "
                          "measurements (their launches would mix into a per-kernel profile of the 7B step)")
@@ -620,90 +826,73 @@ def main():
         print(json.dumps({"error": "this engine runs all N logical ranks on one GPU; "
                                    "--gpus above 1 is not supported", "n_gpus": args.gpus}))
         sys.exit(2)
+    orders = [o for o in args.orders.split(",") if o]
+    for o in orders:
+        if o not in ORDERS:
+            sys.exit(f"unknown allocation order {o!r}; choose from {', '.join(ORDERS)}")
 
     import torch
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
-    W = setup(args.workload)
-    fs = W["fs"]
-    alg = algorithmic_bytes(W)
-    step_bytes = sum(alg.values())
+    import fsdp_sharded_state_amd as fs
 
-    t = 1
-    for _ in range(args.warmup):
-        run_step(W, t)
-        t += 1
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        run_step(W, t, evs[k])
-        t += 1
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
-    phases = ["pack", "unpack", "reduce", "adamw"]
-    ms = {ph: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, ph in enumerate(phases)}
-    med = {ph: sorted(e[i].elapsed_time(e[i + 1]) for e in evs)[args.steps // 2] for i, ph in enumerate(phases)}
-    kern = {ph: {"ms": round(ms[ph], 4), "ms_median": round(med[ph], 4), "GB": round(alg[ph] / 1e9, 3),
-                 "GBps": round(alg[ph] / (ms[ph] * 1e-3) / 1e9, 1),
-                 "frac_hbm_peak": round(alg[ph] / (ms[ph] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-            for ph in phases}
-    ra_ms = ms["reduce"] + ms["adamw"]
-    ra_gbps = (alg["reduce"] + alg["adamw"]) / (ra_ms * 1e-3) / 1e9
-    kern["reduce_adamw"] = {"ms": round(ra_ms, 4), "GBps": round(ra_gbps, 1),
-                            "frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4)}
-    # the fused reduce + AdamW entry point on the same shard (timed separately;
-    # the headline step above is the two-kernel path)
-    fz = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        fz[k][0].record()
-        fs.fs_reduce_adamw_step(W["slices"], W["master"], W["exp_avg"], W["exp_avg_sq"], W["p16"], None,
-                                world=W["world"], grad_acc=W["grad_acc"], lr=1e-3, beta1=0.9, beta2=0.999,
-                                eps=1e-8, weight_decay=0.01, step=t)
-        fz[k][1].record()
-        t += 1
-    torch.cuda.synchronize()
-    fused_ms = sum(e[0].elapsed_time(e[1]) for e in fz) / args.steps
-    fused_bytes = (2 * W["world"] * W["grad_acc"] + 26) * W["S"]
-    extra = extra_measurements(W, args.steps, small=not args.no_small)
+    runs, extra, own, mixes = [], None, None, None
+    for i, order in enumerate(orders):
+        W = setup("7b", order=order, pooled=not args.separate)
+        r = measure_order(W, args.steps, args.warmup)
+        log(f"order {order}: {r['ms_per_step']:.3f} ms per step, {r['value']:.0f} GB/s; reduce "
+            f"{r['kernels']['reduce']['GBps']:.0f}, adamw {r['kernels']['adamw']['GBps']:.0f}, fused "
+            f"{r['kernels']['reduce_adamw_fused']['ms']:.3f} ms")
+        if i == 0:
+            # the engine's other entry points and the streaming ceilings of
+            # the kernels' own buffers, on the first order's placement
+            extra = extra_measurements(W, args.steps, small=not args.no_small)
+            own = own_buffer_ceilings(W)      # last on this setup: it overwrites the shard state
+            P, S, N, A = W["P"], W["S"], W["world"], W["grad_acc"]
+            gath = sum(p.gathered_numel for p in W["plans"])
+            mixes = {"pack": (2 * P, 2 * gath), "unpack": (2 * P, 2 * P), "reduce": (2 * N * A * S, 4 * S),
+                     "adamw": (16 * S, 14 * S), "reduce_adamw_fused": ((2 * N * A + 12) * S, 14 * S),
+                     "reduce_bf16_reduce_dtype": (2 * N * A * S, 4 * S),
+                     "pack_cast_fp32_to_bf16": (4 * P, 2 * gath),
+                     "reshard_n_to_half_n": (2 * P, extra["reshard_n_to_half_n"]["GB"] * 1e9 - 2 * P)}
+            cfg = {"params": W["P"], "shard_numel": W["S"], "world": W["world"], "grad_acc": W["grad_acc"],
+                   "groups": W["groups"]}
+        runs.append(r)
+        release(W)
+        del W
     ceiling = copy_ceiling(fs)
     streams = stream_ceilings(fs)
     tiny = None if args.no_small else tiny_step_latency(fs)
+    big = None if args.no_70b else measure_70b()
 
-    kern["reduce_adamw_fused"] = {"ms": round(fused_ms, 4), "GB": round(fused_bytes / 1e9, 3),
-                                  "GBps": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
-                                  "frac_hbm_peak": round(fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                                  "step_ms_with_fused": round(ms["pack"] + ms["unpack"] + fused_ms, 4)}
+    # headline: the allocation order with the median step time
+    ranked = sorted(runs, key=lambda r: r["ms_per_step"])
+    head = ranked[len(ranked) // 2]
+    worst = ranked[-1]
+    kern = dict(head["kernels"])
     kern.update(extra)
-    # each kernel against the streaming rate of its own read/write mix
-    P, S, N, A = W["P"], W["S"], W["world"], W["grad_acc"]
-    gath = sum(p.gathered_numel for p in W["plans"])
-    rw = {"pack": (2 * P, 2 * gath), "unpack": (2 * P, 2 * P), "reduce": (2 * N * A * S, 4 * S),
-          "adamw": (16 * S, 14 * S), "reduce_adamw_fused": ((2 * N * A + 12) * S, 14 * S),
-          "reduce_bf16_reduce_dtype": (2 * N * A * S, 4 * S), "pack_cast_fp32_to_bf16": (4 * P, 2 * gath),
-          "reshard_n_to_half_n": (2 * P, kern["reshard_n_to_half_n"]["GB"] * 1e9 - 2 * P)}
-    for k, (r, w) in rw.items():
-        c = mix_ceiling(r, w, streams)
-        kern[k]["frac_of_copy_ceiling"] = round(kern[k]["GBps"] / ceiling, 4)
-        kern[k]["mix_ceiling_GBps"] = round(c, 1)
-        kern[k]["frac_of_mix_ceiling"] = round(kern[k]["GBps"] / c, 4)
-    own = own_buffer_ceilings(W)      # last: it overwrites the shard state
+    for k, (rb, wb) in mixes.items():
+        c = mix_ceiling(rb, wb, streams)
+        if k in kern:
+            kern[k]["frac_of_copy_ceiling"] = round(kern[k]["GBps"] / ceiling, 4)
+            kern[k]["mix_ceiling_GBps"] = round(c, 1)
+            kern[k]["frac_of_mix_ceiling"] = round(kern[k]["GBps"] / c, 4)
     for k, v in own.items():
-        kern[k]["own_buffers"] = dict(v, frac=round(kern[k]["GBps"] / v["ceiling_GBps"], 4))
-    red_gbps = alg["reduce"] / (ms["reduce"] * 1e-3) / 1e9
+        kern[k]["own_buffers"] = dict(v, note=f"measured on the {runs[0]['order']} placement")
+    if big is not None:
+        kern["config5_70b"] = big
+    alg = head["alg"]
+    red_gbps = alg["reduce"] / (head["ms"]["reduce"] * 1e-3) / 1e9
     traffic = traffic_for("reduce", alg["reduce"])
+    ra = [r["kernels"]["reduce_adamw"]["frac_hbm_peak"] for r in runs]
     out = {
         "metric": "sharded AdamW+reduce step GB/s and % HBM peak; pack/unpack GB/s (7B, N=8)",
-        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "value": round(head["value"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -711,13 +900,19 @@ def main():
         "dtype_detail": {"pack/unpack": "bf16 bit copy", "reduce": "fp32 accumulate",
                          "adamw": "f64 math on fp32 state, bf16 copy"},
         "data": "synthetic",
-        "config": {"workload": ("7B Llama-style model, rank 0's FSDP2 1/8 shard: pack + unpack of all 33 groups, "
-                                "reduce of 4x8 bf16 gradient slices, AdamW"),
-                   "params": W["P"], "shard_numel": W["S"], "world": W["world"], "grad_acc": W["grad_acc"],
-                   "groups": W["groups"], "step_bytes": step_bytes},
+        "config": dict({"workload": ("7B Llama-style model, rank 0's FSDP2 1/8 shard: pack + unpack of all 33 "
+                                     "groups, reduce of 4x8 bf16 gradient slices, AdamW"),
+                        "allocation_order": head["order"], "orders_timed": orders,
+                        "state_buffers": "per array" if args.separate else "pooled",
+                        "headline": "the allocation order with the median step time",
+                        "step_bytes": head["step_bytes"]}, **cfg),
         "kernels": kern,
-        "reduce_adamw_GBps": round(ra_gbps, 1),
-        "reduce_adamw_frac_hbm_peak": round(ra_gbps / HBM_PEAK_GBPS, 4),
+        "placements": {r["order"]: placement_summary(r) for r in runs},
+        "value_worst_order": round(worst["value"], 1),
+        "reduce_adamw_GBps": kern["reduce_adamw"]["GBps"],
+        "reduce_adamw_frac_hbm_peak": kern["reduce_adamw"]["frac_hbm_peak"],
+        "reduce_adamw_frac_hbm_peak_worst": min(ra),
+        "reduce_adamw_frac_hbm_peak_median": statistics.median(ra),
         "copy_ceiling_GBps": round(ceiling, 1),
         "stream_ceilings_GBps": {k: round(v, 1) for k, v in streams.items()},
         "tiny_mlp_step": tiny,
@@ -726,11 +921,9 @@ def main():
                      "traffic": traffic, "alg_bytes_per_launch": alg["reduce"]},
         "cpu_baseline": None,
     }
-    del W
-    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 
