@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
     L.fs_reshard_destroy.restype = None
     L.fs_reduce_shard_ex.argtypes = [i64, i32, i32, i32, vp, vp, vp]
     L.fs_pack_cast.argtypes = [vp, vp, i32, vp, i32, vp]
+    L.fs_load_local.argtypes = [vp, i32, vp, vp, vp]
     L.fs_reduce_adamw_step.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamWHparams), vp]
     L.fs_copy_bytes.argtypes = [vp, vp, i64, vp]
     L.fs_stream_read.argtypes = [vp, i64, vp, vp]
@@ -108,7 +109,7 @@ def lib() -> ctypes.CDLL:
     for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
                  "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_reduce_adamw_step",
                  "fs_reduce_shard_ex", "fs_pack_cast", "fs_reshard_plan", "fs_reshard_info",
-                 "fs_reshard_upload", "fs_reshard",
+                 "fs_reshard_upload", "fs_reshard", "fs_load_local",
                  "fs_copy_bytes", "fs_stream_read", "fs_stream_fill"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -161,6 +162,8 @@ class Plan:
         self.info = info
         self.workspace: Optional[torch.Tensor] = None
         self._ptr_cache = {}
+        self._pinned = set()        # pointer-table keys a captured graph or another stream may still read
+        self._pieces = {}           # rank -> local piece element counts
         self.numels = [self.param(i).numel for i in range(info.n_params)]
         self.shapes: Optional[List[tuple]] = None   # set by fs_plan()
 
@@ -230,20 +233,31 @@ class Plan:
             views.append(v.view((ln // row,) + tail) if fsdp2 and row else v)
         return views
 
-    def load_local(self, shard: torch.Tensor, rank: int, tensors: Sequence[torch.Tensor]):
-        """Import a sharded state dict: zero `shard` (pads stay zero) and copy
-        each parameter's local tensor (shaped as local_views returns it)
-        into its place."""
-        views = self.local_views(shard, rank)
-        if len(tensors) != len(views):
-            raise ValueError(f"expected {len(views)} local tensors, got {len(tensors)}")
-        for i, (v, t) in enumerate(zip(views, tensors)):
-            if t.numel() != v.numel():
-                raise ValueError(f"local tensor {i}: {t.numel()} elements, rank {rank} holds {v.numel()}")
-        shard.zero_()
-        for v, t in zip(views, tensors):
-            if v.numel():
-                v.copy_(t.reshape(v.shape))
+    def local_numels(self, rank: int) -> List[int]:
+        """Element count of every parameter's local piece on `rank`."""
+        if rank not in self._pieces:
+            self._pieces[rank] = [0 if pc is None else pc[2] for pc in self.local_pieces(rank)]
+        return self._pieces[rank]
+
+    def load_local(self, shard: torch.Tensor, rank: int, tensors: Sequence[torch.Tensor], stream=None):
+        """Import a sharded state dict (fs_load_local): write each parameter's
+        local tensor (shaped as local_views returns it, or flat) into its place
+        in `shard` (that rank's shard buffer on the GPU) and zero the pads."""
+        if not 0 <= rank < self.info.world:
+            raise ValueError(f"rank {rank} out of range [0, {self.info.world})")
+        if shard.dim() != 1 or shard.numel() != self.info.shard_numel:
+            raise ValueError(f"shard must be 1-D with {self.info.shard_numel} elements")
+        if shard.element_size() != self.info.elem_bytes:
+            raise ValueError(f"shard element size {shard.element_size()} != plan's {self.info.elem_bytes}")
+        want = self.local_numels(rank)
+        if len(tensors) != len(want):
+            raise ValueError(f"expected {len(want)} local tensors, got {len(tensors)}")
+        for i, (t, n) in enumerate(zip(tensors, want)):
+            if t.numel() != n:
+                raise ValueError(f"local tensor {i}: {t.numel()} elements, rank {rank} holds {n}")
+        tab = self.ptr_table(tensors, "local tensors", numels=want, stream=stream)
+        _check(lib().fs_load_local(self._h, int(rank), tab.data_ptr(),
+                                   _dev_ptr(shard, "shard") if shard.numel() else 0, _stream(stream)))
 
     def upload(self, device="cuda", stream=None) -> "Plan":
         ws = torch.empty(max(16, self.info.workspace_bytes), dtype=torch.uint8, device=device)
@@ -251,28 +265,54 @@ class Plan:
         self.workspace = ws
         return self
 
-    def ptr_table(self, tensors: Sequence[torch.Tensor], what: str, elem_bytes: Optional[int] = None) -> torch.Tensor:
+    def ptr_table(self, tensors: Sequence[torch.Tensor], what: str, elem_bytes: Optional[int] = None,
+                  numels: Optional[Sequence[int]] = None, stream=None) -> torch.Tensor:
         """Device array of the tensors' data pointers (cached per pointer set).
-        Every tensor must hold its parameter's element count, with elements of
-        `elem_bytes` bytes (default: the plan's)."""
+        Every tensor must hold `numels[i]` elements (default: its parameter's
+        element count) of `elem_bytes` bytes (default: the plan's).
+
+        The kernels read the table when they run, not when they are enqueued,
+        so a table must outlive every launch that uses it.  A few recent sets
+        are kept; the oldest is released when a new one is made, which is safe
+        for launches on the current stream (the allocator reuses its memory in
+        stream order).  A table used while a graph is being captured, or with
+        a stream given as a raw handle, is pinned for the plan's lifetime; one
+        used on another torch stream is recorded on that stream.  A new set
+        cannot be made during capture (its upload would be a captured copy
+        from host memory): run the call once before capturing."""
         if len(tensors) != self.info.n_params:
             raise ValueError(f"{what}: expected {self.info.n_params} tensors, got {len(tensors)}")
         esz = self.info.elem_bytes if elem_bytes is None else elem_bytes
+        want = self.numels if numels is None else numels
         ptrs = []
         for i, t in enumerate(tensors):
             if t.element_size() != esz:
                 raise ValueError(f"{what}[{i}]: element size {t.element_size()} != {esz}")
-            if t.numel() != self.numels[i]:
-                raise ValueError(f"{what}[{i}]: numel {t.numel()} != {self.numels[i]}")
+            if t.numel() != want[i]:
+                raise ValueError(f"{what}[{i}]: numel {t.numel()} != {want[i]}")
             ptrs.append(_dev_ptr(t, f"{what}[{i}]") if t.numel() else 0)
         key = (tuple(ptrs), str(tensors[0].device) if tensors else "")
+        capturing = torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
         tab = self._ptr_cache.get(key)
         if tab is None:
+            if capturing:
+                raise RuntimeError(f"{what}: a pointer set not seen before, during graph capture; run the same "
+                                   "call once before capturing so that its device pointer table exists")
             dev = tensors[0].device if tensors else torch.device("cuda")
             tab = torch.tensor(ptrs or [0], dtype=torch.int64, device=dev)
             if len(self._ptr_cache) >= 8:          # keep a few pointer sets (pack and unpack sides)
-                self._ptr_cache.pop(next(iter(self._ptr_cache)))
+                old = next((k for k in self._ptr_cache if k not in self._pinned), None)
+                if old is not None:
+                    self._ptr_cache.pop(old)
             self._ptr_cache[key] = tab
+        if capturing:
+            self._pinned.add(key)
+        if stream is not None:
+            if isinstance(stream, torch.cuda.Stream):
+                if stream != torch.cuda.current_stream(tab.device):
+                    tab.record_stream(stream)
+            else:
+                self._pinned.add(key)
         return tab
 
 
@@ -339,7 +379,7 @@ def fs_pack(plan: Plan, params: Sequence[torch.Tensor], out: torch.Tensor, rank:
     want = plan.info.gathered_numel if rank < 0 else plan.info.shard_numel
     if out.numel() != want or out.element_size() != plan.info.elem_bytes:
         raise ValueError(f"fs_pack: out must hold {want} elements of {plan.info.elem_bytes} bytes")
-    tab = plan.ptr_table(params, "params")
+    tab = plan.ptr_table(params, "params", stream=stream)
     _check(lib().fs_pack(plan._h, tab.data_ptr(), _dev_ptr(out, "out") if want else 0, int(rank), _stream(stream)))
 
 
@@ -354,7 +394,7 @@ def fs_pack_cast(plan: Plan, params: Sequence[torch.Tensor], out: torch.Tensor, 
     dt = params[0].dtype
     if any(p.dtype != dt for p in params):
         raise ValueError("fs_pack_cast: parameters must share one dtype")
-    tab = plan.ptr_table(params, "params", elem_bytes=params[0].element_size())
+    tab = plan.ptr_table(params, "params", elem_bytes=params[0].element_size(), stream=stream)
     _check(lib().fs_pack_cast(plan._h, tab.data_ptr(), _dtype_code(dt), _dev_ptr(out, "out") if want else 0,
                               int(rank), _stream(stream)))
 
@@ -363,7 +403,7 @@ def fs_unpack(plan: Plan, gathered: torch.Tensor, params: Sequence[torch.Tensor]
     """All-gather copy-out: gathered -> params."""
     if gathered.numel() != plan.info.gathered_numel or gathered.element_size() != plan.info.elem_bytes:
         raise ValueError("fs_unpack: gathered has the wrong size or element size")
-    tab = plan.ptr_table(params, "params")
+    tab = plan.ptr_table(params, "params", stream=stream)
     _check(lib().fs_unpack(plan._h, _dev_ptr(gathered, "gathered") if gathered.numel() else 0,
                            tab.data_ptr(), _stream(stream)))
 

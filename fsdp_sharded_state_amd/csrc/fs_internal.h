@@ -68,6 +68,7 @@ struct WorkspaceLayout {
     int64_t pack_tiles_rank, n_pack_tiles_rank;    // N grids over [r*shard, (r+1)*shard), anchored at r*shard
     int64_t unpack_tiles, n_unpack_tiles;
     int64_t bufinfo, n_bufinfo;
+    int64_t local_first, n_local_first;            // [N][n_params]: first parameter element of each rank's run
     int64_t total_bytes;
 };
 

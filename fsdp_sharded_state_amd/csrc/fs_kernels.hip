@@ -22,6 +22,7 @@
 #include <algorithm>
 
 #include "fs_plan_impl.h"
+#include "../../include/fs_bench.h"
 
 using fsi::BufInfo;
 using fsi::Segment;
@@ -140,6 +141,18 @@ struct PackSrc {
 struct UnpackSrc {
     const char *gathered;
     __device__ __forceinline__ const char *operator()(int) const { return gathered; }
+};
+// State-dict import: parameter `buf`'s elements come from the rank's local
+// piece of it, which starts at the parameter element first[buf].  The base
+// is shifted back by that many elements so the segments' parameter offsets
+// index the piece; only offsets inside the piece are ever read.
+template <int W>
+struct LocalSrc {
+    const void *const *pieces;
+    const int64_t *first;
+    __device__ __forceinline__ const char *operator()(int buf) const {
+        return reinterpret_cast<const char *>(pieces[buf]) - first[buf] * W;
+    }
 };
 
 // Assemble the 16-byte block of virtual elements [x0, x0+VEC) from the
@@ -1202,6 +1215,7 @@ extern "C" int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hip
         {w.pack_tiles_rank, plan->pack_tiles_rank.data(), w.n_pack_tiles_rank * (int64_t)sizeof(Tile)},
         {w.unpack_tiles, plan->unpack_tiles.data(), w.n_unpack_tiles * (int64_t)sizeof(Tile)},
         {w.bufinfo, plan->bufinfo.data(), w.n_bufinfo * (int64_t)sizeof(BufInfo)},
+        {w.local_first, plan->local_first.data(), w.n_local_first * (int64_t)sizeof(int64_t)},
     };
     for (const Part &p : parts) {
         if (p.bytes == 0) continue;
@@ -1252,6 +1266,37 @@ extern "C" int fs_pack(fs_plan_t plan, const void *const *params, void *out, int
         hipLaunchKernelGGL((scatter_kernel<4, PackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
                            tiles, src, base, lo, hi);
     return check_launch("fs_pack");
+}
+
+extern "C" int fs_load_local(fs_plan_t plan, int32_t rank, const void *const *pieces, void *shard,
+                             hipStream_t stream) {
+    fsi::clear_error();
+    if (!plan) return fsi::fail(FS_E_INVAL, "fs_load_local: plan is NULL");
+    const fs_plan_info_t &I = plan->info;
+    if (!plan->dev_ws) return fsi::fail(FS_E_INVAL, "fs_load_local: plan has no uploaded workspace (call fs_plan_upload)");
+    if (int rc = check_device("fs_load_local", plan->dev_id)) return rc;
+    if (rank < 0 || rank >= I.world) return fsi::fail(FS_E_INVAL, "fs_load_local: rank %d out of range [0, %d)", rank, I.world);
+    if (I.shard_numel == 0) return FS_OK;
+    if (!shard) return fsi::fail(FS_E_INVAL, "fs_load_local: shard is NULL");
+    if (I.n_params > 0 && !pieces) return fsi::fail(FS_E_INVAL, "fs_load_local: pieces is NULL");
+    if (misaligned(shard, I.elem_bytes))
+        return fsi::fail(FS_E_ALIGN, "fs_load_local: shard not aligned to %d bytes", I.elem_bytes);
+    const char *ws = static_cast<const char *>(plan->dev_ws);
+    const Segment *segs = reinterpret_cast<const Segment *>(ws + plan->ws.pack_segs);
+    const Tile *tiles = reinterpret_cast<const Tile *>(ws + plan->ws.pack_tiles_rank) + plan->rank_tile_off[rank];
+    const int64_t ntiles = plan->rank_tile_off[rank + 1] - plan->rank_tile_off[rank];
+    if (ntiles == 0) return FS_OK;
+    const int64_t *first = reinterpret_cast<const int64_t *>(ws + plan->ws.local_first) + (int64_t)rank * I.n_params;
+    const int64_t lo = (int64_t)rank * I.shard_numel, hi = lo + I.shard_numel;
+    (void)hipGetLastError();
+    char *out = static_cast<char *>(shard);   // addressed from the virtual element lo
+    if (I.elem_bytes == 2)
+        hipLaunchKernelGGL((scatter_kernel<2, LocalSrc<2>>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+                           tiles, LocalSrc<2>{pieces, first}, out, lo, hi);
+    else
+        hipLaunchKernelGGL((scatter_kernel<4, LocalSrc<4>>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+                           tiles, LocalSrc<4>{pieces, first}, out, lo, hi);
+    return check_launch("fs_load_local");
 }
 
 extern "C" int fs_reshard_upload(fs_reshard_t r, void *workspace, size_t bytes, hipStream_t stream) {

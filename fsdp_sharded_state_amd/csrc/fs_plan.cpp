@@ -247,6 +247,12 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
             delete p;
             return fsi::fail(FS_E_OVERFLOW, "fs_plan: too many copy segments");
         }
+        // A parameter's elements on one rank form one run in both layouts
+        // (FSDP1 cuts the flat at rank boundaries, FSDP2 gives each rank one
+        // dim-0 chunk), so the rank's local piece of parameter i starts at the
+        // run's first parameter element: the state-dict import reads it there.
+        p->local_first.assign((size_t)world * (size_t)n_params, 0);
+        for (const Segment &sg : ps) p->local_first[(size_t)sg.rank * (size_t)n_params + (size_t)sg.buf] = sg.src_off;
 
         // ---- unpack view: parameters laid end to end on 16-byte boundaries
         p->bufinfo.resize(n_params);
@@ -301,6 +307,7 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
         }
         place((int64_t)p->unpack_tiles.size(), sizeof(Tile), &w.unpack_tiles, &w.n_unpack_tiles);
         place((int64_t)p->bufinfo.size(), sizeof(fsi::BufInfo), &w.bufinfo, &w.n_bufinfo);
+        place((int64_t)p->local_first.size(), sizeof(int64_t), &w.local_first, &w.n_local_first);
         w.total_bytes = std::max<int64_t>(off, 256);
 
         // ---- summary and ledger

@@ -20,6 +20,7 @@ struct fs_plan_s {
     std::vector<int64_t> rank_tile_off;        // N+1 offsets into pack_tiles_rank
     std::vector<fsi::Tile> unpack_tiles;
     std::vector<fsi::BufInfo> bufinfo;
+    std::vector<int64_t> local_first;          // [N][n_params]: src_off of parameter i's run on rank r (0 if none)
     fsi::WorkspaceLayout ws;
     void *dev_ws = nullptr;                    // bound by fs_plan_upload
     int dev_id = -1;                           // device of dev_ws

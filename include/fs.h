@@ -24,9 +24,13 @@
  *     is the fast path.
  *   - Work is issued asynchronously on `stream` (NULL = the null stream) as
  *     kernel launches only -- no copies, allocations or waits -- so the calls
- *     can be captured into a HIP graph.  A call launches its main kernel and
- *     at most one more for a ragged tail or a misaligned remainder; the
- *     reduces do so once per pass of up to 32 terms.
+ *     can be captured into a HIP graph.  A call launches one kernel; the
+ *     reduces launch one per pass of up to 32 terms.
+ *   - fs_plan_info, fs_plan_param, fs_plan_segments, fs_plan_upload,
+ *     fs_plan_destroy, the fs_reshard_info/upload/destroy calls and
+ *     fs_last_error are infrastructure around the method's steps (reading a
+ *     plan back, placing its tables in device memory, reporting errors); no
+ *     passage of the pages defines them.
  *   - Inputs and outputs must not overlap, except the in-place AdamW state.
  *   - Errors are reported by return code (fs_status); the call then has
  *     launched nothing.  fs_last_error() describes the last failure of the
@@ -259,6 +263,31 @@ int fs_reshard(fs_reshard_t r, const void *src_gathered, void *dst_gathered, hip
 void fs_reshard_destroy(fs_reshard_t r);
 
 /*
+ * fs_load_local -- import rank `rank`'s part of a sharded state dict into its
+ * shard buffer [FvF, memory and engineering section: FSDP2's shards are the
+ * sharded state dict, saved and loaded per rank without communication; the
+ * FSDP tutorial page (m.xxqk.cn), section 3.3: sharded checkpoints are
+ * loaded rank by rank].  The inverse of viewing a shard's local pieces: with
+ * the plan's fp32 twin the same call restores master, m or v.
+ *
+ *   rank            0 <= rank < N.
+ *   pieces (device) array of n_params device pointers; entry i points to the
+ *                   rank's local piece of parameter i: the run of its
+ *                   elements that fs_plan_segments lists on this rank (FSDP2:
+ *                   the rank's torch.chunk dim-0 chunk; FSDP1: the flattened
+ *                   parameter's elements inside the rank's flat shard), in
+ *                   element order, contiguous, aligned to the element size.
+ *                   Entries of parameters the rank holds none of are not read.
+ *   shard  (device) shard_numel elements of the plan's dtype; every element
+ *                   that no piece covers (a pad) is written as zero.
+ * Same kernels and tables as fs_pack with rank = r.
+ * Errors: FS_E_INVAL (plan not uploaded, rank out of range, NULL pointers),
+ * FS_E_ALIGN (shard not aligned to the element size), FS_E_HIP.
+ */
+int fs_load_local(fs_plan_t plan, int32_t rank, const void *const *pieces, void *shard,
+                  hipStream_t stream);
+
+/*
  * fs_reduce_shard -- this rank's averaged fp32 gradient shard [DPZ section
  * 2.1: sum the ranks' gradients, then divide by N; DPZ sections 1 and 9.2:
  * fp32 accumulation over micro-steps on the own shard; DPZ section 5: the
@@ -368,28 +397,6 @@ int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc,
                          float *exp_avg, float *exp_avg_sq, uint16_t *param_bf16,
                          float *grad_out, const fs_adamw_hparams_t *hp,
                          hipStream_t stream);
-
-/*
- * fs_copy_bytes -- plain streaming copy of `bytes` bytes (dst, src device,
- * both 16-byte aligned, bytes a multiple of 16).  A measurement aid, not
- * part of the method: it gives the practical copy ceiling of the HBM and the
- * scale of the hardware traffic counters for a kernel of known traffic.
- * Errors: FS_E_INVAL, FS_E_ALIGN, FS_E_HIP.
- */
-int fs_copy_bytes(void *dst, const void *src, int64_t bytes, hipStream_t stream);
-
-/*
- * fs_stream_read / fs_stream_fill -- measurement aids beside fs_copy_bytes,
- * not part of the method: the HBM read-only and write-only streaming rates
- * that, with the copy rate, bound each kernel's read/write mix.
- * fs_stream_read reads `bytes` bytes at src and discards them; sink (device,
- * 4 bytes) may receive an unspecified value.  fs_stream_fill writes the
- * 32-bit `value` over `bytes` bytes at dst.  Pointers 16-byte aligned (sink
- * 4-byte), bytes a multiple of 16.  Errors: FS_E_INVAL, FS_E_ALIGN,
- * FS_E_OVERFLOW, FS_E_HIP.
- */
-int fs_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
-int fs_stream_fill(void *dst, int64_t bytes, uint32_t value, hipStream_t stream);
 
 /* fs_last_error -- message for the calling thread's last failed call
  * (empty string if none).  The pointer stays valid until the next call. */

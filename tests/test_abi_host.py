@@ -1,6 +1,6 @@
 """Host-side checks of the C-ABI library (no GPU call is made).
 
-* libfsstate.so loads and exports every function include/fs.h declares;
+* libfsstate.so loads and exports every function include/*.h declares;
 * the planner (fs_plan) lays out exactly what the oracle lays out, on the
   exhaustive tiny cases and on the workload shapes;
 * the ledger fields equal the oracle's ledger;
@@ -23,9 +23,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_exports_every_declared_symbol():
-    hdr = open(os.path.join(ROOT, "include", "fs.h")).read()
-    names = set(re.findall(r"^\s*(?:int|void|const char\s*\*)\s*\*?\s*(fs_\w+)\s*\(", hdr, re.M))
-    assert {"fs_plan", "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step"} <= names
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            hdr = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:int|void|const char\s*\*)\s*\*?\s*(fs_\w+)\s*\(", hdr, re.M))
+    assert {"fs_plan", "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_load_local",
+            "fs_copy_bytes", "fs_stream_read", "fs_stream_fill"} <= names
     L = ctypes.CDLL(fs.LIB_PATH)
     missing = [n for n in sorted(names) if not hasattr(L, n)]
     assert not missing, missing

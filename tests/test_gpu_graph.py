@@ -143,3 +143,46 @@ def test_graph_replay_matches_eager(case):
         other.run(t + rep)
         torch.cuda.synchronize()
     del g
+
+
+def test_captured_pointer_table_outlives_later_pointer_sets(monkeypatch):
+    """A captured graph holds the device address of the plan's pointer table
+    for its parameters.  Ten other pointer sets going through the same plan
+    afterwards (more than the cache keeps) must not release that table: the
+    replay still packs the right parameters and the table keeps its address.
+    A pointer set first seen during capture is refused (its upload would be
+    a captured copy from host memory)."""
+    say("graph: pinned pointer table")
+    shapes, N = synth.llama_block_shapes(256, 688), 8
+    plan = fs.fs_plan(shapes, "bf16", N, False, "fsdp2").upload()
+    params, off = [], 0
+    for s in shapes:
+        n = int(np.prod(s))
+        params.append(synth.normal_bf16(3, synth.STREAM_PARAMS, n, 0.02, device="cuda", start=off))
+        off += n
+    out = torch.empty(plan.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    fs.fs_pack(plan, params, out)            # eager call: makes the table
+    torch.cuda.synchronize()
+    ref = out.clone()
+    addr = plan.ptr_table(params, "params").data_ptr()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fs.fs_pack(plan, params, out)
+    scratch = torch.empty_like(out)
+    for k in range(10):
+        others = [p.clone() for p in params]
+        fs.fs_pack(plan, others, scratch)
+        del others
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+    assert plan.ptr_table(params, "params").data_ptr() == addr
+    del g
+    fresh = [p.clone() for p in params]
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    with pytest.raises(RuntimeError, match="capture"):
+        plan.ptr_table(fresh, "params")

@@ -8,8 +8,9 @@ Expected local pieces come from the pages' definitions, not from the plan:
 FSDP2 -- torch.chunk(param, N, dim=0)[r] (section 03); FSDP1 -- the
 flattened parameter's elements whose flat index falls in [r*c, (r+1)*c),
 with flat indices from the oracle's layout.  Shards are cut from the
-oracle's pack.  The CPU tests run on host tensors; the GPU test takes the
-shard from fs_pack(rank=r).
+oracle's pack.  The CPU tests check the exported views on host tensors; the
+GPU tests take the shard from fs_pack(rank=r) and import the pieces with
+fs_load_local, compared bit for bit with the oracle's pack of rank r.
 """
 import numpy as np
 import pytest
@@ -90,10 +91,7 @@ def test_local_views_are_the_sharded_state_dict(case):
             assert torch.equal(v, e), (name, r, i)
             assert v.numel() == 0 or v.data_ptr() >= shard.data_ptr()       # a view, not a copy
             held[i] += v.numel()
-        # import into a scribbled buffer: pads come back zero, pieces in place
-        back = torch.full_like(shard, 0x5A5A if dt == "bf16" else 0x5A5A5A5A)
-        plan.load_local(back, r, [e.clone() for e in exp])
-        assert torch.equal(back, shard), (name, r)
+        assert plan.local_numels(r) == [e.numel() for e in exp]
     np.testing.assert_array_equal(held, L.numel)     # every element on exactly one rank
 
 
@@ -148,3 +146,64 @@ def test_gpu_pack_rank_then_local_views(case):
         exp = _expected_local(mode, L, params, shapes, N, r)
         for i, (v, e) in enumerate(zip(views, exp)):
             assert torch.equal(v.cpu().view(_tdt(dt)), e), (name, r, i)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_gpu_load_local_matches_oracle_pack(case):
+    """Import on the GPU (fs_load_local): every rank's local pieces, by the
+    pages' definitions, into a scribbled shard inside guard bands; the result
+    equals the oracle's pack of that rank bit for bit (pads zero), and nothing
+    outside the shard is written."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gpu_util import Guarded, bits, say
+    name, mode, shapes, dt, N, uo = case
+    say("state dict: fs_load_local", name)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    plan = fs.fs_plan(shapes, dt, N, uo, mode).upload()
+    L = _layout(mode, shapes, dt, N, uo)
+    params = _params(shapes, dt, seed=37)
+    host = [p.reshape(-1).numpy().view(np.uint16 if dt == "bf16" else np.uint32) for p in params]
+    for r in range(N):
+        exp = _expected_local(mode, L, params, shapes, N, r)
+        pieces = [e.contiguous().view(tdt).cuda() for e in exp]
+        out = Guarded(plan.shard_numel, tdt, fill=None)
+        out.t.view(torch.int16 if dt == "bf16" else torch.int32).fill_(0x5A5A if dt == "bf16" else 0x5A5A5A5A)
+        plan.load_local(out.t, r, pieces)
+        torch.cuda.synchronize()
+        out.check()
+        np.testing.assert_array_equal(bits(out.t), oracle.pack(L, host, rank=r), err_msg=f"{name} rank {r}")
+
+
+@pytest.mark.gpu
+def test_gpu_load_local_misaligned_pieces_and_errors():
+    """Pieces at odd element offsets (views into one buffer) load bit-exactly;
+    a wrong rank or size is refused before any launch."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gpu_util import bits, say
+    say("state dict: fs_load_local, misaligned pieces")
+    shapes, N = synth.llama_block_shapes(256, 688), 8
+    plan = fs.fs_plan(shapes, "bf16", N, False, "fsdp2").upload()
+    L = oracle.fsdp2_layout(shapes, 2, N)
+    params = _params(shapes, "bf16", seed=41)
+    host = [p.reshape(-1).numpy().view(np.uint16) for p in params]
+    r = 5
+    exp = _expected_local("fsdp2", L, params, shapes, N, r)
+    total = sum(e.numel() for e in exp)
+    buf = torch.zeros(total + 2 * len(exp) + 1, dtype=torch.int16, device="cuda")
+    pieces, off = [], 1
+    for e in exp:                                   # odd offsets: 2-byte but not 16-byte aligned
+        v = buf[off:off + e.numel()]
+        v.copy_(e.reshape(-1).cuda())
+        pieces.append(v.view(torch.bfloat16))
+        off += e.numel() + 1
+    shard = torch.empty(plan.shard_numel, dtype=torch.bfloat16, device="cuda")
+    plan.load_local(shard, r, pieces)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(shard), oracle.pack(L, host, rank=r))
+    with pytest.raises(ValueError):
+        plan.load_local(shard, N, pieces)
+    with pytest.raises(ValueError):
+        plan.load_local(shard, r, pieces[:-1])
