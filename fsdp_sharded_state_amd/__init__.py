@@ -29,6 +29,7 @@ FS_E_INVAL, FS_E_UNSUPPORTED, FS_E_DTYPE, FS_E_OVERFLOW, FS_E_ALIGN, FS_E_HIP, F
 _CODES = {0: "FS_OK", -1: "FS_E_INVAL", -2: "FS_E_UNSUPPORTED", -3: "FS_E_DTYPE",
           -4: "FS_E_OVERFLOW", -5: "FS_E_ALIGN", -6: "FS_E_HIP", -7: "FS_E_NOMEM"}
 FS_BF16, FS_FP32 = 0, 1
+NOALLOC_MAX_NUMEL = 16777216   # scratch capacity of fs_reduce_adamw_step_noalloc (fp32 elements)
 FS_FSDP1_FLAT, FS_FSDP2_PER_PARAM = 1, 2
 
 
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
     L.fs_reduce_shard_ex.argtypes = [i64, i32, i32, i32, vp, vp, vp]
     L.fs_pack_cast.argtypes = [vp, vp, i32, vp, i32, vp]
     L.fs_load_local.argtypes = [vp, i32, vp, vp, vp]
+    L.fs_reduce_adamw_step_noalloc.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(AdamWHparams), vp]
     L.fs_reduce_adamw_step.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(AdamWHparams), vp]
     L.fs_copy_bytes.argtypes = [vp, vp, i64, vp]
     L.fs_stream_read.argtypes = [vp, i64, vp, vp]
@@ -109,7 +111,7 @@ def lib() -> ctypes.CDLL:
     for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
                  "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_reduce_adamw_step",
                  "fs_reduce_shard_ex", "fs_pack_cast", "fs_reshard_plan", "fs_reshard_info",
-                 "fs_reshard_upload", "fs_reshard", "fs_load_local",
+                 "fs_reshard_upload", "fs_reshard", "fs_load_local", "fs_reduce_adamw_step_noalloc",
                  "fs_copy_bytes", "fs_stream_read", "fs_stream_fill"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -495,6 +497,34 @@ def fs_reduce_adamw_step(slices: Sequence[torch.Tensor], master: torch.Tensor, e
                                       ptr(exp_avg, "exp_avg"), ptr(exp_avg_sq, "exp_avg_sq"),
                                       ptr(param_bf16, "param_bf16"), ptr(grad_out, "grad_out"),
                                       ctypes.byref(hp), _stream(stream)))
+
+
+def fs_reduce_adamw_step_noalloc(slices: Sequence[torch.Tensor], master: torch.Tensor, exp_avg: torch.Tensor,
+                                 exp_avg_sq: torch.Tensor, param_bf16: Optional[torch.Tensor] = None, *, world: int,
+                                 grad_acc: int = 1, lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999,
+                                 eps: float = 1e-8, weight_decay: float = 0.01, step: int = 1, stream=None):
+    """fs_reduce_adamw_step without grad_out, for callers that cannot
+    allocate: with more than 32 terms the partial sums go to the library's
+    per-GPU scratch array (at most NOALLOC_MAX_NUMEL elements)."""
+    n = master.numel()
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if t.dtype != torch.float32 or t.numel() != n:
+            raise ValueError(f"fs_reduce_adamw_step_noalloc: {name} must be float32 with {n} elements")
+    if len(slices) != world * grad_acc:
+        raise ValueError(f"fs_reduce_adamw_step_noalloc: need world*grad_acc = {world * grad_acc} slices")
+    ptrs = []
+    for k, s in enumerate(slices):
+        if s.dtype != torch.bfloat16 or s.numel() != n:
+            raise ValueError(f"fs_reduce_adamw_step_noalloc: slice {k} must be bf16 with {n} elements")
+        ptrs.append(_dev_ptr(s, f"slices[{k}]") if n else 0)
+    if param_bf16 is not None and (param_bf16.dtype != torch.bfloat16 or param_bf16.numel() != n):
+        raise ValueError("fs_reduce_adamw_step_noalloc: param_bf16 must be bfloat16 with n elements")
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    hp = AdamWHparams(lr, beta1, beta2, eps, weight_decay, 0, int(step))
+    ptr = (lambda t, w: (_dev_ptr(t, w) if n else 0) if t is not None else None)
+    _check(lib().fs_reduce_adamw_step_noalloc(n, int(world), int(grad_acc), arr, ptr(master, "master"),
+                                              ptr(exp_avg, "exp_avg"), ptr(exp_avg_sq, "exp_avg_sq"),
+                                              ptr(param_bf16, "param_bf16"), ctypes.byref(hp), _stream(stream)))
 
 
 def fs_copy_bytes(dst: torch.Tensor, src: torch.Tensor, stream=None):

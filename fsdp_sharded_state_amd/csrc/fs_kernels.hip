@@ -20,6 +20,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "fs_plan_impl.h"
 #include "../../include/fs_bench.h"
@@ -928,13 +930,13 @@ template <int G, bool HAS_P16, bool HAS_G, bool TAIL>
 __device__ __forceinline__ void reduce_adamw_chunk(const SliceArgs &sa, int nterms, int first_pass, float world,
                                                    float *__restrict__ th, float *__restrict__ m,
                                                    float *__restrict__ v, uint16_t *__restrict__ p16,
-                                                   float *__restrict__ gout, const AdamConsts &c, int64_t base,
-                                                   int64_t n) {
+                                                   const float *part, float *gout, const AdamConsts &c,
+                                                   int64_t base, int64_t n) {
     constexpr int KB = kFusedBatch < G ? kFusedBatch : G;
     constexpr int NB = G / KB;
     const Bounds<G, TAIL> B(base, n);
     float acc[4 * G];
-    if (!first_pass) load_f32_groups<G, G, TAIL>(acc, gout, base, B);   // partial sums left by the reduce passes
+    if (!first_pass) load_f32_groups<G, G, TAIL>(acc, part, base, B);   // partial sums left by the reduce passes
     sum_slices<G, 2, TAIL>(sa, nterms, first_pass, acc, base, B);
 #pragma unroll
     for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
@@ -974,14 +976,14 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
                                                                       float *__restrict__ m,
                                                                       float *__restrict__ v,
                                                                       uint16_t *__restrict__ p16,
-                                                                      float *__restrict__ gout, AdamConsts c,
+                                                                      const float *part, float *gout, AdamConsts c,
                                                                       int64_t n) {
     static_assert(G % kTailGroups == 0, "the tail walks whole sub-chunks");
     FS_CHUNK_DISPATCH(G,
                       (reduce_adamw_chunk<G, HAS_P16, HAS_G, false>(sa, nterms, first_pass, world, th, m, v, p16,
-                                                                    gout, c, base, n)),
+                                                                    part, gout, c, base, n)),
                       (reduce_adamw_chunk<kTailGroups, HAS_P16, HAS_G, true>(sa, nterms, first_pass, world, th, m,
-                                                                             v, p16, gout, c, base, n)));
+                                                                             v, p16, part, gout, c, base, n)));
 }
 
 // Misaligned variant: lane i owns 8 consecutive elements (the general
@@ -990,7 +992,8 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
 __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArgs sa, int nterms, int first_pass,
                                                                         float world, int64_t n, float *th,
                                                                         float *m, float *v, uint16_t *p16,
-                                                                        float *gout, AdamConsts c) {
+                                                                        const float *part, float *gout,
+                                                                        AdamConsts c) {
     const int64_t nvec = n >> 3;
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i < nvec) {
@@ -1002,7 +1005,7 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArg
             t = 1;
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = gout[8 * i + e];
+            for (int e = 0; e < 8; ++e) acc[e] = part[8 * i + e];
         }
         for (; t < nterms; ++t) add_bf16x8(acc, ld_slice16<false>(sa.p[t], off));
 #pragma unroll
@@ -1027,7 +1030,7 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArg
             acc = __uint_as_float((uint32_t)sa.p[0][k] << 16);
             t = 1;
         } else {
-            acc = gout[k];
+            acc = part[k];
         }
         for (; t < nterms; ++t) acc = acc + __uint_as_float((uint32_t)sa.p[t][k] << 16);
         const float g = acc / world;
@@ -1140,20 +1143,20 @@ int check_launch(const char *what) {
 
 template <int G>
 void launch_fused(int64_t n, hipStream_t stream, const SliceArgs &sa, int cnt, int first, float world, float *th,
-                  float *m, float *v, uint16_t *p16, float *gout, const AdamConsts &c) {
+                  float *m, float *v, uint16_t *p16, const float *part, float *gout, const AdamConsts &c) {
     const dim3 g((uint32_t)((n + kWgRow * G - 1) / (kWgRow * G))), b(kThreads);
     if (p16 && gout)
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, true>), g, b, 0, stream, sa, cnt, first, world, th, m,
-                           v, p16, gout, c, n);
+                           v, p16, part, gout, c, n);
     else if (p16)
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, false>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, gout, c, n);
+                           m, v, p16, part, gout, c, n);
     else if (gout)
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, true>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, gout, c, n);
+                           m, v, p16, part, gout, c, n);
     else
         hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, false>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, gout, c, n);
+                           m, v, p16, part, gout, c, n);
 }
 
 // One pass of the fp32 reduce over terms [t0, t0 + cnt): chunked when every
@@ -1559,51 +1562,99 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
     return check_launch("fs_adamw_step");
 }
 
-extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, const uint16_t *const *slices,
-                                    float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_bf16,
-                                    float *grad_out, const fs_adamw_hparams_t *hp, hipStream_t stream) {
-    fsi::clear_error();
-    if (n < 0) return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: n < 0");
+namespace {
+
+// ------------------------------------------------------ no-allocation scratch --
+//
+// fs_reduce_adamw_step_noalloc keeps the partial sums of a step with more
+// than kTermsPerPass terms in this file-scope device array instead of a
+// caller-supplied buffer, so it allocates nothing.  Every GPU the library
+// runs on holds its own copy (64 MiB) until the process ends, and every call
+// on that GPU shares it: the first reduce pass writes all n partial sums
+// before any is read, so nothing needs clearing, and calls that overlap on
+// one GPU (two streams at once) race.  In host code the array's name is not
+// a device address: its per-device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr int64_t kScratchBytes = 64ll << 20;
+constexpr int64_t kScratchFloats = kScratchBytes / (int64_t)sizeof(float);
+static __device__ __align__(256) float scratch[kScratchFloats];
+static_assert(kScratchFloats == FS_NOALLOC_MAX_NUMEL, "the header states the scratch capacity");
+
+int scratch_on_current_device(const char *what, float **out) {
+    static std::mutex mu;
+    static std::vector<float *> by_device;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fsi::fail(FS_E_HIP, "%s: no current device", what);
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)by_device.size() <= dev) by_device.resize((size_t)dev + 1, nullptr);
+    if (!by_device[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fsi::fail(FS_E_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", what, dev,
+                             hipGetErrorString(e));
+        by_device[dev] = static_cast<float *>(ptr);
+    }
+    *out = by_device[dev];
+    return FS_OK;
+}
+
+// The fused step behind both entry points.  More than kTermsPerPass terms
+// run as plain reduce passes that leave partial sums in `partial`
+// (fs_reduce_adamw_step: the caller's grad_out; the no-allocation variant:
+// the library's scratch array, obtained only when it is needed).
+int reduce_adamw_impl(const char *what, int64_t n, int32_t world, int32_t grad_acc, const uint16_t *const *slices,
+                      float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_bf16, float *grad_out,
+                      bool static_partial, const fs_adamw_hparams_t *hp, hipStream_t stream) {
+    if (n < 0) return fsi::fail(FS_E_INVAL, "%s: n < 0", what);
     if (world < 1 || grad_acc < 1)
-        return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: world and grad_acc must be >= 1");
-    if (int rc = check_hparams("fs_reduce_adamw_step", hp)) return rc;
+        return fsi::fail(FS_E_INVAL, "%s: world and grad_acc must be >= 1", what);
+    if (int rc = check_hparams(what, hp)) return rc;
     int64_t terms64, bytes_in, bytes_out;
     if (__builtin_mul_overflow((int64_t)world, (int64_t)grad_acc, &terms64) || terms64 > (1 << 20))
-        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: too many terms");
+        return fsi::fail(FS_E_OVERFLOW, "%s: too many terms", what);
     if (__builtin_mul_overflow(n, (int64_t)2, &bytes_in) || __builtin_mul_overflow(n, (int64_t)4, &bytes_out))
-        return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: n too large");
+        return fsi::fail(FS_E_OVERFLOW, "%s: n too large", what);
     if (n == 0) return FS_OK;
     const int terms = (int)terms64;
     if (!slices || !master || !exp_avg || !exp_avg_sq)
-        return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: NULL pointer");
-    if (terms > kTermsPerPass && !grad_out)
-        return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: more than %d terms need grad_out for the partial sums",
+        return fsi::fail(FS_E_INVAL, "%s: NULL pointer", what);
+    const bool multi_pass = terms > kTermsPerPass;
+    if (multi_pass && static_partial && n > kScratchFloats)
+        return fsi::fail(FS_E_OVERFLOW, "%s: more than %d terms keep partial sums in the library's scratch "
+                         "array, which holds %lld elements (n = %lld)", what, kTermsPerPass,
+                         (long long)kScratchFloats, (long long)n);
+    if (multi_pass && !static_partial && !grad_out)
+        return fsi::fail(FS_E_INVAL, "%s: more than %d terms need grad_out for the partial sums", what,
                          kTermsPerPass);
     if (misaligned(master, 4) || misaligned(exp_avg, 4) || misaligned(exp_avg_sq, 4) ||
         (grad_out && misaligned(grad_out, 4)) || (param_bf16 && misaligned(param_bf16, 2)))
-        return fsi::fail(FS_E_ALIGN, "fs_reduce_adamw_step: pointer not aligned to its element size");
+        return fsi::fail(FS_E_ALIGN, "%s: pointer not aligned to its element size", what);
     bool aligned = !misaligned(master, 16) && !misaligned(exp_avg, 16) && !misaligned(exp_avg_sq, 16) &&
                    !(grad_out && misaligned(grad_out, 16)) && !(param_bf16 && misaligned(param_bf16, 16));
     const void *outs[5] = {master, exp_avg, exp_avg_sq, grad_out, param_bf16};
     const int64_t out_bytes[5] = {bytes_out, bytes_out, bytes_out, grad_out ? bytes_out : 0,
                                   param_bf16 ? bytes_in : 0};
     for (int t = 0; t < terms; ++t) {
-        if (!slices[t]) return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: slice %d is NULL", t);
+        if (!slices[t]) return fsi::fail(FS_E_INVAL, "%s: slice %d is NULL", what, t);
         if (misaligned(slices[t], 2))
-            return fsi::fail(FS_E_ALIGN, "fs_reduce_adamw_step: slice %d not 2-byte aligned", t);
+            return fsi::fail(FS_E_ALIGN, "%s: slice %d not 2-byte aligned", what, t);
         if (misaligned(slices[t], 16)) aligned = false;
         for (int o = 0; o < 5; ++o)
             if (ranges_overlap(slices[t], bytes_in, outs[o], out_bytes[o]))
-                return fsi::fail(FS_E_INVAL, "fs_reduce_adamw_step: an output overlaps slice %d", t);
+                return fsi::fail(FS_E_INVAL, "%s: an output overlaps slice %d", what, t);
     }
     const AdamConsts c = adam_consts(*hp);
-    if (!grid_fits(n)) return fsi::fail(FS_E_OVERFLOW, "fs_reduce_adamw_step: n too large for one launch");
-    // terms before the last kTermsPerPass: plain reduce passes leave partial sums in grad_out
+    if (!grid_fits(n)) return fsi::fail(FS_E_OVERFLOW, "%s: n too large for one launch", what);
+    float *partial = grad_out;
+    if (multi_pass && static_partial)
+        if (int rc = scratch_on_current_device(what, &partial)) return rc;
+    // terms before the last kTermsPerPass: plain reduce passes leave partial sums in `partial`
     const int last_cnt = terms - (terms - 1) / kTermsPerPass * kTermsPerPass;
     const int t_last = terms - last_cnt;
     (void)hipGetLastError();
     for (int t0 = 0; t0 < t_last; t0 += kTermsPerPass)
-        launch_reduce_pass(n, stream, slices, t0, kTermsPerPass, t0 == 0, 0, (float)world, aligned, grad_out);
+        launch_reduce_pass(n, stream, slices, t0, kTermsPerPass, t0 == 0, 0, (float)world, aligned, partial);
     SliceArgs sa;
     memset(&sa, 0, sizeof sa);
     for (int k = 0; k < last_cnt; ++k) sa.p[k] = slices[t_last + k];
@@ -1611,16 +1662,35 @@ extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, 
     if (aligned) {
         if (last_cnt <= kRedFewTerms)
             launch_fused<kFusedGroupsFew>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg, exp_avg_sq,
-                                          param_bf16, grad_out, c);
+                                          param_bf16, partial, grad_out, c);
         else
             launch_fused<kFusedGroupsMany>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg, exp_avg_sq,
-                                           param_bf16, grad_out, c);
+                                           param_bf16, partial, grad_out, c);
     } else {
         const int64_t grid = std::max<int64_t>(1, ((n >> 3) + kThreads - 1) / kThreads);
         hipLaunchKernelGGL(reduce_adamw_general_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, last_cnt,
-                           first, (float)world, n, master, exp_avg, exp_avg_sq, param_bf16, grad_out, c);
+                           first, (float)world, n, master, exp_avg, exp_avg_sq, param_bf16, partial, grad_out, c);
     }
-    return check_launch("fs_reduce_adamw_step");
+    return check_launch(what);
+}
+
+}  // namespace
+
+extern "C" int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc, const uint16_t *const *slices,
+                                    float *master, float *exp_avg, float *exp_avg_sq, uint16_t *param_bf16,
+                                    float *grad_out, const fs_adamw_hparams_t *hp, hipStream_t stream) {
+    fsi::clear_error();
+    return reduce_adamw_impl("fs_reduce_adamw_step", n, world, grad_acc, slices, master, exp_avg, exp_avg_sq,
+                             param_bf16, grad_out, false, hp, stream);
+}
+
+extern "C" int fs_reduce_adamw_step_noalloc(int64_t n, int32_t world, int32_t grad_acc,
+                                            const uint16_t *const *slices, float *master, float *exp_avg,
+                                            float *exp_avg_sq, uint16_t *param_bf16, const fs_adamw_hparams_t *hp,
+                                            hipStream_t stream) {
+    fsi::clear_error();
+    return reduce_adamw_impl("fs_reduce_adamw_step_noalloc", n, world, grad_acc, slices, master, exp_avg,
+                             exp_avg_sq, param_bf16, nullptr, true, hp, stream);
 }
 
 extern "C" int fs_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream) {

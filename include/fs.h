@@ -398,6 +398,24 @@ int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc,
                          float *grad_out, const fs_adamw_hparams_t *hp,
                          hipStream_t stream);
 
+/*
+ * fs_reduce_adamw_step_noalloc -- fs_reduce_adamw_step with grad_out = NULL
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): with more
+ * than 32 terms the partial sums that fs_reduce_adamw_step keeps in the
+ * caller's grad_out go to a scratch array the library holds on each GPU
+ * instead (FS_NOALLOC_MAX_NUMEL fp32 elements, 64 MiB, held until the process
+ * ends).  Allocates and frees nothing.  Same arguments, results (bit for bit)
+ * and errors as fs_reduce_adamw_step, plus FS_E_OVERFLOW when more than 32
+ * terms meet n > FS_NOALLOC_MAX_NUMEL.  Calls on one GPU share the scratch
+ * array: calls that overlap in time on one GPU race.
+ */
+#define FS_NOALLOC_MAX_NUMEL 16777216
+int fs_reduce_adamw_step_noalloc(int64_t n, int32_t world, int32_t grad_acc,
+                                 const uint16_t *const *slices, float *master,
+                                 float *exp_avg, float *exp_avg_sq, uint16_t *param_bf16,
+                                 const fs_adamw_hparams_t *hp, hipStream_t stream);
+
 /* fs_last_error -- message for the calling thread's last failed call
  * (empty string if none).  The pointer stays valid until the next call. */
 const char *fs_last_error(void);
