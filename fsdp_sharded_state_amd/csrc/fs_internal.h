@@ -22,16 +22,13 @@
 
 namespace fsi {
 
-#ifndef FS_TILE_BLOCKS_PER_THREAD
-#define FS_TILE_BLOCKS_PER_THREAD 4
-#endif
+// Tile sizes measured on the 7B model's 33 groups: unpack 16 KB of
+// destination per workgroup (8 KB: -1%, 32 KB: -8%), pack and reshard 8 KB
+// (16 KB: -4%, 4 KB: -3%).
 constexpr int kThreads = 256;                 // threads per workgroup (4 waves of 64)
-constexpr int kBlocksPerThread = FS_TILE_BLOCKS_PER_THREAD;   // 16-byte blocks per thread per tile
+constexpr int kBlocksPerThread = 4;           // 16-byte blocks per thread per tile
 constexpr int kTileBlocks = kThreads * kBlocksPerThread;      // unpack tiles (16 KB of destination)
-#ifndef FS_PACK_TILE_BLOCKS
-#define FS_PACK_TILE_BLOCKS (kTileBlocks / 2)
-#endif
-constexpr int kPackTileBlocks = FS_PACK_TILE_BLOCKS;          // pack / reshard tiles (8 KB of destination)
+constexpr int kPackTileBlocks = kTileBlocks / 2;              // pack / reshard tiles (8 KB of destination)
 static_assert(kPackTileBlocks <= kTileBlocks, "a tile must fit the kernel's per-thread loop");
 constexpr int kTileSegs = 256;                // max segments staged in LDS per tile
 

@@ -198,38 +198,42 @@ __device__ __forceinline__ void stage_tile(TileLds &L, const Segment *segs, cons
 
 // Uniform fast path: the whole tile is one contiguous run src -> dst with a
 // 16-byte-aligned destination.  `src` is the byte address of the tile's
-// first element in the source.
-__device__ __forceinline__ void copy_run(char *dst, const char *src, int nblk) {
+// first element in the source.  run_load reads, per lane, the aligned
+// 16-byte block holding the start of each of its destination blocks (all of
+// a lane's loads in flight at once); run_store completes misaligned blocks
+// and writes them.  (Issuing an unpack tile's loads before its destination
+// pointer is read measured 3% slower on the 7B groups, so the unpack reads
+// the pointer first.)
+__device__ __forceinline__ void run_load(const char *src, int nblk, u32x4 (&lo)[fsi::kBlocksPerThread]) {
     constexpr int U = fsi::kBlocksPerThread;
     const int tid = threadIdx.x;
-    const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(src) & 15);
-    if (sh == 0) {
-        u32x4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int b = u * kThreads + tid;
-            if (b < nblk) v[u] = ld16(src + 16 * (int64_t)b);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int b = u * kThreads + tid;
-            if (b < nblk) st16(dst + 16 * (int64_t)b, v[u]);
-        }
-        return;
-    }
-    // Misaligned source: lane l loads aligned block b (containing the start
-    // of its 16 bytes); the following aligned block is lane l+1's load,
-    // fetched with a wavefront shuffle.  The last lane of each wave (and the
-    // lane holding the tile's last block) loads it itself; that block holds
-    // needed bytes because sh > 0.
-    const char *a = src - sh;
-    const int lane = tid & 63;
-    u32x4 lo[U];
+    const char *a = src - (reinterpret_cast<uintptr_t>(src) & 15);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int b = u * kThreads + tid;
         lo[u] = b < nblk ? ld16(a + 16 * (int64_t)b) : u32x4{0u, 0u, 0u, 0u};
     }
+}
+
+__device__ __forceinline__ void run_store(char *dst, const char *src, int nblk,
+                                          const u32x4 (&lo)[fsi::kBlocksPerThread]) {
+    constexpr int U = fsi::kBlocksPerThread;
+    const int tid = threadIdx.x;
+    const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(src) & 15);
+    if (sh == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = u * kThreads + tid;
+            if (b < nblk) st16(dst + 16 * (int64_t)b, lo[u]);
+        }
+        return;
+    }
+    // Misaligned source: the aligned block following lane l's is lane l+1's
+    // load, fetched with a wavefront shuffle.  The last lane of each wave
+    // (and the lane holding the tile's last block) loads it itself; that
+    // block holds needed bytes because sh > 0.
+    const char *a = src - sh;
+    const int lane = tid & 63;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int b = u * kThreads + tid;
@@ -243,6 +247,12 @@ __device__ __forceinline__ void copy_run(char *dst, const char *src, int nblk) {
             st16(dst + 16 * (int64_t)b, funnel16(lo[u], hi, sh));
         }
     }
+}
+
+__device__ __forceinline__ void copy_run(char *dst, const char *src, int nblk) {
+    u32x4 lo[fsi::kBlocksPerThread];
+    run_load(src, nblk, lo);
+    run_store(dst, src, nblk, lo);
 }
 
 // Destination-driven copy into one contiguous buffer (`out`, addressed from
