@@ -22,14 +22,16 @@
 
 namespace fsi {
 
-// Tile sizes measured on the 7B model's 33 groups: unpack 16 KB of
-// destination per workgroup (8 KB: -1%, 32 KB: -8%), pack and reshard 8 KB
-// (16 KB: -4%, 4 KB: -3%).
+// Tile sizes measured on the 7B model's 33 groups: every copy kernel (pack,
+// unpack, reshard, local import) builds tiles of 8 KB of destination per
+// workgroup (pack 16 KB: -4%, 4 KB: -3%; unpack 16 KB: -3%, 4 KB: -1%).  The
+// kernels' per-thread loop has room for twice that: the same 8 KB tiles with
+// a loop of two blocks per thread measured 3% slower on the unpack.
 constexpr int kThreads = 256;                 // threads per workgroup (4 waves of 64)
-constexpr int kBlocksPerThread = 4;           // 16-byte blocks per thread per tile
-constexpr int kTileBlocks = kThreads * kBlocksPerThread;      // unpack tiles (16 KB of destination)
-constexpr int kPackTileBlocks = kTileBlocks / 2;              // pack / reshard tiles (8 KB of destination)
-static_assert(kPackTileBlocks <= kTileBlocks, "a tile must fit the kernel's per-thread loop");
+constexpr int kBlocksPerThread = 4;           // loop capacity: 16-byte blocks per thread
+constexpr int kTileBlocks = kThreads * kBlocksPerThread;      // largest tile a kernel accepts (16 KB)
+constexpr int kCopyTileBlocks = kTileBlocks / 2;              // tiles the planner builds (8 KB of destination)
+static_assert(kCopyTileBlocks <= kTileBlocks, "a tile must fit the kernel's per-thread loop");
 constexpr int kTileSegs = 256;                // max segments staged in LDS per tile
 
 struct Segment {        // 32 bytes, sorted by vx, non-overlapping, len > 0

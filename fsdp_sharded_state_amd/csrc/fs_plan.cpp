@@ -273,19 +273,19 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
         // starts on a 16-byte block of the gathered buffer, their concatenation
         // is also a grid anchored at 0 and serves the all-ranks pack: one table.
         p->rank_tile_off.push_back(0);
-        p->pack_tiles_rank.reserve((size_t)world * (size_t)(ceil_div(ceil_div(shard, vec), fsi::kPackTileBlocks) + 1));
+        p->pack_tiles_rank.reserve((size_t)world * (size_t)(ceil_div(ceil_div(shard, vec), fsi::kCopyTileBlocks) + 1));
         for (int32_t r = 0; r < world; ++r) {
-            fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, fsi::kPackTileBlocks,
+            fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, fsi::kCopyTileBlocks,
                              p->pack_tiles_rank);
             p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
         }
         const bool shared_grid = world == 1 || shard % vec == 0;
         if (!shared_grid) {
-            p->pack_tiles_all.reserve((size_t)(ceil_div(ceil_div(gathered, vec), fsi::kPackTileBlocks) + 1));
-            fsi::build_tiles(ps, 0, gathered, vec, fsi::kPackTileBlocks, p->pack_tiles_all);
+            p->pack_tiles_all.reserve((size_t)(ceil_div(ceil_div(gathered, vec), fsi::kCopyTileBlocks) + 1));
+            fsi::build_tiles(ps, 0, gathered, vec, fsi::kCopyTileBlocks, p->pack_tiles_all);
         }
-        p->unpack_tiles.reserve((size_t)(ceil_div(ceil_div(vb, vec), fsi::kTileBlocks) + 1));
-        fsi::build_tiles(p->unpack_segs, 0, vb, vec, fsi::kTileBlocks, p->unpack_tiles);
+        p->unpack_tiles.reserve((size_t)(ceil_div(ceil_div(vb, vec), fsi::kCopyTileBlocks) + 1));
+        fsi::build_tiles(p->unpack_segs, 0, vb, vec, fsi::kCopyTileBlocks, p->unpack_tiles);
         for (Tile &t : p->unpack_tiles)
             if (t.run_buf >= 0) t.run_dst = t.x_begin - p->bufinfo[t.run_buf].vbase;
 
@@ -451,7 +451,7 @@ extern "C" int fs_reshard_plan(fs_plan_t src, fs_plan_t dst, fs_reshard_t *out) 
             return fsi::fail(FS_E_OVERFLOW, "fs_reshard_plan: too many copy segments");
         }
         r->segs = std::move(pieces);
-        fsi::build_tiles(r->segs, 0, r->dst_gathered, r->vec, fsi::kPackTileBlocks, r->tiles);
+        fsi::build_tiles(r->segs, 0, r->dst_gathered, r->vec, fsi::kCopyTileBlocks, r->tiles);
         r->ws_segs = 0;
         r->ws_tiles = align_up((int64_t)r->segs.size() * (int64_t)sizeof(Segment), 256);
         r->ws_bytes = std::max<int64_t>(256, r->ws_tiles + align_up((int64_t)r->tiles.size() * (int64_t)sizeof(Tile), 256));
