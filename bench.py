@@ -252,7 +252,9 @@ def measure_order(W, steps: int, warmup: int) -> dict:
 
 def placement_summary(r: dict) -> dict:
     k = r["kernels"]
-    return {"ms_per_step": round(r["ms_per_step"], 4), "value_GBps": round(r["value"], 1),
+    own = {f"{n}_of_own_buffer_ceiling": round(k[n]["GBps"] / r["own"][n]["ceiling_GBps"], 4)
+           for n in ("reduce", "adamw") if "own" in r}
+    return {**own, "ms_per_step": round(r["ms_per_step"], 4), "value_GBps": round(r["value"], 1),
             "frac_hbm_peak": round(r["value"] / HBM_PEAK_GBPS, 4),
             "reduce_GBps": k["reduce"]["GBps"], "adamw_GBps": k["adamw"]["GBps"],
             "pack_GBps": k["pack"]["GBps"], "unpack_GBps": k["unpack"]["GBps"],
@@ -836,7 +838,7 @@ def main():
         sys.exit("bench.py needs a GPU")
     import fsdp_sharded_state_amd as fs
 
-    runs, extra, own, mixes = [], None, None, None
+    runs, extra, mixes = [], None, None
     for i, order in enumerate(orders):
         W = setup("7b", order=order, pooled=not args.separate)
         r = measure_order(W, args.steps, args.warmup)
@@ -844,10 +846,12 @@ def main():
             f"{r['kernels']['reduce']['GBps']:.0f}, adamw {r['kernels']['adamw']['GBps']:.0f}, fused "
             f"{r['kernels']['reduce_adamw_fused']['ms']:.3f} ms")
         if i == 0:
-            # the engine's other entry points and the streaming ceilings of
-            # the kernels' own buffers, on the first order's placement
+            # the engine's other entry points, on the first order's placement
             extra = extra_measurements(W, args.steps, small=not args.no_small)
-            own = own_buffer_ceilings(W)      # last on this setup: it overwrites the shard state
+        # the streaming ceilings of the reduce's and AdamW's own buffers on this
+        # placement; last on this setup: it overwrites the shard state
+        r["own"] = own_buffer_ceilings(W)
+        if i == 0:
             P, S, N, A = W["P"], W["S"], W["world"], W["grad_acc"]
             gath = sum(p.gathered_numel for p in W["plans"])
             mixes = {"pack": (2 * P, 2 * gath), "unpack": (2 * P, 2 * P), "reduce": (2 * N * A * S, 4 * S),
@@ -877,8 +881,8 @@ def main():
             kern[k]["frac_of_copy_ceiling"] = round(kern[k]["GBps"] / ceiling, 4)
             kern[k]["mix_ceiling_GBps"] = round(c, 1)
             kern[k]["frac_of_mix_ceiling"] = round(kern[k]["GBps"] / c, 4)
-    for k, v in own.items():
-        kern[k]["own_buffers"] = dict(v, note=f"measured on the {runs[0]['order']} placement")
+    for k, v in head["own"].items():
+        kern[k]["own_buffers"] = dict(v, frac=round(kern[k]["GBps"] / v["ceiling_GBps"], 4))
     if big is not None:
         kern["config5_70b"] = big
     alg = head["alg"]
