@@ -275,16 +275,18 @@ def _timed(fn, reps):
     return sum(e[0].elapsed_time(e[1]) for e in evs) / reps
 
 
-def _timed_graph(fn, reps):
+def _timed_graph(fn, reps, calls=8):
     """GPU time per call of fn for launches too short to hide the Python
-    call: fn is captured once into a HIP graph and the graph replayed
-    back to back."""
+    call: `calls` calls of fn are captured back to back into one HIP graph
+    (as a sequence of groups would issue them), the graph is replayed reps
+    times, and the time is divided by reps * calls."""
     import torch
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn()
+        for _ in range(calls):
+            fn()
     g.replay()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -294,7 +296,7 @@ def _timed_graph(fn, reps):
     e.record()
     e.synchronize()
     del g
-    return s.elapsed_time(e) / reps
+    return s.elapsed_time(e) / (reps * calls)
 
 
 def extra_measurements(W, reps, small: bool = True) -> dict:
@@ -369,6 +371,11 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
     ms_f = _timed_graph(lambda: fs.fs_reduce_adamw_step(sl1, th, m, v, pb, None, world=N, grad_acc=1, step=3),
                         4 * reps)
     br, ba, bfz = (2 * N + 4) * sb, 30 * sb, (2 * N + 26) * sb
+    # one block group's copy-in (all N shards) and copy-out, 202,383,360 parameters
+    bpl, bps, bg, bo = W["plans"][0], W["params"][0], W["gathered"][0], W["outs"][0]
+    ms_bp = _timed_graph(lambda: fs.fs_pack(bpl, bps, bg), 4 * reps)
+    ms_bu = _timed_graph(lambda: fs.fs_unpack(bpl, bg, bo), 4 * reps)
+    bbp, bbu = 2 * bpl.total_numel + 2 * bpl.gathered_numel, 4 * bpl.total_numel
     # the padding-stress parameter list (97 parameters, 21,444,378 elements, FSDP1
     # with use_orig_params, N = 8): alignment and world pads, short segments
     st = [(n,) for n in synth.padding_stress_numels()]
@@ -389,7 +396,11 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
         "reduce": {"us": round(ms_r * 1e3, 1), "GB": round(br / 1e9, 3), "GBps": round(br / (ms_r * 1e-3) / 1e9, 1)},
         "adamw": {"us": round(ms_a * 1e3, 1), "GB": round(ba / 1e9, 3), "GBps": round(ba / (ms_a * 1e-3) / 1e9, 1)},
         "reduce_adamw_fused": {"us": round(ms_f * 1e3, 1), "GB": round(bfz / 1e9, 3),
-                               "GBps": round(bfz / (ms_f * 1e-3) / 1e9, 1)}}
+                               "GBps": round(bfz / (ms_f * 1e-3) / 1e9, 1)},
+        "pack": {"params": bpl.total_numel, "us": round(ms_bp * 1e3, 1), "GB": round(bbp / 1e9, 3),
+                 "GBps": round(bbp / (ms_bp * 1e-3) / 1e9, 1)},
+        "unpack": {"params": bpl.total_numel, "us": round(ms_bu * 1e3, 1), "GB": round(bbu / 1e9, 3),
+                   "GBps": round(bbu / (ms_bu * 1e-3) / 1e9, 1)}}
     return out
 
 
