@@ -156,6 +156,29 @@ def test_pack_unpack_misaligned_buffers(case, shift):
         np.testing.assert_array_equal(bits(o.t), h)
 
 
+@pytest.mark.parametrize("case", [c for c in _layout_cases() if c[0] in (
+    "many_tiles_ragged", "padding_stress_bf16_F", "padding_stress_fp32_T", "llama_block_fsdp2")],
+    ids=lambda c: c[0])
+def test_unpack_aligned_source_misaligned_outputs(case):
+    """A 16-byte-aligned gathered buffer with outputs off their 16-byte
+    boundary: single-run tiles issue their aligned loads, find the
+    destination misaligned, and finish on the segment path."""
+    name, mode, shapes, dt, N, uo = case
+    say("unpack: aligned source, misaligned outputs", name)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    plan = fs.fs_plan(shapes, dt, N, uo, mode).upload()
+    L = _olayout(mode, shapes, dt, N, uo)
+    params = _params(shapes, dt, seed=43)
+    host = [bits(p.t) for p in params]
+    src = Guarded(plan.gathered_numel, tdt, fill=from_bits(oracle.pack(L, host), tdt))
+    outs = [Guarded(p.n, tdt, shift=1 + i % 3) for i, p in enumerate(params)]
+    fs.fs_unpack(plan, src.t, [o.t for o in outs])
+    torch.cuda.synchronize()
+    for o, h in zip(outs, host):
+        o.check()
+        np.testing.assert_array_equal(bits(o.t), h)
+
+
 def test_pack_empty_and_degenerate():
     say("pack empty/degenerate")
     p = fs.fs_plan([(0,), (0, 4)], "bf16", 4, False, "fsdp2").upload()
