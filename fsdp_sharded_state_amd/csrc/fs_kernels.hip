@@ -20,6 +20,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -1124,6 +1125,68 @@ AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
     return c;
 }
 
+// Workgroups resident per CU.  The reduce and AdamW kernels stream HBM best
+// with about 48-64 KB of loads in flight per CU; their register use alone
+// would let more workgroups share a CU (the 32-term reduce three, AdamW
+// eight), and the extra concurrent streams cost DRAM efficiency.  Measured
+// side by side on one MI355X, same buffers, three placements: the 32-term
+// reduce on the 7B shard ran 4-8% faster at one workgroup per CU, AdamW 2-9%
+// at three; on a 70B group's shard the 16-term reduce gained 6% at three,
+// the bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4
+// groups).  The copy kernels keep full occupancy: eight 8 KB tiles per CU
+// are already in that range, and fewer measured slower.  A cap of k is set
+// by reserving dynamic LDS that the kernel never touches: with L bytes of
+// LDS per CU, L / (k + 1) + 1 bytes per workgroup let k workgroups fit but
+// not k + 1.  Grids shorter than kCapMinRounds rounds of resident
+// workgroups keep full occupancy: the last round of a short grid weighs
+// more than the DRAM gain (one block's 8-term reduce measured 2% slower
+// capped).
+constexpr int kRedManyWgsPerCu = 1;    // reduce_chunk_kernel<kRedGroupsMany>
+constexpr int kRedFewWgsPerCu = 3;     // reduce_chunk_kernel<kRedGroupsFew>
+constexpr int kRsManyWgsPerCu = 2;     // reduce_rs_chunk_kernel<kRsGroupsMany>
+constexpr int kRsFewWgsPerCu = 3;      // reduce_rs_chunk_kernel<kRsGroupsFew>
+constexpr int kAdamWgsPerCu = 3;       // adamw_kernel
+constexpr int64_t kCapMinRounds = 16;
+
+struct CuLimits {
+    int lds_per_cu = 0, lds_per_wg = 0, cus = 0;   // 0: unknown, no cap
+};
+
+CuLimits cu_limits() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> lds_cu[kMaxDev], lds_wg[kMaxDev], ncu[kMaxDev];   // 0: not read yet, -1: failed
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return {};
+    if (lds_cu[dev].load(std::memory_order_acquire) == 0) {
+        int a = 0, b = 0, c = 0;
+        const bool ok = hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) ==
+                            hipSuccess &&
+                        hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+                        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                        a > 0 && b > 0 && c > 0;
+        lds_wg[dev].store(ok ? b : -1, std::memory_order_relaxed);
+        ncu[dev].store(ok ? c : -1, std::memory_order_relaxed);
+        lds_cu[dev].store(ok ? a : -1, std::memory_order_release);
+    }
+    CuLimits L;
+    if (lds_cu[dev].load(std::memory_order_acquire) < 0) return L;
+    L.lds_per_cu = lds_cu[dev].load(std::memory_order_relaxed);
+    L.lds_per_wg = lds_wg[dev].load(std::memory_order_relaxed);
+    L.cus = ncu[dev].load(std::memory_order_relaxed);
+    return L;
+}
+
+// Dynamic LDS bytes for a grid of `grid` workgroups capped at k per CU (0:
+// no cap).
+uint32_t lds_cap(int k, int64_t grid) {
+    const CuLimits L = cu_limits();
+    if (L.lds_per_cu <= 0 || k < 1) return 0;
+    if (grid < kCapMinRounds * k * (int64_t)L.cus) return 0;
+    const int64_t bytes = L.lds_per_cu / (k + 1) + 1;
+    if (bytes > L.lds_per_wg || bytes * k > L.lds_per_cu) return 0;
+    return (uint32_t)bytes;
+}
+
 int check_hparams(const char *what, const fs_adamw_hparams_t *hp) {
     if (!hp) return fsi::fail(FS_E_INVAL, "%s: hp is NULL", what);
     if (hp->step < 1) return fsi::fail(FS_E_INVAL, "%s: step must be >= 1", what);
@@ -1195,11 +1258,12 @@ void launch_reduce_pass(int64_t n, hipStream_t stream, const uint16_t *const *sl
         const bool few = cnt <= kRedFewTerms;
         const int64_t chunk = few ? kRedChunkFew : kRedChunk;
         const dim3 g((uint32_t)((n + chunk - 1) / chunk));
+        const uint32_t lds = lds_cap(few ? kRedFewWgsPerCu : kRedManyWgsPerCu, g.x);
         if (few)
-            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsFew>, g, dim3(kThreads), 0, stream, sa, cnt, first, last,
-                               world, out, n);
+            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsFew>, g, dim3(kThreads), lds, stream, sa, cnt, first,
+                               last, world, out, n);
         else
-            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsMany>, g, dim3(kThreads), 0, stream, sa, cnt, first,
+            hipLaunchKernelGGL(reduce_chunk_kernel<kRedGroupsMany>, g, dim3(kThreads), lds, stream, sa, cnt, first,
                                last, world, out, n);
     } else {
         const int64_t grid = std::max<int64_t>(1, ((n >> 3) + kThreads - 1) / kThreads);
@@ -1487,11 +1551,12 @@ extern "C" int fs_reduce_shard_ex(int64_t n, int32_t world, int32_t grad_acc, fs
             const bool few = steps * world <= kRedFewTerms;
             const int64_t chunk = kWgRow * (few ? kRsGroupsFew : kRsGroupsMany);
             const dim3 g((uint32_t)((n + chunk - 1) / chunk));
+            const uint32_t lds = lds_cap(few ? kRsFewWgsPerCu : kRsManyWgsPerCu, g.x);
             if (few)
-                hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsFew>, g, dim3(kThreads), 0, stream, sa, steps,
+                hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsFew>, g, dim3(kThreads), lds, stream, sa, steps,
                                    (int)world, first, (float)world, out, n);
             else
-                hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsMany>, g, dim3(kThreads), 0, stream, sa, steps,
+                hipLaunchKernelGGL(reduce_rs_chunk_kernel<kRsGroupsMany>, g, dim3(kThreads), lds, stream, sa, steps,
                                    (int)world, first, (float)world, out, n);
         } else {
             const int64_t grid = std::max<int64_t>(1, ((n >> 3) + kThreads - 1) / kThreads);
@@ -1563,19 +1628,20 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
     (void)hipGetLastError();
     if (aligned) {
         const dim3 g((uint32_t)((n + kWgRow - 1) / kWgRow)), b(kThreads);
+        const uint32_t lds = lds_cap(kAdamWgsPerCu, g.x);
         if (grad_dtype == FS_BF16) {
             if (param_bf16)
-                hipLaunchKernelGGL((adamw_kernel<true, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                hipLaunchKernelGGL((adamw_kernel<true, true>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
                                    param_bf16, c, n);
             else
-                hipLaunchKernelGGL((adamw_kernel<true, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                hipLaunchKernelGGL((adamw_kernel<true, false>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
                                    param_bf16, c, n);
         } else {
             if (param_bf16)
-                hipLaunchKernelGGL((adamw_kernel<false, true>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                hipLaunchKernelGGL((adamw_kernel<false, true>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
                                    param_bf16, c, n);
             else
-                hipLaunchKernelGGL((adamw_kernel<false, false>), g, b, 0, stream, master, exp_avg, exp_avg_sq, grad,
+                hipLaunchKernelGGL((adamw_kernel<false, false>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
                                    param_bf16, c, n);
         }
     } else {
