@@ -1071,17 +1071,24 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArg
 
 // ------------------------------------------------------------------ copy --
 
-// Read-only and write-only streams (measurement aids), dwordx4 accesses with
-// every instruction covering 4 KB of the workgroup's contiguous range: the
-// read stream keeps 16 loads per lane in flight (64 KB per workgroup; 4 per
-// lane measured 3% slower), the write stream 4 stores per lane.
-constexpr int kReadVecs = 16;
+// Streaming ceilings (measurement aids): read-only, write-only and copy
+// kernels, dwordx4 accesses, every instruction covering 4 KB of the
+// workgroup's contiguous range, each in the shape that measured fastest on
+// MI355X.  Reads want many loads in flight: two per lane at full occupancy
+// (7.2 TB/s; 16 per lane 7.1).  Writes want few stores outstanding per CU:
+// two per lane at one workgroup per CU (7.2 TB/s), against 5.8 for four per
+// lane at full occupancy.  A copy mixes both: two blocks per lane at three
+// workgroups per CU (6.6 TB/s; one block at full occupancy 6.5).
+constexpr int kStreamVecs = 2;         // 16-byte blocks per lane
+constexpr int kFillWgsPerCu = 1;
+constexpr int kCopyWgsPerCu = 3;
+
 __global__ __launch_bounds__(kThreads) void read_kernel(const char *__restrict__ src, int64_t nvec,
                                                         uint32_t *__restrict__ sink) {
-    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kReadVecs + threadIdx.x;
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kStreamVecs + threadIdx.x;
     uint32_t x = 0;
 #pragma unroll
-    for (int u = 0; u < kReadVecs; ++u) {
+    for (int u = 0; u < kStreamVecs; ++u) {
         const int64_t i = i0 + u * kThreads;
         if (i < nvec) {
             const u32x4 v = ld16(src + 16 * i);
@@ -1092,10 +1099,10 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const char *__restrict__
 }
 
 __global__ __launch_bounds__(kThreads) void fill_kernel(char *__restrict__ dst, int64_t nvec, uint32_t value) {
-    const int64_t i0 = (int64_t)blockIdx.x * kThreads * 4 + threadIdx.x;
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kStreamVecs + threadIdx.x;
     const u32x4 v = {value, value, value, value};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kStreamVecs; ++u) {
         const int64_t i = i0 + u * kThreads;
         if (i < nvec) st16(dst + 16 * i, v);
     }
@@ -1103,8 +1110,14 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(char *__restrict__ dst, 
 
 __global__ __launch_bounds__(kThreads) void copy_kernel(char *__restrict__ dst,
                                                         const char *__restrict__ src, int64_t nvec) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < nvec) st16(dst + 16 * i, ld16(src + 16 * i));
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kStreamVecs + threadIdx.x;
+    u32x4 v[kStreamVecs];
+#pragma unroll
+    for (int u = 0; u < kStreamVecs; ++u)
+        if (i0 + u * kThreads < nvec) v[u] = ld16(src + 16 * (i0 + u * kThreads));
+#pragma unroll
+    for (int u = 0; u < kStreamVecs; ++u)
+        if (i0 + u * kThreads < nvec) st16(dst + 16 * (i0 + u * kThreads), v[u]);
 }
 
 // -------------------------------------------------------------- launchers --
@@ -1790,7 +1803,7 @@ extern "C" int fs_stream_read(const void *src, int64_t bytes, uint32_t *sink, hi
     if (!src || !sink) return fsi::fail(FS_E_INVAL, "fs_stream_read: NULL pointer");
     if (misaligned(src, 16) || misaligned(sink, 4)) return fsi::fail(FS_E_ALIGN, "fs_stream_read: misaligned pointer");
     const int64_t nvec = bytes / 16;
-    const int64_t grid = (nvec + kReadVecs * kThreads - 1) / (kReadVecs * kThreads);
+    const int64_t grid = (nvec + kStreamVecs * kThreads - 1) / (kStreamVecs * kThreads);
     if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_stream_read: too large for one launch");
     (void)hipGetLastError();
     hipLaunchKernelGGL(read_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, static_cast<const char *>(src),
@@ -1805,11 +1818,11 @@ extern "C" int fs_stream_fill(void *dst, int64_t bytes, uint32_t value, hipStrea
     if (!dst) return fsi::fail(FS_E_INVAL, "fs_stream_fill: NULL pointer");
     if (misaligned(dst, 16)) return fsi::fail(FS_E_ALIGN, "fs_stream_fill: dst must be 16-byte aligned");
     const int64_t nvec = bytes / 16;
-    const int64_t grid = (nvec + 4 * kThreads - 1) / (4 * kThreads);
+    const int64_t grid = (nvec + kStreamVecs * kThreads - 1) / (kStreamVecs * kThreads);
     if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_stream_fill: too large for one launch");
     (void)hipGetLastError();
-    hipLaunchKernelGGL(fill_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, static_cast<char *>(dst), nvec,
-                       value);
+    hipLaunchKernelGGL(fill_kernel, dim3((uint32_t)grid), dim3(kThreads), lds_cap(kFillWgsPerCu, grid), stream,
+                       static_cast<char *>(dst), nvec, value);
     return check_launch("fs_stream_fill");
 }
 
@@ -1821,10 +1834,10 @@ extern "C" int fs_copy_bytes(void *dst, const void *src, int64_t bytes, hipStrea
     if (misaligned(dst, 16) || misaligned(src, 16)) return fsi::fail(FS_E_ALIGN, "fs_copy_bytes: pointers must be 16-byte aligned");
     if (ranges_overlap(dst, bytes, src, bytes)) return fsi::fail(FS_E_INVAL, "fs_copy_bytes: ranges overlap");
     const int64_t nvec = bytes / 16;
-    const int64_t grid = (nvec + kThreads - 1) / kThreads;
+    const int64_t grid = (nvec + kStreamVecs * kThreads - 1) / (kStreamVecs * kThreads);
     if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_copy_bytes: too large for one launch");
     (void)hipGetLastError();
-    hipLaunchKernelGGL(copy_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, static_cast<char *>(dst),
-                       static_cast<const char *>(src), nvec);
+    hipLaunchKernelGGL(copy_kernel, dim3((uint32_t)grid), dim3(kThreads), lds_cap(kCopyWgsPerCu, grid), stream,
+                       static_cast<char *>(dst), static_cast<const char *>(src), nvec);
     return check_launch("fs_copy_bytes");
 }

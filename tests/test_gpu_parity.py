@@ -633,10 +633,14 @@ def test_reduce_adamw_fused_special_values(n, N, A):
     np.testing.assert_array_equal(bits(p2.t), bits(pf.t))
 
 
-def test_stream_read_and_fill():
+@pytest.mark.parametrize("n", [(1 << 20) + 4 * 256 * 3 + 4, (1 << 24) + 4 * 256 * 3 + 4],
+                         ids=["small_grid", "capped_grid"])
+def test_stream_read_fill_and_copy(n):
     """The measurement aids: fill writes its word everywhere (and only inside
-    the buffer); read leaves its source untouched."""
-    n = (1 << 20) + 4 * 256 * 3 + 4    # not a whole number of workgroups
+    the buffer); read leaves its source untouched; copy reproduces its source
+    bit for bit.  n is not a whole number of workgroups; the larger size is
+    long enough for the launches' resident-workgroup caps to apply."""
+    say("stream read / fill / copy", n)
     g = Guarded(n, torch.float32)
     fs.fs_stream_fill(g.t, 0x3F800000)
     torch.cuda.synchronize()
@@ -649,6 +653,11 @@ def test_stream_read_and_fill():
     torch.cuda.synchronize()
     src.check()
     np.testing.assert_array_equal(bits(src.t), before)
+    dst = Guarded(n, torch.float32)
+    fs.fs_copy_bytes(dst.t, src.t)
+    torch.cuda.synchronize()
+    dst.check()
+    np.testing.assert_array_equal(bits(dst.t), before)
 
 
 def test_deterministic_across_runs_and_streams():
