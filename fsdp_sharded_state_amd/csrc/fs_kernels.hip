@@ -869,12 +869,16 @@ __device__ __forceinline__ void store_bf16_group(uint16_t *p, int64_t base, int 
 }
 
 // Main AdamW kernel (all buffers 16-byte aligned): one group of 4 elements per
-// lane, 1024 elements per workgroup, so each wave's load or store of an array
-// covers 1 KB (fp32) or 512 B (bf16) contiguous.  At about 50 registers the
-// kernel runs 8 waves per SIMD; small workgroups keep the last round of a
-// launch short (one Llama-7B block's shard, 25.3M elements: 117 us against
-// 143 us for 8192-element workgroups with a separate remainder launch) and
-// measured equal on the 842M-element shard.
+// lane and one wave per workgroup (256 elements), so each load or store of an
+// array covers 1 KB (fp32) or 512 B (bf16) contiguous.  The kernel needs about
+// 50 registers; its launch caps residency at twelve workgroups (waves) per CU.
+// Small workgroups keep the last round of a launch short (one Llama-7B
+// block's shard, 25.3M elements: 117 us for 1024-element workgroups against
+// 143 us for 8192-element ones with a separate remainder launch); single-wave
+// workgroups at twelve per CU measured 2-4% faster than 1024-element ones at
+// three per CU on two of three placements and equal on the third.
+constexpr int kAdamThreads = 64;
+constexpr int64_t kAdamRow = (int64_t)kAdamThreads * 4;   // elements per workgroup
 template <bool GRAD_BF16, bool HAS_P16, bool TAIL>
 __device__ __forceinline__ void adamw_group(float *__restrict__ th, float *__restrict__ m, float *__restrict__ v,
                                             const void *__restrict__ grad, uint16_t *__restrict__ p16,
@@ -901,11 +905,11 @@ __device__ __forceinline__ void adamw_group(float *__restrict__ th, float *__res
 }
 
 template <bool GRAD_BF16, bool HAS_P16>
-__global__ __launch_bounds__(kThreads) void adamw_kernel(float *__restrict__ th, float *__restrict__ m,
-                                                         float *__restrict__ v, const void *__restrict__ grad,
-                                                         uint16_t *__restrict__ p16, AdamConsts c, int64_t n) {
-    const int64_t e = (int64_t)blockIdx.x * kWgRow + 4 * threadIdx.x;
-    if ((int64_t)(blockIdx.x + 1) * kWgRow <= n)
+__global__ __launch_bounds__(kAdamThreads) void adamw_kernel(float *__restrict__ th, float *__restrict__ m,
+                                                             float *__restrict__ v, const void *__restrict__ grad,
+                                                             uint16_t *__restrict__ p16, AdamConsts c, int64_t n) {
+    const int64_t e = (int64_t)blockIdx.x * kAdamRow + 4 * threadIdx.x;
+    if ((int64_t)(blockIdx.x + 1) * kAdamRow <= n)
         adamw_group<GRAD_BF16, HAS_P16, false>(th, m, v, grad, p16, c, e, n);
     else
         adamw_group<GRAD_BF16, HAS_P16, true>(th, m, v, grad, p16, c, e, n);
@@ -1141,10 +1145,11 @@ AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
 // Workgroups resident per CU.  The reduce and AdamW kernels stream HBM best
 // with about 48-64 KB of loads in flight per CU; their register use alone
 // would let more workgroups share a CU (the 32-term reduce three, AdamW
-// eight), and the extra concurrent streams cost DRAM efficiency.  Measured
-// side by side on one MI355X, same buffers, three placements: the 32-term
-// reduce on the 7B shard ran 4-8% faster at one workgroup per CU, AdamW 2-9%
-// at three; on a 70B group's shard the 16-term reduce gained 6% at three,
+// eight waves per SIMD), and the extra concurrent streams cost DRAM
+// efficiency.  Measured side by side on one MI355X, same buffers, three
+// placements: the 32-term reduce on the 7B shard ran 4-8% faster at one
+// workgroup per CU, AdamW 2-9% at three 4-wave workgroups (twelve waves) per
+// CU; on a 70B group's shard the 16-term reduce gained 6% at three,
 // the bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4
 // groups).  The copy kernels keep full occupancy: eight 8 KB tiles per CU
 // are already in that range, and fewer measured slower.  A cap of k is set
@@ -1158,7 +1163,7 @@ constexpr int kRedManyWgsPerCu = 1;    // reduce_chunk_kernel<kRedGroupsMany>
 constexpr int kRedFewWgsPerCu = 3;     // reduce_chunk_kernel<kRedGroupsFew>
 constexpr int kRsManyWgsPerCu = 2;     // reduce_rs_chunk_kernel<kRsGroupsMany>
 constexpr int kRsFewWgsPerCu = 3;      // reduce_rs_chunk_kernel<kRsGroupsFew>
-constexpr int kAdamWgsPerCu = 3;       // adamw_kernel
+constexpr int kAdamWgsPerCu = 12;      // adamw_kernel (one wave per workgroup)
 constexpr int64_t kCapMinRounds = 16;
 
 struct CuLimits {
@@ -1285,11 +1290,11 @@ void launch_reduce_pass(int64_t n, hipStream_t stream, const uint16_t *const *sl
     }
 }
 
-// Largest grid any launch over n elements needs: one workgroup per kWgRow
+// Largest grid any launch over n elements needs: one workgroup per kAdamRow
 // elements (AdamW) bounds every chunked kernel; the general kernels use one
 // lane per 8 elements.
 bool grid_fits(int64_t n) {
-    return (n + kWgRow - 1) / kWgRow <= INT32_MAX && ((n >> 3) + kThreads - 1) / kThreads <= INT32_MAX;
+    return (n + kAdamRow - 1) / kAdamRow <= INT32_MAX && ((n >> 3) + kThreads - 1) / kThreads <= INT32_MAX;
 }
 
 bool ranges_overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
@@ -1640,7 +1645,7 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
     if (!grid_fits(n)) return fsi::fail(FS_E_OVERFLOW, "fs_adamw_step: n too large for one launch");
     (void)hipGetLastError();
     if (aligned) {
-        const dim3 g((uint32_t)((n + kWgRow - 1) / kWgRow)), b(kThreads);
+        const dim3 g((uint32_t)((n + kAdamRow - 1) / kAdamRow)), b(kAdamThreads);
         const uint32_t lds = lds_cap(kAdamWgsPerCu, g.x);
         if (grad_dtype == FS_BF16) {
             if (param_bf16)
