@@ -1081,11 +1081,15 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_general_kernel(SliceArg
 // MI355X.  Reads want many loads in flight: two per lane at full occupancy
 // (7.2 TB/s; 16 per lane 7.1).  Writes want few stores outstanding per CU:
 // two per lane at one workgroup per CU (7.2 TB/s), against 5.8 for four per
-// lane at full occupancy.  A copy mixes both: two blocks per lane at three
-// workgroups per CU (6.6 TB/s; one block at full occupancy 6.5).
-constexpr int kStreamVecs = 2;         // 16-byte blocks per lane
+// lane at full occupancy.  A copy mixes both: one block per lane in
+// single-wave workgroups at full occupancy copies 6.7 TB/s (256-thread
+// workgroups: 6.6 at two blocks per lane and three per CU, 6.5 at one block
+// uncapped).  Read and write streams do not take single-wave workgroups of
+// one block per lane: at 1 KB per workgroup the dispatcher's rate of about
+// two workgroups per clock caps them near 4.8 TB/s.
+constexpr int kStreamVecs = 2;         // 16-byte blocks per lane (read, fill)
 constexpr int kFillWgsPerCu = 1;
-constexpr int kCopyWgsPerCu = 3;
+constexpr int kCopyThreads = 64;       // one wave per workgroup, one block per lane
 
 __global__ __launch_bounds__(kThreads) void read_kernel(const char *__restrict__ src, int64_t nvec,
                                                         uint32_t *__restrict__ sink) {
@@ -1112,16 +1116,10 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(char *__restrict__ dst, 
     }
 }
 
-__global__ __launch_bounds__(kThreads) void copy_kernel(char *__restrict__ dst,
-                                                        const char *__restrict__ src, int64_t nvec) {
-    const int64_t i0 = (int64_t)blockIdx.x * kThreads * kStreamVecs + threadIdx.x;
-    u32x4 v[kStreamVecs];
-#pragma unroll
-    for (int u = 0; u < kStreamVecs; ++u)
-        if (i0 + u * kThreads < nvec) v[u] = ld16(src + 16 * (i0 + u * kThreads));
-#pragma unroll
-    for (int u = 0; u < kStreamVecs; ++u)
-        if (i0 + u * kThreads < nvec) st16(dst + 16 * (i0 + u * kThreads), v[u]);
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(char *__restrict__ dst,
+                                                            const char *__restrict__ src, int64_t nvec) {
+    const int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (i < nvec) st16(dst + 16 * i, ld16(src + 16 * i));
 }
 
 // -------------------------------------------------------------- launchers --
@@ -1839,10 +1837,10 @@ extern "C" int fs_copy_bytes(void *dst, const void *src, int64_t bytes, hipStrea
     if (misaligned(dst, 16) || misaligned(src, 16)) return fsi::fail(FS_E_ALIGN, "fs_copy_bytes: pointers must be 16-byte aligned");
     if (ranges_overlap(dst, bytes, src, bytes)) return fsi::fail(FS_E_INVAL, "fs_copy_bytes: ranges overlap");
     const int64_t nvec = bytes / 16;
-    const int64_t grid = (nvec + kStreamVecs * kThreads - 1) / (kStreamVecs * kThreads);
+    const int64_t grid = (nvec + kCopyThreads - 1) / kCopyThreads;
     if (grid > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_copy_bytes: too large for one launch");
     (void)hipGetLastError();
-    hipLaunchKernelGGL(copy_kernel, dim3((uint32_t)grid), dim3(kThreads), lds_cap(kCopyWgsPerCu, grid), stream,
-                       static_cast<char *>(dst), static_cast<const char *>(src), nvec);
+    hipLaunchKernelGGL(copy_kernel, dim3((uint32_t)grid), dim3(kCopyThreads), 0, stream, static_cast<char *>(dst),
+                       static_cast<const char *>(src), nvec);
     return check_launch("fs_copy_bytes");
 }
