@@ -4,8 +4,9 @@
 // unpack move bytes, the reduce does one fp32 add per input element, AdamW a
 // few dozen flops per 30 bytes.  None is a contraction, so none uses MFMA;
 // the design goals are 16-byte (dwordx4) accesses on every lane, enough loads
-// in flight per wave to cover HBM latency, and no divergent control flow at
-// layout boundaries.
+// in flight to cover HBM latency but not so many concurrent streams per CU
+// that the DRAM loses efficiency (the reduce and AdamW launches cap their
+// resident workgroups), and no divergent control flow at layout boundaries.
 //
 // Sources (page title, section):
 //   pack / unpack: "FSDP1 vs FSDP2", section 03 (FlatParameter padding and
@@ -470,9 +471,10 @@ __global__ __launch_bounds__(kThreads) void pack_cast_kernel(const Segment *__re
 // workgroup little work, and G = 4 (more, shorter workgroups) measured 6-10%
 // faster there (8 terms) and no slower at 16.
 //
-// General kernel (misaligned slices or output, and the chunk remainder):
-// lane i owns 8 consecutive elements, one 16-byte (funnel-shifted when
-// misaligned) load per term, plus an element-wise tail.
+// General kernel (misaligned slices or output): lane i owns 8 consecutive
+// elements, one 16-byte (funnel-shifted when misaligned) load per term, plus
+// an element-wise tail.  The main kernel covers a partial last chunk itself
+// (see the chunk dispatch below).
 //
 // More than kTermsPerPass terms run as chained passes that carry the fp32
 // partial sum through `out` -- the same arithmetic as one pass.

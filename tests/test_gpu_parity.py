@@ -309,17 +309,20 @@ def _adam_inputs(n, seed, step, grad_bf16, shift=0):
     return G, Gg, P
 
 
+ADAM_WG = 256   # elements per workgroup of the aligned AdamW kernel (one wave, 4 per lane)
 ADAM_CASES = [
-    # (n, step, grad_bf16, with p16, shift); the aligned kernel works in
-    # 1024-element workgroups, the last one cut by n
+    # (n, step, grad_bf16, with p16, shift); the aligned kernel's last
+    # workgroup is cut by n
     (1, 1, False, True, 0), (7, 1, False, True, 0), (8, 2, True, True, 0), (1003, 1000, False, True, 0),
-    (1023, 3, False, False, 0), (1024, 1, False, False, 0), (1025, 2, True, False, 0),
+    (ADAM_WG - 1, 3, False, False, 0), (ADAM_WG, 1, False, False, 0), (ADAM_WG + 1, 2, True, False, 0),
+    (4 * ADAM_WG - 1, 3, False, False, 0), (4 * ADAM_WG, 1, False, False, 0), (4 * ADAM_WG + 1, 2, True, False, 0),
     (1 << 20, 1, False, True, 0), (1 << 20, 1000, True, False, 0), (4101, 7, False, True, 1),
     # every <bf16 grad, bf16 copy> build over whole workgroups plus a ragged last one
-    (1024 * 13 + 3, 3, True, True, 0), (1024 * 7 + 2, 5, False, False, 0),
-    (1024 * 9 + 1, 4, True, False, 0), (1024 * 11 + 3, 6, False, True, 0),
+    (ADAM_WG * 53 + 3, 3, True, True, 0), (ADAM_WG * 29 + 2, 5, False, False, 0),
+    (ADAM_WG * 37 + 1, 4, True, False, 0), (ADAM_WG * 45 + 3, 6, False, True, 0),
     (50003, 9, True, True, 2),
-    (25_297_920, 1000, False, True, 0),
+    # long enough for the launch's resident-workgroup cap (at least 16 rounds)
+    (25_297_920, 1000, False, True, 0), (ADAM_WG * 60_001 + 2, 11, True, True, 0),
 ]
 
 
