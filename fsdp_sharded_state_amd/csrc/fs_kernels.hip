@@ -461,15 +461,18 @@ __global__ __launch_bounds__(kThreads) void pack_cast_kernel(const Segment *__re
 // Main kernel (16-byte-aligned slices and output): a workgroup owns a chunk
 // of kThreads*4*G elements and walks the slices one after another, reading G
 // groups of 4 bf16 (8 bytes) per lane from the current slice -- 2*G KB
-// contiguous per slice per workgroup -- while the next slice's loads are
-// already in flight (two register slots).  The 4*G fp32 accumulators live in
+// contiguous per slice per workgroup.  The 4*G fp32 accumulators live in
 // registers; the chunk is written once, 16 bytes per lane, every store
 // instruction covering 1 KB contiguous.  Reading each slice in long
 // contiguous runs keeps the HBM row buffers busy on one stream at a time,
-// which measured faster than interleaving all slices per element.  G = 16
-// (32 KB per slice) for passes of more than 16 terms; fewer terms give each
-// workgroup little work, and G = 4 (more, shorter workgroups) measured 6-10%
-// faster there (8 terms) and no slower at 16.
+// which measured faster than interleaving all slices per element.  Passes of
+// more than 16 terms use G = 32 (64 KB per slice) with one slice in flight,
+// at one workgroup per CU: against G = 16 with two slices in flight (the
+// same 64 KB in flight, 32 KB runs) it measured 3% faster on two of three
+// placements and 1% slower on the third; G = 24 was slower on all three.
+// Fewer terms give each workgroup little work, and G = 4 with two slices in
+// flight (more, shorter workgroups) measured 6-10% faster there (8 terms)
+// and no slower at 16.
 //
 // General kernel (misaligned slices or output): lane i owns 8 consecutive
 // elements, one 16-byte (funnel-shifted when misaligned) load per term, plus
@@ -567,11 +570,11 @@ __global__ __launch_bounds__(kThreads) void reduce_general_kernel(SliceArgs sa, 
     }
 }
 
-constexpr int kRedGroupsMany = 16;                                      // passes of > kRedFewTerms terms
+constexpr int kRedGroupsMany = 32;                                      // passes of > kRedFewTerms terms
 constexpr int kRedGroupsFew = 4;                                        // passes of <= kRedFewTerms terms
 constexpr int kRedFewTerms = 16;
 constexpr int64_t kWgRow = (int64_t)kThreads * 4;                       // elements of one group index across a workgroup
-constexpr int64_t kRedChunk = kWgRow * kRedGroupsMany;                  // 16384 elements
+constexpr int64_t kRedChunk = kWgRow * kRedGroupsMany;                  // 32768 elements
 constexpr int64_t kRedChunkFew = kWgRow * kRedGroupsFew;                // 4096 elements
 
 __device__ __forceinline__ void f4(u32x4 v, float o[4]) {
@@ -689,7 +692,7 @@ __device__ __forceinline__ void reduce_chunk(const SliceArgs &sa, int nterms, in
     const Bounds<G, TAIL> B(base, n);
     float acc[4 * G];
     if (!first_pass) load_f32_groups<G, G, TAIL>(acc, out, base, B);   // partial sums of the earlier passes
-    sum_slices<G, 2, TAIL>(sa, nterms, first_pass, acc, base, B);
+    sum_slices<G, (G >= 32 ? 1 : 2), TAIL>(sa, nterms, first_pass, acc, base, B);   // slices in flight
     if (last_pass) {
 #pragma unroll
         for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;

@@ -210,6 +210,8 @@ def _slices(n, terms, seed, shift=0, sigma=1e-3, specials=False):
     return out
 
 
+RED_CHUNK = 32768     # elements per workgroup of the reduce's passes of more than 16 terms
+RED_SUB = 4096        # the partial last chunk is walked in sub-chunks of this many elements
 REDUCE_CASES = [
     # (n, world, grad_acc, slice shift, out shift)
     (1, 1, 1, 0, 0), (7, 2, 1, 0, 0), (8, 8, 1, 0, 0), (9, 3, 1, 0, 0),
@@ -218,7 +220,11 @@ REDUCE_CASES = [
     (3001, 2, 33, 0, 0),         # 66 terms: three passes
     (40000, 8, 5, 0, 0),         # 40 terms over whole 16384-element chunks + remainder
     (20000 + 7, 2, 33, 0, 0),    # 66 terms, chunks + ragged remainder
-    (16384 * 3, 8, 4, 0, 0),     # whole chunks only
+    (16384 * 3, 8, 4, 0, 0),     # one and a half chunks
+    (RED_CHUNK * 3, 8, 4, 0, 0), # whole chunks only
+    (RED_CHUNK * 2 + RED_SUB * 7 + 5, 8, 4, 0, 0),   # last chunk: eight sub-chunks, 5 elements in the eighth
+    (RED_CHUNK + RED_SUB - 1, 4, 8, 0, 0),           # last chunk: one sub-chunk, a straddling group of 3
+    (RED_CHUNK - 1, 8, 4, 0, 0), (RED_CHUNK + 1, 8, 4, 0, 0),
     (4097, 8, 4, 1, 0), (4097, 8, 4, 3, 1), (4096, 4, 2, 0, 2),   # misaligned slices / out
     (70001, 8, 4, 1, 0),         # misaligned, large
     (30011, 5, 7, 0, 0),         # 35 terms: a 32-term pass (long chunks), then 3 terms (short chunks)
