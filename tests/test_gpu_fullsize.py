@@ -2,7 +2,9 @@
 grad_acc = 4, S = 842,301,440), in the launch configuration the benchmark
 times (one fs_reduce_shard over 32 separate bf16 slices, one fs_adamw_step
 with an fp32 gradient and a bf16 copy, fs_pack with rank -1 and fs_unpack
-per group).
+per group), plus the bf16 reduce dtype and the fused reduce + AdamW over the
+same slices; at these sizes the reduce and AdamW launches cap their
+resident workgroups.
 
 The oracle cannot run the whole shard here, so it computes sampled outputs
 one by one from inputs it regenerates itself (synth is counter-based: element
@@ -60,10 +62,20 @@ def test_fullsize_reduce_and_adamw(plans):
     g32 = torch.empty(S, dtype=torch.float32, device="cuda")
     say("full-size reduce: launch")
     fs.fs_reduce_shard(slices, g32, N, A)
+    # the bf16 reduce dtype over the same slices (its launches cap residency at this size)
+    g_rs = torch.empty(S, dtype=torch.float32, device="cuda")
+    say("full-size bf16 reduce dtype: launch")
+    fs.fs_reduce_shard_ex(slices, g_rs, N, A, reduce_dtype="bf16")
     master = synth.normal_f32(SEED, synth.STREAM_MASTER, S, 0.02, device="cuda")
     m = torch.zeros(S, device="cuda")
     v = torch.zeros(S, device="cuda")
     p16 = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    # the fused step from the same state: bit-identical to the two kernels below
+    fmaster, fm, fv = master.clone(), torch.zeros(S, device="cuda"), torch.zeros(S, device="cuda")
+    fp16 = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    say("full-size fused reduce + AdamW: launch")
+    fs.fs_reduce_adamw_step(slices, fmaster, fm, fv, fp16, None, world=N, grad_acc=A, lr=1e-3, beta1=0.9,
+                            beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
     del slices
     say("full-size AdamW: launch")
     fs.fs_adamw_step(master, m, v, g32, p16, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
@@ -79,6 +91,9 @@ def test_fullsize_reduce_and_adamw(plans):
     it_dev = it.cuda()
     got_g = g32[it_dev].cpu().numpy()
     np.testing.assert_array_equal(got_g.view(np.uint32), ref_g.view(np.uint32))
+    ref_rs = oracle.reduce_shard_bf16rs(sl_host, N, A)
+    np.testing.assert_array_equal(g_rs[it_dev].cpu().numpy().view(np.uint32), ref_rs.view(np.uint32))
+    del g_rs
 
     th0 = synth.normal_f32_at(SEED, synth.STREAM_MASTER, it, 0.02).numpy()
     z = np.zeros(idx.size, np.float32)
@@ -94,6 +109,9 @@ def test_fullsize_reduce_and_adamw(plans):
     inexact = np.mean((gt.view(np.uint32) != rt.view(np.uint32)) | (gm.view(np.uint32) != rm.view(np.uint32)) |
                       (gv.view(np.uint32) != rv.view(np.uint32)))
     assert inexact <= 1e-6, inexact
+    for a, b in ((fmaster, master), (fm, m), (fv, v)):
+        np.testing.assert_array_equal(a[it_dev].cpu().numpy().view(np.uint32), b[it_dev].cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(bits(fp16[it_dev]), bits(p16[it_dev]))
 
 
 @pytest.mark.parametrize("which", ["block0", "block31", "root"])
@@ -202,6 +220,8 @@ def test_fullsize_70b_group_reduce_pack_unpack(plans70, which):
               for j in range(A70) for k in range(N70)]
     out = torch.empty(n, dtype=torch.float32, device="cuda")
     fs.fs_reduce_shard(slices, out, N70, A70)
+    out_rs = torch.empty(n, dtype=torch.float32, device="cuda")
+    fs.fs_reduce_shard_ex(slices, out_rs, N70, A70, reduce_dtype="bf16")
     torch.cuda.synchronize()
     del slices
     idx = _sample(n, 100_000, np.random.default_rng(gi))
@@ -210,7 +230,9 @@ def test_fullsize_70b_group_reduce_pack_unpack(plans70, which):
                for j in range(A70) for k in range(N70)]
     ref = oracle.reduce_shard(sl_host, N70, A70)
     np.testing.assert_array_equal(out[it.cuda()].cpu().numpy().view(np.uint32), ref.view(np.uint32))
-    del out
+    ref_rs = oracle.reduce_shard_bf16rs(sl_host, N70, A70)
+    np.testing.assert_array_equal(out_rs[it.cuda()].cpu().numpy().view(np.uint32), ref_rs.view(np.uint32))
+    del out, out_rs
 
     say("70B group pack/unpack", which)
     off = sum(math.prod(s) for g in groups[:gi] for s in g)
