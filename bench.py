@@ -701,8 +701,12 @@ def traffic_for(kernel: str, launch_bytes_alg: float):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+# the reduce's kernel for passes of more than 16 terms (its template argument
+# is the number of 4-element groups per lane)
+REDUCE_KERNEL = "reduce_chunk_kernel<32>"
+
 KERNELS = {  # rocprofv3 kernel-name fragment -> bench phase
-    "reduce_chunk_kernel<16>": "reduce",
+    REDUCE_KERNEL: "reduce",
     "scatter_kernel<2, (anonymous namespace)::UnpackSrc": "reshard",
     "reduce_rs_chunk_kernel": "reduce_bf16_reduce_dtype",
     "pack_cast_kernel": "pack_cast",
@@ -755,7 +759,7 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     f_write = copy_bytes / (avg["copy_kernel"]["WRITE_SIZE"] * 1024)
     # algorithmic bytes per launch of the 7B shard step
     S, N, A = 842301440, 8, 4
-    alg = {"reduce_chunk_kernel<16>": (2 * N * A + 4) * S, "adamw_kernel": 30 * S,
+    alg = {REDUCE_KERNEL: (2 * N * A + 4) * S, "adamw_kernel": 30 * S,
            "reduce_adamw_chunk_kernel": (2 * N * A + 26) * S,
            "reduce_rs_chunk_kernel": (2 * N * A + 4) * S,
            "copy_kernel": 2 * copy_bytes}
@@ -931,7 +935,7 @@ def main():
         "copy_ceiling_GBps": round(ceiling, 1),
         "stream_ceilings_GBps": {k: round(v, 1) for k, v in streams.items()},
         "tiny_mlp_step": tiny,
-        "roofline": {"bound": "hbm", "kernel": "reduce_chunk_kernel<16>", "achieved": round(red_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": REDUCE_KERNEL, "achieved": round(red_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(red_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": alg["reduce"]},
         "cpu_baseline": None,
