@@ -1154,8 +1154,10 @@ AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
 // workgroup per CU, AdamW 2-9% at three 4-wave workgroups (twelve waves) per
 // CU; on a 70B group's shard the 16-term reduce gained 6% at three,
 // the bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4
-// groups).  The copy kernels keep full occupancy: eight 8 KB tiles per CU
-// are already in that range, and fewer measured slower.  A cap of k is set
+// groups).  Of the copy kernels only the unpack is capped (six per CU, 1.6%
+// faster than the seven its registers allow); the pack and the cast pack,
+// which read a pointer table before their loads, measured slower capped.  A
+// cap of k is set
 // by reserving dynamic LDS that the kernel never touches: with L bytes of
 // LDS per CU, L / (k + 1) + 1 bytes per workgroup let k workgroups fit but
 // not k + 1.  Grids shorter than kCapMinRounds rounds of resident
@@ -1167,6 +1169,7 @@ constexpr int kRedFewWgsPerCu = 3;     // reduce_chunk_kernel<kRedGroupsFew>
 constexpr int kRsManyWgsPerCu = 2;     // reduce_rs_chunk_kernel<kRsGroupsMany>
 constexpr int kRsFewWgsPerCu = 3;      // reduce_rs_chunk_kernel<kRsGroupsFew>
 constexpr int kAdamWgsPerCu = 12;      // adamw_kernel (one wave per workgroup)
+constexpr int kUnpackWgsPerCu = 6;     // unpack_kernel (registers allow 7-8)
 constexpr int64_t kCapMinRounds = 16;
 
 struct CuLimits {
@@ -1197,15 +1200,15 @@ CuLimits cu_limits() {
     return L;
 }
 
-// Dynamic LDS bytes for a grid of `grid` workgroups capped at k per CU (0:
-// no cap).
-uint32_t lds_cap(int k, int64_t grid) {
+// Dynamic LDS bytes for a grid of `grid` workgroups capped at k per CU, for a
+// kernel that already uses `static_bytes` of LDS (0: no cap).
+uint32_t lds_cap(int k, int64_t grid, int64_t static_bytes = 0) {
     const CuLimits L = cu_limits();
     if (L.lds_per_cu <= 0 || k < 1) return 0;
     if (grid < kCapMinRounds * k * (int64_t)L.cus) return 0;
-    const int64_t bytes = L.lds_per_cu / (k + 1) + 1;
-    if (bytes > L.lds_per_wg || bytes * k > L.lds_per_cu) return 0;
-    return (uint32_t)bytes;
+    const int64_t per_wg = L.lds_per_cu / (k + 1) + 1;   // k of these fit in a CU, k + 1 do not
+    if (per_wg > L.lds_per_wg || per_wg * k > L.lds_per_cu || per_wg <= static_bytes) return 0;
+    return (uint32_t)(per_wg - static_bytes);
 }
 
 int check_hparams(const char *what, const fs_adamw_hparams_t *hp) {
@@ -1484,11 +1487,12 @@ extern "C" int fs_unpack(fs_plan_t plan, const void *gathered, void *const *para
     const BufInfo *bufs = reinterpret_cast<const BufInfo *>(ws + plan->ws.bufinfo);
     (void)hipGetLastError();
     const char *g = static_cast<const char *>(gathered);
+    const uint32_t lds = lds_cap(kUnpackWgsPerCu, ntiles, (int64_t)sizeof(TileLds));
     if (I.elem_bytes == 2)
-        hipLaunchKernelGGL(unpack_kernel<2>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
+        hipLaunchKernelGGL(unpack_kernel<2>, dim3((uint32_t)ntiles), dim3(kThreads), lds, stream, segs, tiles,
                            bufs, g, params);
     else
-        hipLaunchKernelGGL(unpack_kernel<4>, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles,
+        hipLaunchKernelGGL(unpack_kernel<4>, dim3((uint32_t)ntiles), dim3(kThreads), lds, stream, segs, tiles,
                            bufs, g, params);
     return check_launch("fs_unpack");
 }
