@@ -1154,10 +1154,10 @@ AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
 // workgroup per CU, AdamW 2-9% at three 4-wave workgroups (twelve waves) per
 // CU; on a 70B group's shard the 16-term reduce gained 6% at three,
 // the bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4
-// groups).  Of the copy kernels only the unpack is capped (six per CU, 1.6%
-// faster than the seven its registers allow); the pack and the cast pack,
-// which read a pointer table before their loads, measured slower capped.  A
-// cap of k is set
+// groups).  Of the copy kernels the unpack and the re-shard, whose loads do
+// not wait for a pointer-table read, run capped at six per CU (1.6% and 2.6%
+// faster); the pack and the cast pack, which read the parameter pointer
+// table before their loads, measured slower capped.  A cap of k is set
 // by reserving dynamic LDS that the kernel never touches: with L bytes of
 // LDS per CU, L / (k + 1) + 1 bytes per workgroup let k workgroups fit but
 // not k + 1.  Grids shorter than kCapMinRounds rounds of resident
@@ -1170,6 +1170,7 @@ constexpr int kRsManyWgsPerCu = 2;     // reduce_rs_chunk_kernel<kRsGroupsMany>
 constexpr int kRsFewWgsPerCu = 3;      // reduce_rs_chunk_kernel<kRsGroupsFew>
 constexpr int kAdamWgsPerCu = 12;      // adamw_kernel (one wave per workgroup)
 constexpr int kUnpackWgsPerCu = 6;     // unpack_kernel (registers allow 7-8)
+constexpr int kReshardWgsPerCu = 6;    // scatter_kernel<W, UnpackSrc> (registers allow 8)
 constexpr int64_t kCapMinRounds = 16;
 
 struct CuLimits {
@@ -1461,11 +1462,12 @@ extern "C" int fs_reshard(fs_reshard_t r, const void *src_gathered, void *dst_ga
     (void)hipGetLastError();
     const UnpackSrc src{static_cast<const char *>(src_gathered)};
     char *dst = static_cast<char *>(dst_gathered);
+    const uint32_t lds = lds_cap(kReshardWgsPerCu, ntiles, (int64_t)sizeof(TileLds));
     if (r->elem_bytes == 2)
-        hipLaunchKernelGGL((scatter_kernel<2, UnpackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+        hipLaunchKernelGGL((scatter_kernel<2, UnpackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), lds, stream, segs,
                            tiles, src, dst, (int64_t)0, r->dst_gathered);
     else
-        hipLaunchKernelGGL((scatter_kernel<4, UnpackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs,
+        hipLaunchKernelGGL((scatter_kernel<4, UnpackSrc>), dim3((uint32_t)ntiles), dim3(kThreads), lds, stream, segs,
                            tiles, src, dst, (int64_t)0, r->dst_gathered);
     return check_launch("fs_reshard");
 }

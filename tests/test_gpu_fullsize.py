@@ -116,9 +116,9 @@ def test_fullsize_reduce_and_adamw(plans):
 
 @pytest.mark.parametrize("which", ["block0", "block31", "root"])
 def test_fullsize_pack_unpack_groups(plans, which):
-    """Pack (all ranks) and unpack of a full-size group; sampled elements of
-    the gathered buffer and of the unpacked parameters against the oracle's
-    layout, and every pad element zero."""
+    """Pack (all ranks), unpack and re-shard (N -> N/2) of a full-size group;
+    sampled elements of the gathered buffers and of the unpacked parameters
+    against the oracle's layouts, and every pad element zero."""
     groups, ps = plans
     gi = {"block0": 0, "block31": 31, "root": 32}[which]
     shapes, plan = groups[gi], ps[gi]
@@ -135,9 +135,15 @@ def test_fullsize_pack_unpack_groups(plans, which):
     fs.fs_pack(plan, params, gathered)
     outs = [torch.empty_like(p) for p in params]
     fs.fs_unpack(plan, gathered, outs)
+    # re-shard the gathered buffer from N to N/2 logical ranks
+    half = fs.fs_plan(shapes, "bf16", N // 2, False, "fsdp2", A).upload()
+    rs = fs.fs_reshard_plan(plan, half).upload()
+    regathered = torch.empty(half.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    fs.fs_reshard(rs, gathered, regathered)
     torch.cuda.synchronize()
 
     L = oracle.fsdp2_layout(shapes, 2, N)
+    Lh = oracle.fsdp2_layout(shapes, 2, N // 2)
     rng = np.random.default_rng(gi)
     for i, (s, st) in enumerate(zip(shapes, starts)):
         n = math.prod(s)
@@ -146,6 +152,8 @@ def test_fullsize_pack_unpack_groups(plans, which):
         expect = synth.to_numpy_bits(synth.bits16_at(SEED, synth.STREAM_PARAMS, torch.from_numpy(e + st)))
         got = bits(gathered.view(torch.int16)[torch.from_numpy(x).cuda()])
         np.testing.assert_array_equal(got, expect)
+        xh = Lh.index_at(np.full(e.size, i, np.int32), e)
+        np.testing.assert_array_equal(bits(regathered.view(torch.int16)[torch.from_numpy(xh).cuda()]), expect)
         got_u = bits(outs[i].view(-1).view(torch.int16)[torch.from_numpy(e).cuda()])
         np.testing.assert_array_equal(got_u, expect)
         assert torch.equal(outs[i].view(torch.int16), params[i].view(torch.int16))
