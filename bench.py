@@ -348,6 +348,23 @@ def extra_measurements(W, reps, small: bool = True) -> dict:
                                   "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     del dst, rs, half
     torch.cuda.empty_cache()
+    # sharded state-dict import of rank 0 (fs_load_local): every group's local
+    # pieces, held as separate tensors, written into that rank's shard buffer
+    pieces, shards = [], []
+    for p, gath in zip(W["plans"], W["gathered"]):
+        views = p.local_views(gath[:p.shard_numel], 0)
+        pieces.append([v.clone() for v in views])
+        shards.append(torch.empty(p.shard_numel, dtype=torch.bfloat16, device="cuda"))
+
+    def load_all():
+        for p, pc, sh in zip(W["plans"], pieces, shards):
+            p.load_local(sh, 0, pc)
+    ms = _timed_graph(load_all, reps, calls=2)   # 33 launches of about 20 us each: replayed as a graph
+    b = 2 * sum(v.numel() for pc in pieces for v in pc) + 2 * sum(sh.numel() for sh in shards)
+    out["load_local_rank0"] = {"ms": round(ms, 4), "GB": round(b / 1e9, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del pieces, shards
+    torch.cuda.empty_cache()
     # the same groups under the FSDP1 FlatParameter layout (use_orig_params):
     # 16-byte-aligned parameter starts, flat chunked into N equal shards
     f1 = [fs.fs_plan(g, "bf16", N, True, "fsdp1", A).upload() for g in groups] if small else []
@@ -873,6 +890,7 @@ def main():
                      "adamw": (16 * S, 14 * S), "reduce_adamw_fused": ((2 * N * A + 12) * S, 14 * S),
                      "reduce_bf16_reduce_dtype": (2 * N * A * S, 4 * S),
                      "pack_cast_fp32_to_bf16": (4 * P, 2 * gath),
+                     "load_local_rank0": (2 * S, 2 * S),
                      "reshard_n_to_half_n": (2 * P, extra["reshard_n_to_half_n"]["GB"] * 1e9 - 2 * P)}
             cfg = {"params": W["P"], "shard_numel": W["S"], "world": W["world"], "grad_acc": W["grad_acc"],
                    "groups": W["groups"]}
