@@ -1,0 +1,104 @@
+"""Several sharded training steps end to end on the GPU, against the oracle
+running the same sequence on the CPU.
+
+One FSDP2 group with N logical ranks and grad_acc micro-steps, all ranks'
+state held in gathered-layout buffers (each rank's shard is its slice, as
+"FSDP1 vs FSDP2" section 03 lays them out): per step,
+
+  1. unpack the gathered bf16 parameters (the all-gather copy-out),
+  2. pack every (micro-step j, rank k) gradient into the gathered layout --
+     what the reduce-scatter delivers, one slice per term,
+  3. average the N * grad_acc terms into the fp32 gradient ("Data
+     parallelism, ZeRO and FSDP", sections 2.1, 5 and 9.2),
+  4. AdamW on the fp32 master, moments and the bf16 copy, which is written
+     straight into the gathered buffer the next step unpacks (section 9.1).
+
+The gradients are seeded synthetic values (the same counter-based streams on
+both sides), not functions of the parameters.  Every intermediate is
+compared bit for bit after each step; pads stay zero throughout.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import bits, say
+
+pytestmark = pytest.mark.gpu
+fs = pytest.importorskip("fsdp_sharded_state_amd")
+
+CASES = [
+    # (name, shapes, N, grad_acc, steps)
+    ("mixed_pads", [(6, 3), (9,), (1, 1), (13, 5), (0, 2), (33, 16)], 4, 2, 3),
+    ("llama_block_d256", synth.llama_block_shapes(256, 688), 8, 4, 3),
+]
+
+
+def _grad_stream(j, k, N, t):
+    return synth.stream_grad(j, k, N) + 1000 * t
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_training_steps_match_oracle(case):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    name, shapes, N, A, steps = case
+    say("train loop", name, N, A, steps)
+    plan = fs.fs_plan(shapes, "bf16", N, False, "fsdp2", A).upload()
+    L = oracle.fsdp2_layout(shapes, 2, N)
+    numel = [int(np.prod(s)) if len(s) else 1 for s in shapes]
+    n = plan.gathered_numel
+
+    # initial parameters -> gathered bf16 buffer (both sides)
+    p0 = [synth.to_numpy_bits(synth.normal_bf16(21, synth.STREAM_PARAMS, k, 0.02, start=sum(numel[:i])))
+          for i, k in enumerate(numel)]
+    g_host = oracle.pack(L, p0)
+    gathered = torch.from_numpy(g_host.view(np.int16)).cuda().view(torch.bfloat16)
+    # fp32 master = the bf16 values widened; moments start at zero
+    th_host = (g_host.astype(np.uint32) << 16).view(np.float32)
+    m_host = np.zeros(n, np.float32)
+    v_host = np.zeros(n, np.float32)
+    th = torch.from_numpy(th_host.copy()).cuda()
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    grad = torch.empty(n, dtype=torch.float32, device="cuda")
+    outs = [torch.empty(k, dtype=torch.bfloat16, device="cuda") for k in numel]
+    gpack = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(N * A)]
+
+    for t in range(1, steps + 1):
+        hp = oracle.AdamWHparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=t)
+        # 1. copy-out
+        fs.fs_unpack(plan, gathered, outs)
+        params_host = oracle.unpack(L, g_host)
+        # 2. per-(micro-step, rank) gradients, packed
+        terms_host = []
+        for j in range(A):
+            for k in range(N):
+                gh = [synth.to_numpy_bits(synth.normal_bf16(21, _grad_stream(j, k, N, t), c, 1e-3,
+                                                             start=sum(numel[:i])))
+                      for i, c in enumerate(numel)]
+                gd = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16).reshape(s)
+                      for x, s in zip(gh, shapes)]
+                fs.fs_pack(plan, gd, gpack[j * N + k])
+                terms_host.append(oracle.pack(L, gh))
+        # 3. average
+        fs.fs_reduce_shard(gpack, grad, N, A)
+        grad_host = oracle.reduce_shard(terms_host, N, A)
+        # 4. AdamW, bf16 copy into the gathered buffer
+        fs.fs_adamw_step(th, m, v, grad, gathered, lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
+                         weight_decay=hp.weight_decay, step=t)
+        th_host, m_host, v_host, g_host = oracle.adamw_step(th_host, m_host, v_host, grad_host, hp)
+        torch.cuda.synchronize()
+
+        for i, (o, ph) in enumerate(zip(outs, params_host)):
+            np.testing.assert_array_equal(bits(o), ph, err_msg=f"{name} step {t}: unpacked parameter {i}")
+        for k in range(N * A):
+            np.testing.assert_array_equal(bits(gpack[k]), terms_host[k], err_msg=f"{name} step {t}: term {k}")
+        np.testing.assert_array_equal(bits(grad), grad_host.view(np.uint32), err_msg=f"{name} step {t}: gradient")
+        for got, want, what in ((th, th_host, "master"), (m, m_host, "exp_avg"), (v, v_host, "exp_avg_sq")):
+            np.testing.assert_array_equal(bits(got), want.view(np.uint32), err_msg=f"{name} step {t}: {what}")
+        np.testing.assert_array_equal(bits(gathered), g_host, err_msg=f"{name} step {t}: bf16 parameters")
+        pads = np.ones(n, bool)
+        pads[L.index_map()] = False
+        assert not np.any(bits(gathered)[pads]), f"{name} step {t}: a pad of the gathered buffer is not zero"
