@@ -1,9 +1,10 @@
 """Several sharded training steps end to end on the GPU, against the oracle
 running the same sequence on the CPU.
 
-One FSDP2 group with N logical ranks and grad_acc micro-steps, all ranks'
-state held in gathered-layout buffers (each rank's shard is its slice, as
-"FSDP1 vs FSDP2" section 03 lays them out): per step,
+One FSDP group (FSDP2 per-parameter chunks, or the FSDP1 flat parameter with
+or without use_orig_params) with N logical ranks and grad_acc micro-steps,
+all ranks' state held in gathered-layout buffers (each rank's shard is its
+slice, as "FSDP1 vs FSDP2" section 03 lays them out): per step,
 
   1. unpack the gathered bf16 parameters (the all-gather copy-out),
   2. pack every (micro-step j, rank k) gradient into the gathered layout --
@@ -28,10 +29,13 @@ from gpu_util import bits, say
 pytestmark = pytest.mark.gpu
 fs = pytest.importorskip("fsdp_sharded_state_amd")
 
+MIXED = [(6, 3), (9,), (1, 1), (13, 5), (0, 2), (33, 16)]
 CASES = [
-    # (name, shapes, N, grad_acc, steps)
-    ("mixed_pads", [(6, 3), (9,), (1, 1), (13, 5), (0, 2), (33, 16)], 4, 2, 3),
-    ("llama_block_d256", synth.llama_block_shapes(256, 688), 8, 4, 3),
+    # (name, mode, use_orig_params, shapes, N, grad_acc, steps)
+    ("fsdp2_mixed_pads", "fsdp2", False, MIXED, 4, 2, 3),
+    ("fsdp2_llama_block_d256", "fsdp2", False, synth.llama_block_shapes(256, 688), 8, 4, 3),
+    ("fsdp1_orig_params_mixed", "fsdp1", True, MIXED, 4, 2, 3),
+    ("fsdp1_flat_mixed", "fsdp1", False, MIXED, 3, 3, 2),
 ]
 
 
@@ -43,10 +47,10 @@ def _grad_stream(j, k, N, t):
 def test_training_steps_match_oracle(case):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    name, shapes, N, A, steps = case
+    name, mode, uo, shapes, N, A, steps = case
     say("train loop", name, N, A, steps)
-    plan = fs.fs_plan(shapes, "bf16", N, False, "fsdp2", A).upload()
-    L = oracle.fsdp2_layout(shapes, 2, N)
+    plan = fs.fs_plan(shapes, "bf16", N, uo, mode, A).upload()
+    L = oracle.fsdp2_layout(shapes, 2, N) if mode == "fsdp2" else oracle.fsdp1_layout(shapes, 2, N, uo)
     numel = [int(np.prod(s)) if len(s) else 1 for s in shapes]
     n = plan.gathered_numel
 
