@@ -14,7 +14,10 @@ slice, as "FSDP1 vs FSDP2" section 03 lays them out): per step,
   4. AdamW on the fp32 master, moments and the bf16 copy, which is written
      straight into the gathered buffer the next step unpacks (section 9.1).
 
-The gradients are seeded synthetic values (the same counter-based streams on
+Steps 3 and 4 run as two kernels, as the fused reduce + AdamW (the fp32
+gradient never stored), or with the bf16 reduce dtype (each micro-step's
+average delivered in bf16, "FSDP1 vs FSDP2", mixed precision).  The
+gradients are seeded synthetic values (the same counter-based streams on
 both sides), not functions of the parameters.  Every intermediate is
 compared bit for bit after each step; pads stay zero throughout.
 """
@@ -43,12 +46,13 @@ def _grad_stream(j, k, N, t):
     return synth.stream_grad(j, k, N) + 1000 * t
 
 
+@pytest.mark.parametrize("variant", ["two_kernels", "fused", "bf16_reduce_dtype"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
-def test_training_steps_match_oracle(case):
+def test_training_steps_match_oracle(case, variant):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     name, mode, uo, shapes, N, A, steps = case
-    say("train loop", name, N, A, steps)
+    say("train loop", name, variant, N, A, steps)
     plan = fs.fs_plan(shapes, "bf16", N, uo, mode, A).upload()
     L = oracle.fsdp2_layout(shapes, 2, N) if mode == "fsdp2" else oracle.fsdp1_layout(shapes, 2, N, uo)
     numel = [int(np.prod(s)) if len(s) else 1 for s in shapes]
@@ -86,12 +90,19 @@ def test_training_steps_match_oracle(case):
                       for x, s in zip(gh, shapes)]
                 fs.fs_pack(plan, gd, gpack[j * N + k])
                 terms_host.append(oracle.pack(L, gh))
-        # 3. average
-        fs.fs_reduce_shard(gpack, grad, N, A)
-        grad_host = oracle.reduce_shard(terms_host, N, A)
-        # 4. AdamW, bf16 copy into the gathered buffer
-        fs.fs_adamw_step(th, m, v, grad, gathered, lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
-                         weight_decay=hp.weight_decay, step=t)
+        # 3. average and 4. AdamW, bf16 copy into the gathered buffer
+        adam = dict(lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps, weight_decay=hp.weight_decay, step=t)
+        if variant == "fused":
+            fs.fs_reduce_adamw_step(gpack, th, m, v, gathered, grad, world=N, grad_acc=A, **adam)
+            grad_host = oracle.reduce_shard(terms_host, N, A)
+        else:
+            if variant == "bf16_reduce_dtype":
+                fs.fs_reduce_shard_ex(gpack, grad, N, A, reduce_dtype="bf16")
+                grad_host = oracle.reduce_shard_bf16rs(terms_host, N, A)
+            else:
+                fs.fs_reduce_shard(gpack, grad, N, A)
+                grad_host = oracle.reduce_shard(terms_host, N, A)
+            fs.fs_adamw_step(th, m, v, grad, gathered, **adam)
         th_host, m_host, v_host, g_host = oracle.adamw_step(th_host, m_host, v_host, grad_host, hp)
         torch.cuda.synchronize()
 
