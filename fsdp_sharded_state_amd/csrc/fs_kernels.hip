@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "fs_plan_impl.h"
@@ -1253,22 +1254,27 @@ int check_launch(const char *what) {
     return FS_OK;
 }
 
+// Call f(std::integral_constant<bool, a>, std::integral_constant<bool, b>):
+// picks the kernel instantiation for two run-time flags.
+template <class F>
+void with_flags(bool a, bool b, F &&f) {
+    using T = std::true_type;
+    using U = std::false_type;
+    if (a) {
+        if (b) f(T{}, T{}); else f(T{}, U{});
+    } else {
+        if (b) f(U{}, T{}); else f(U{}, U{});
+    }
+}
+
 template <int G>
 void launch_fused(int64_t n, hipStream_t stream, const SliceArgs &sa, int cnt, int first, float world, float *th,
                   float *m, float *v, uint16_t *p16, const float *part, float *gout, const AdamConsts &c) {
     const dim3 g((uint32_t)((n + kWgRow * G - 1) / (kWgRow * G))), b(kThreads);
-    if (p16 && gout)
-        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, true>), g, b, 0, stream, sa, cnt, first, world, th, m,
-                           v, p16, part, gout, c, n);
-    else if (p16)
-        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, true, false>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, part, gout, c, n);
-    else if (gout)
-        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, true>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, part, gout, c, n);
-    else
-        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, false, false>), g, b, 0, stream, sa, cnt, first, world, th,
-                           m, v, p16, part, gout, c, n);
+    with_flags(p16 != nullptr, gout != nullptr, [&](auto has_p16, auto has_g) {
+        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, decltype(has_p16)::value, decltype(has_g)::value>), g, b, 0,
+                           stream, sa, cnt, first, world, th, m, v, p16, part, gout, c, n);
+    });
 }
 
 // One pass of the fp32 reduce over terms [t0, t0 + cnt): chunked when every
@@ -1656,21 +1662,10 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
     if (aligned) {
         const dim3 g((uint32_t)((n + kAdamRow - 1) / kAdamRow)), b(kAdamThreads);
         const uint32_t lds = lds_cap(kAdamWgsPerCu, g.x);
-        if (grad_dtype == FS_BF16) {
-            if (param_bf16)
-                hipLaunchKernelGGL((adamw_kernel<true, true>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
-                                   param_bf16, c, n);
-            else
-                hipLaunchKernelGGL((adamw_kernel<true, false>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
-                                   param_bf16, c, n);
-        } else {
-            if (param_bf16)
-                hipLaunchKernelGGL((adamw_kernel<false, true>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
-                                   param_bf16, c, n);
-            else
-                hipLaunchKernelGGL((adamw_kernel<false, false>), g, b, lds, stream, master, exp_avg, exp_avg_sq, grad,
-                                   param_bf16, c, n);
-        }
+        with_flags(grad_dtype == FS_BF16, param_bf16 != nullptr, [&](auto grad_bf16, auto has_p16) {
+            hipLaunchKernelGGL((adamw_kernel<decltype(grad_bf16)::value, decltype(has_p16)::value>), g, b, lds, stream,
+                               master, exp_avg, exp_avg_sq, grad, param_bf16, c, n);
+        });
     } else {
         hipLaunchKernelGGL(adamw_scalar_kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                            stream, n, master, exp_avg, exp_avg_sq, grad, (int)(grad_dtype == FS_BF16), param_bf16,
