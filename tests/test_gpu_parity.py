@@ -218,7 +218,7 @@ REDUCE_CASES = [
     (1000, 8, 4, 0, 0), (65536 + 3, 8, 4, 0, 0), (4099, 3, 5, 0, 0),
     (5003, 8, 5, 0, 0),          # 40 terms: two passes
     (3001, 2, 33, 0, 0),         # 66 terms: three passes
-    (40000, 8, 5, 0, 0),         # 40 terms over whole 16384-element chunks + remainder
+    (40000, 8, 5, 0, 0),         # 40 terms: a 32-term pass over one whole chunk + remainder, then 8 terms
     (20000 + 7, 2, 33, 0, 0),    # 66 terms, chunks + ragged remainder
     (16384 * 3, 8, 4, 0, 0),     # one and a half chunks
     (RED_CHUNK * 3, 8, 4, 0, 0), # whole chunks only
@@ -229,7 +229,7 @@ REDUCE_CASES = [
     (70001, 8, 4, 1, 0),         # misaligned, large
     (30011, 5, 7, 0, 0),         # 35 terms: a 32-term pass (long chunks), then 3 terms (short chunks)
     (16384 * 2 + 4096 * 3 + 5, 8, 4, 0, 0),   # last chunk cut into four sub-chunks, the fourth holding 5 elements
-    (16384 + 4095, 4, 8, 0, 0),  # last chunk: four sub-chunks, a straddling group of 3 elements
+    (16384 + 4095, 4, 8, 0, 0),  # a single partial chunk: five sub-chunks, a straddling group of 3 elements
     (4096 * 5 + 1027, 8, 1, 0, 0),   # few terms: last chunk of 1027 elements
     (1025, 8, 1, 0, 0), (4095, 16, 1, 0, 0), (4097, 17, 1, 0, 0),   # 16 / 17 terms: the chunk switch
     (25_297_920, 8, 1, 0, 0),    # one Llama-7B block shard, 8-buffer average

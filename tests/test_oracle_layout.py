@@ -33,7 +33,7 @@ def test_worked_example_table3():
     assert f1f.shard == per["fsdp1_use_orig_params_false"]
     assert f1t.shard == per["fsdp1_use_orig_params_true"]
     assert f2.shard == per["fsdp2"]
-    # "pad 5 before P2, then world pad 3"
+    # the table's alignment pad ahead of the second parameter, then its world pad
     assert f1t.start[1] - 3 == g["fsdp1_use_orig_params_true_align_pad_before_second_param"]
     assert f1t.world * f1t.shard - f1t.flat_len == g["fsdp1_use_orig_params_true_world_pad"]
     assert list(f2.chunk_rows * f2.row) == g["fsdp2_per_param_chunk_elements"]

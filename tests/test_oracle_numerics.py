@@ -52,7 +52,7 @@ def test_ledger_zero_stages(name):
 
 
 def test_ledger_fp32_accumulation_term():
-    """P2 section 9: fp32 gradient accumulation adds 4 bytes per parameter on
+    """"Data parallelism, ZeRO and FSDP" section 9: fp32 gradient accumulation adds 4 bytes per parameter on
     the kept gradient part: 4P/N under ZeRO-2/3, 4P under DP and ZeRO-1."""
     P, N = 7e9, 8
     a = oracle.ledger(P, N, 2, 12, fp32_grad_acc=False)
