@@ -1315,6 +1315,16 @@ bool ranges_overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes
     return abytes > 0 && bbytes > 0 && x < y + (uintptr_t)bbytes && y < x + (uintptr_t)abytes;
 }
 
+// Index of the first of `cnt` buffers that overlaps an earlier one, or -1.
+// AdamW reads element k of every array and writes element k of its outputs,
+// so two arrays sharing memory would mix one element's state into another's.
+int first_overlap(const void *const *ptr, const int64_t *bytes, int cnt) {
+    for (int i = 1; i < cnt; ++i)
+        for (int j = 0; j < i; ++j)
+            if (ranges_overlap(ptr[i], bytes[i], ptr[j], bytes[j])) return i;
+    return -1;
+}
+
 }  // namespace
 
 extern "C" int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hipStream_t stream) {
@@ -1654,6 +1664,13 @@ extern "C" int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *ex
     if (misaligned(master, 4) || misaligned(exp_avg, 4) || misaligned(exp_avg_sq, 4) || misaligned(grad, gb) ||
         (param_bf16 && misaligned(param_bf16, 2)))
         return fsi::fail(FS_E_ALIGN, "fs_adamw_step: pointer not aligned to its element size");
+    {
+        const void *arr[5] = {master, exp_avg, exp_avg_sq, grad, param_bf16};
+        const int64_t len[5] = {nb, nb, nb, n * gb, param_bf16 ? 2 * n : 0};
+        static const char *const name[5] = {"master", "exp_avg", "exp_avg_sq", "grad", "param_bf16"};
+        const int i = first_overlap(arr, len, 5);
+        if (i >= 0) return fsi::fail(FS_E_INVAL, "fs_adamw_step: %s overlaps another array", name[i]);
+    }
     const AdamConsts c = adam_consts(*hp);
     const bool aligned = !misaligned(master, 16) && !misaligned(exp_avg, 16) && !misaligned(exp_avg_sq, 16) &&
                          !misaligned(grad, 16) && !(param_bf16 && misaligned(param_bf16, 16));
@@ -1747,6 +1764,11 @@ int reduce_adamw_impl(const char *what, int64_t n, int32_t world, int32_t grad_a
     const void *outs[5] = {master, exp_avg, exp_avg_sq, grad_out, param_bf16};
     const int64_t out_bytes[5] = {bytes_out, bytes_out, bytes_out, grad_out ? bytes_out : 0,
                                   param_bf16 ? bytes_in : 0};
+    {
+        static const char *const name[5] = {"master", "exp_avg", "exp_avg_sq", "grad_out", "param_bf16"};
+        const int i = first_overlap(outs, out_bytes, 5);
+        if (i >= 0) return fsi::fail(FS_E_INVAL, "%s: %s overlaps another output", what, name[i]);
+    }
     for (int t = 0; t < terms; ++t) {
         if (!slices[t]) return fsi::fail(FS_E_INVAL, "%s: slice %d is NULL", what, t);
         if (misaligned(slices[t], 2))

@@ -371,8 +371,9 @@ int fs_pack_cast(fs_plan_t plan, const void *const *params, fs_dtype param_dtype
  *   m' = b1*m + (1-b1)*g;  v' = b2*v + (1-b2)*g*g;
  *   theta' = theta*(1 - lr*wd) - lr*(m'/(1-b1^t)) / (sqrt(v'/(1-b2^t)) + eps);
  *   param_bf16 = round-to-nearest-even bf16 of the stored fp32 theta'.
- * Errors: FS_E_INVAL (n < 0, NULL pointers, step < 1, betas outside [0,1)),
- * FS_E_DTYPE, FS_E_ALIGN, FS_E_HIP.
+ * Errors: FS_E_INVAL (n < 0, NULL pointers, step < 1, betas outside [0,1),
+ * two of master, exp_avg, exp_avg_sq, grad and param_bf16 sharing memory),
+ * FS_E_DTYPE, FS_E_ALIGN, FS_E_OVERFLOW (n beyond one launch), FS_E_HIP.
  */
 int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *exp_avg_sq,
                   const void *grad, fs_dtype grad_dtype, uint16_t *param_bf16,
@@ -395,7 +396,8 @@ int fs_adamw_step(int64_t n, float *master, float *exp_avg, float *exp_avg_sq,
  * fs_reduce_shard's output.  HBM traffic per element: 2*A*N + 26 bytes
  * (+4 with grad_out) instead of 2*A*N + 34.
  * Errors: those of fs_reduce_shard and fs_adamw_step; FS_E_INVAL also for an
- * output overlapping a slice, or more than 32 terms without grad_out.
+ * output overlapping a slice or another output, or more than 32 terms
+ * without grad_out.
  */
 int fs_reduce_adamw_step(int64_t n, int32_t world, int32_t grad_acc,
                          const uint16_t *const *slices, float *master,

@@ -222,6 +222,43 @@ def test_call_validation_before_gpu():
     assert L.fs_stream_fill(ctypes.c_void_p(256), 0, 0, None) == fs.FS_OK           # nothing to do
 
 
+def test_adamw_rejects_arrays_that_share_memory():
+    """AdamW updates element k of every array from element k of the others:
+    any two of theta, m, v, the gradient and the bf16 copy that share memory
+    are refused on the host, for the fused step as well.  n = 2**40 is more
+    than one launch covers, so a call that passes every check still fails
+    (FS_E_OVERFLOW) before launching anything: no call here reaches a GPU."""
+    L = fs.lib()
+    hp = fs.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0, 1)
+    n = 1 << 40
+    A, B, C, G, P, S = (k << 44 for k in range(1, 7))          # disjoint, 16 TiB apart
+    vp = ctypes.c_void_p
+
+    def adamw(th, m, v, g, p, gdt=fs.FS_FP32):
+        return L.fs_adamw_step(n, vp(th), vp(m), vp(v), vp(g), gdt, vp(p), ctypes.byref(hp), None)
+
+    assert adamw(A, B, C, G, P) == fs.FS_E_OVERFLOW                           # disjoint: only the size fails
+    for args, name in [((A, A, C, G, P), b"exp_avg"), ((A, B, B + 4 * n - 16, G, P), b"exp_avg_sq"),
+                       ((A, B, C, A + 16, P), b"grad"), ((A, B, C, G, C + 4 * n - 2), b"param_bf16")]:
+        assert adamw(*args) == fs.FS_E_INVAL, name
+        assert name in L.fs_last_error() and b"overlaps" in L.fs_last_error()
+    assert adamw(A, A + 4 * n, C, G, P) == fs.FS_E_OVERFLOW                   # adjacent, not overlapping
+    assert adamw(A, B, C, G, G + 2 * n, fs.FS_BF16) == fs.FS_E_OVERFLOW       # a bf16 gradient is 2n bytes
+    assert adamw(A, B, C, G, G + 2 * n, fs.FS_FP32) == fs.FS_E_INVAL          # an fp32 one is 4n
+
+    sl = (ctypes.c_void_p * 2)(S, S + (1 << 43))
+    for fused in (L.fs_reduce_adamw_step, L.fs_reduce_adamw_step_noalloc):
+        def call(th, m, v, p, go=None):
+            extra = (vp(go),) if fused is L.fs_reduce_adamw_step else ()
+            return fused(n, 2, 1, sl, vp(th), vp(m), vp(v), vp(p), *extra, ctypes.byref(hp), None)
+        assert call(A, B, C, P) == fs.FS_E_OVERFLOW
+        for args, name in [((A, B, A, P), b"exp_avg_sq"), ((A, B, C, A + 2), b"param_bf16")]:
+            assert call(*args) == fs.FS_E_INVAL, name
+            assert name in L.fs_last_error() and b"overlaps" in L.fs_last_error()
+    assert L.fs_reduce_adamw_step(n, 2, 1, sl, vp(A), vp(B), vp(C), vp(P), vp(B + 8), ctypes.byref(hp),
+                                  None) == fs.FS_E_INVAL
+    assert b"grad_out" in L.fs_last_error()
+
 def test_fused_call_validation_before_gpu():
     L = fs.lib()
     hp = fs.AdamWHparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 0, 1)
