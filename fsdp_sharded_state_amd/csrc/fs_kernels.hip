@@ -1,12 +1,14 @@
 // fs_kernels.hip -- gfx950 (CDNA4) kernels and the C-ABI launchers.
 //
-// All four kernels are HBM-bandwidth-bound streams with no reuse: pack and
-// unpack move bytes, the reduce does one fp32 add per input element, AdamW a
-// few dozen flops per 30 bytes.  None is a contraction, so none uses MFMA;
-// the design goals are 16-byte (dwordx4) accesses on every lane, enough loads
-// in flight to cover HBM latency but not so many concurrent streams per CU
-// that the DRAM loses efficiency (the reduce and AdamW launches cap their
-// resident workgroups), and no divergent control flow at layout boundaries.
+// Every kernel here is an HBM-bandwidth-bound stream with no reuse: the
+// copies (pack, unpack, cast pack, re-shard, state-dict import) move bytes,
+// the reduces do one fp32 add per input element, AdamW a few dozen flops per
+// 30 bytes.  None is a contraction, so none uses MFMA; the design goals are
+// 16-byte (dwordx4) accesses on every lane, enough loads in flight to cover
+// HBM latency but not so many concurrent streams per CU that the DRAM loses
+// efficiency (long launches of the reduces, AdamW, the unpack and the
+// re-shard cap their resident workgroups), and no divergent control flow at
+// layout boundaries.
 //
 // Sources (page title, section):
 //   pack / unpack: "FSDP1 vs FSDP2", section 03 (FlatParameter padding and
@@ -16,6 +18,12 @@
 //     the loss).
 //   AdamW: "Data parallelism, ZeRO and FSDP", sections 1 (moments, then the
 //     parameter) and 9.1 (update the fp32 shard, then cast it to bf16).
+//   fused reduce + AdamW: the same, section 9.2 (the own averaged fp32
+//     gradient feeds the own shard's update).
+//   bf16 reduce dtype and the fp32 -> bf16 cast pack: "FSDP1 vs FSDP2",
+//     mixed-precision section (reduce_dtype, param_dtype).
+//   re-shard and the state-dict import: "FSDP1 vs FSDP2", memory and
+//     engineering section (the shards are the sharded state dict).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <string.h>
@@ -250,9 +258,10 @@ __device__ __forceinline__ void copy_run(char *dst, const char *src, int nblk) {
 
 // Destination-driven copy into one contiguous buffer (`out`, addressed from
 // virtual element dst_lo): the gathered buffer for pack (Src = PackSrc, one
-// source per parameter) and for reshard (Src = UnpackSrc, one source: the
-// other plan's gathered buffer).  Elements no segment covers are written as
-// zero.
+// source per parameter), for reshard (Src = UnpackSrc, one source: the
+// other plan's gathered buffer) and one rank's shard for the state-dict
+// import (Src = LocalSrc, one local piece per parameter).  Elements no
+// segment covers are written as zero.
 template <int W, class Src>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(const Segment *__restrict__ segs,
                                                            const Tile *__restrict__ tiles, Src S,
@@ -1147,14 +1156,16 @@ AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
 }
 
 // Workgroups resident per CU.  The reduce and AdamW kernels stream HBM best
-// with about 48-64 KB of loads in flight per CU; their register use alone
-// would let more workgroups share a CU (the 32-term reduce three, AdamW
-// eight waves per SIMD), and the extra concurrent streams cost DRAM
-// efficiency.  Measured side by side on one MI355X, same buffers, three
-// placements: the 32-term reduce on the 7B shard ran 4-8% faster at one
-// workgroup per CU, AdamW 2-9% at three 4-wave workgroups (twelve waves) per
-// CU; on a 70B group's shard the 16-term reduce gained 6% at three,
-// the bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4
+// with about 48-64 KB of loads in flight per CU; where their register use
+// alone would let more workgroups share a CU, the extra concurrent streams
+// cost DRAM efficiency.  Measured side by side on one MI355X, same buffers,
+// three placements: the 32-term reduce on the 7B shard ran 4-8% faster at
+// one workgroup per CU than at three (with 16 groups per lane; the 32-group
+// shape kept now fills one workgroup's worth of a CU's registers, so its cap
+// of one restates that), AdamW's single-wave workgroups 4-11% faster at
+// twelve per CU (registers allow 32) than 256-thread workgroups uncapped; on
+// a 70B group's shard the 16-term reduce gained 6% at three, the
+// bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4
 // groups).  Of the copy kernels the unpack and the re-shard, whose loads do
 // not wait for a pointer-table read, run capped at six per CU (1.6% and 2.6%
 // faster); the pack and the cast pack, which read the parameter pointer
