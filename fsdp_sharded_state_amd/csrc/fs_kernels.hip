@@ -1398,6 +1398,7 @@ extern "C" int fs_pack(fs_plan_t plan, const void *const *params, void *out, int
         ntiles = plan->rank_tile_off[rank + 1] - plan->rank_tile_off[rank];
     }
     if (ntiles == 0) return FS_OK;
+    if (ntiles > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_pack: too many tiles for one launch");
     (void)hipGetLastError();
     // `out` is addressed from the virtual element `lo` on
     char *base = static_cast<char *>(out);
@@ -1429,6 +1430,7 @@ extern "C" int fs_load_local(fs_plan_t plan, int32_t rank, const void *const *pi
     const Tile *tiles = reinterpret_cast<const Tile *>(ws + plan->ws.pack_tiles_rank) + plan->rank_tile_off[rank];
     const int64_t ntiles = plan->rank_tile_off[rank + 1] - plan->rank_tile_off[rank];
     if (ntiles == 0) return FS_OK;
+    if (ntiles > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_load_local: too many tiles for one launch");
     const int64_t *first = reinterpret_cast<const int64_t *>(ws + plan->ws.local_first) + (int64_t)rank * I.n_params;
     const int64_t lo = (int64_t)rank * I.shard_numel, hi = lo + I.shard_numel;
     (void)hipGetLastError();
@@ -1507,6 +1509,7 @@ extern "C" int fs_unpack(fs_plan_t plan, const void *gathered, void *const *para
     if (int rc = check_device("fs_unpack", plan->dev_id)) return rc;
     const int64_t ntiles = plan->ws.n_unpack_tiles;
     if (ntiles == 0 || I.total_numel == 0) return FS_OK;
+    if (ntiles > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_unpack: too many tiles for one launch");
     if (!gathered || !params) return fsi::fail(FS_E_INVAL, "fs_unpack: NULL pointer");
     if (misaligned(gathered, I.elem_bytes))
         return fsi::fail(FS_E_ALIGN, "fs_unpack: gathered not aligned to %d bytes", I.elem_bytes);
@@ -1654,6 +1657,7 @@ extern "C" int fs_pack_cast(fs_plan_t plan, const void *const *params, fs_dtype 
         ntiles = plan->rank_tile_off[rank + 1] - plan->rank_tile_off[rank];
     }
     if (ntiles == 0) return FS_OK;
+    if (ntiles > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_pack_cast: too many tiles for one launch");
     (void)hipGetLastError();
     hipLaunchKernelGGL(pack_cast_kernel, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles, params,
                        static_cast<char *>(out), lo, hi);
