@@ -480,9 +480,10 @@ __global__ __launch_bounds__(kThreads) void pack_cast_kernel(const Segment *__re
 // at one workgroup per CU: against G = 16 with two slices in flight (the
 // same 64 KB in flight, 32 KB runs) it measured 3% faster on two of three
 // placements and 1% slower on the third; G = 24 was slower on all three.
-// Fewer terms give each workgroup little work, and G = 4 with two slices in
-// flight (more, shorter workgroups) measured 6-10% faster there (8 terms)
-// and no slower at 16.
+// Fewer terms give each workgroup little work, and G = 4 (more, shorter
+// workgroups) measured 6-10% faster there (8 terms) and no slower at 16;
+// at G = 4 one slice in flight beat two by 1-3% at 8 terms and 1% at 16
+// (three or four: slower).
 //
 // General kernel (misaligned slices or output): lane i owns 8 consecutive
 // elements, one 16-byte (funnel-shifted when misaligned) load per term, plus
@@ -702,7 +703,7 @@ __device__ __forceinline__ void reduce_chunk(const SliceArgs &sa, int nterms, in
     const Bounds<G, TAIL> B(base, n);
     float acc[4 * G];
     if (!first_pass) load_f32_groups<G, G, TAIL>(acc, out, base, B);   // partial sums of the earlier passes
-    sum_slices<G, (G >= 32 ? 1 : 2), TAIL>(sa, nterms, first_pass, acc, base, B);   // slices in flight
+    sum_slices<G, 1, TAIL>(sa, nterms, first_pass, acc, base, B);   // one slice in flight
     if (last_pass) {
 #pragma unroll
         for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
@@ -781,15 +782,23 @@ __device__ __forceinline__ void reduce_rs_chunk(const SliceArgs &sa, int nsteps,
             }
         }
     };
-    int t = 0;
-    if (t < total) load_groups<G, TAIL>(xa, sa.p[t], base, B);
-    while (t < total) {
-        if (t + 1 < total) load_groups<G, TAIL>(xb, sa.p[t + 1], base, B);
-        consume(xa, t);
-        if (++t >= total) break;
-        if (t + 1 < total) load_groups<G, TAIL>(xa, sa.p[t + 1], base, B);
-        consume(xb, t);
-        ++t;
+    if constexpr (G <= 4) {   // short chunks: one slice in flight (1% faster at 8 terms than two)
+        (void)xb;
+        for (int t = 0; t < total; ++t) {
+            load_groups<G, TAIL>(xa, sa.p[t], base, B);
+            consume(xa, t);
+        }
+    } else {            // two slices in flight (one: 3-5% slower at 32 terms)
+        int t = 0;
+        if (t < total) load_groups<G, TAIL>(xa, sa.p[t], base, B);
+        while (t < total) {
+            if (t + 1 < total) load_groups<G, TAIL>(xb, sa.p[t + 1], base, B);
+            consume(xa, t);
+            if (++t >= total) break;
+            if (t + 1 < total) load_groups<G, TAIL>(xa, sa.p[t + 1], base, B);
+            consume(xb, t);
+            ++t;
+        }
     }
 #pragma unroll
     for (int u = 0; u < G; ++u) store_f32_group<G, TAIL>(out, base, u, acc + 4 * u, B);
@@ -966,11 +975,16 @@ __global__ __launch_bounds__(kThreads) void adamw_scalar_kernel(int64_t n, float
 // slice loop and storing group by group.  The kernel is bound by HBM's mixed
 // read/write rate, not by its double-precision arithmetic: a cheaper update
 // formula and variants at two to four waves per SIMD measured no faster.
+// Slices in flight (SL): two at 16 groups; at 4 groups (passes of at most
+// kRedFewTerms terms) four when the pass has at most kFusedDeepTerms terms
+// (3% faster than two at 8 terms, 2% slower at 16) and one above that (1%
+// faster than two at 16 terms, up to 1% slower at 8).
 constexpr int kFusedGroupsMany = 16;
 constexpr int kFusedGroupsFew = 4;
 constexpr int kFusedBatch = 8;
+constexpr int kFusedDeepTerms = 8;
 
-template <int G, bool HAS_P16, bool HAS_G, bool TAIL>
+template <int G, int SL, bool HAS_P16, bool HAS_G, bool TAIL>
 __device__ __forceinline__ void reduce_adamw_chunk(const SliceArgs &sa, int nterms, int first_pass, float world,
                                                    float *__restrict__ th, float *__restrict__ m,
                                                    float *__restrict__ v, uint16_t *__restrict__ p16,
@@ -981,7 +995,7 @@ __device__ __forceinline__ void reduce_adamw_chunk(const SliceArgs &sa, int nter
     const Bounds<G, TAIL> B(base, n);
     float acc[4 * G];
     if (!first_pass) load_f32_groups<G, G, TAIL>(acc, part, base, B);   // partial sums left by the reduce passes
-    sum_slices<G, 2, TAIL>(sa, nterms, first_pass, acc, base, B);
+    sum_slices<G, SL, TAIL>(sa, nterms, first_pass, acc, base, B);
 #pragma unroll
     for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
     float T[2][4 * KB], M[2][4 * KB], V[2][4 * KB];
@@ -1014,7 +1028,7 @@ __device__ __forceinline__ void reduce_adamw_chunk(const SliceArgs &sa, int nter
     }
 }
 
-template <int G, bool HAS_P16, bool HAS_G>
+template <int G, int SL, bool HAS_P16, bool HAS_G>
 __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs sa, int nterms, int first_pass,
                                                                       float world, float *__restrict__ th,
                                                                       float *__restrict__ m,
@@ -1024,10 +1038,10 @@ __global__ __launch_bounds__(kThreads) void reduce_adamw_chunk_kernel(SliceArgs 
                                                                       int64_t n) {
     static_assert(G % kTailGroups == 0, "the tail walks whole sub-chunks");
     FS_CHUNK_DISPATCH(G,
-                      (reduce_adamw_chunk<G, HAS_P16, HAS_G, false>(sa, nterms, first_pass, world, th, m, v, p16,
-                                                                    part, gout, c, base, n)),
-                      (reduce_adamw_chunk<kTailGroups, HAS_P16, HAS_G, true>(sa, nterms, first_pass, world, th, m,
-                                                                             v, p16, part, gout, c, base, n)));
+                      (reduce_adamw_chunk<G, SL, HAS_P16, HAS_G, false>(sa, nterms, first_pass, world, th, m, v,
+                                                                        p16, part, gout, c, base, n)),
+                      (reduce_adamw_chunk<kTailGroups, SL, HAS_P16, HAS_G, true>(sa, nterms, first_pass, world, th,
+                                                                                 m, v, p16, part, gout, c, base, n)));
 }
 
 // Misaligned variant: lane i owns 8 consecutive elements (the general
@@ -1278,13 +1292,13 @@ void with_flags(bool a, bool b, F &&f) {
     }
 }
 
-template <int G>
+template <int G, int SL>
 void launch_fused(int64_t n, hipStream_t stream, const SliceArgs &sa, int cnt, int first, float world, float *th,
                   float *m, float *v, uint16_t *p16, const float *part, float *gout, const AdamConsts &c) {
     const dim3 g((uint32_t)((n + kWgRow * G - 1) / (kWgRow * G))), b(kThreads);
     with_flags(p16 != nullptr, gout != nullptr, [&](auto has_p16, auto has_g) {
-        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, decltype(has_p16)::value, decltype(has_g)::value>), g, b, 0,
-                           stream, sa, cnt, first, world, th, m, v, p16, part, gout, c, n);
+        hipLaunchKernelGGL((reduce_adamw_chunk_kernel<G, SL, decltype(has_p16)::value, decltype(has_g)::value>), g, b,
+                           0, stream, sa, cnt, first, world, th, m, v, p16, part, gout, c, n);
     });
 }
 
@@ -1809,12 +1823,15 @@ int reduce_adamw_impl(const char *what, int64_t n, int32_t world, int32_t grad_a
     for (int k = 0; k < last_cnt; ++k) sa.p[k] = slices[t_last + k];
     const int first = t_last == 0;
     if (aligned) {
-        if (last_cnt <= kRedFewTerms)
-            launch_fused<kFusedGroupsFew>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg, exp_avg_sq,
-                                          param_bf16, partial, grad_out, c);
+        if (last_cnt <= kFusedDeepTerms)
+            launch_fused<kFusedGroupsFew, 4>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg,
+                                             exp_avg_sq, param_bf16, partial, grad_out, c);
+        else if (last_cnt <= kRedFewTerms)
+            launch_fused<kFusedGroupsFew, 1>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg,
+                                             exp_avg_sq, param_bf16, partial, grad_out, c);
         else
-            launch_fused<kFusedGroupsMany>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg, exp_avg_sq,
-                                           param_bf16, partial, grad_out, c);
+            launch_fused<kFusedGroupsMany, 2>(n, stream, sa, last_cnt, first, (float)world, master, exp_avg,
+                                              exp_avg_sq, param_bf16, partial, grad_out, c);
     } else {
         const int64_t grid = std::max<int64_t>(1, ((n >> 3) + kThreads - 1) / kThreads);
         hipLaunchKernelGGL(reduce_adamw_general_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream, sa, last_cnt,
