@@ -377,6 +377,11 @@ FUSED_CASES = [
     (16384 * 2 + 4096 * 3 + 5, 8, 4, 0, True, True, 2),   # last chunk in four sub-chunks, 5 elements in the fourth
     (4096 * 6 + 1029, 8, 1, 0, True, False, 1),           # few terms: a last chunk of 1029 elements
     (16384 + 4095, 4, 8, 0, False, True, 4),              # straddling group of 3 elements, no bf16 copy
+    # the 4-group kernel's two shapes: four slices in flight up to 8 terms, one from 9 to 16
+    (70001, 8, 2, 0, True, True, 3),                      # 16 terms, ragged last chunk
+    (4096 * 7 + 13, 3, 4, 0, True, False, 2),             # 12 terms
+    (50000, 6, 8, 0, True, True, 6),                      # 48 terms: a 32-term reduce pass, then 16 fused
+    (9001, 3, 3, 1, True, True, 2),                       # 9 terms, misaligned: the general kernel
     (25_297_920, 8, 1, 0, True, False, 1000),
 ]
 
