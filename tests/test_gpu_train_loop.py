@@ -117,3 +117,109 @@ def test_training_steps_match_oracle(case, variant):
         pads = np.ones(n, bool)
         pads[L.index_map()] = False
         assert not np.any(bits(gathered)[pads]), f"{name} step {t}: a pad of the gathered buffer is not zero"
+
+
+RESUME_CASES = [
+    # (name, mode, shapes, N, N2): FSDP2 and the FSDP1 flat parameter without alignment, whose
+    # element positions are the same for bf16 parameters and fp32 state
+    ("fsdp2_mixed_4_to_2", "fsdp2", MIXED, 4, 2),
+    ("fsdp2_llama_block_d256_8_to_2", "fsdp2", synth.llama_block_shapes(256, 688), 8, 2),
+    ("fsdp1_flat_mixed_4_to_2", "fsdp1", MIXED, 4, 2),
+]
+
+
+def _scaled_bits(x, scale):
+    """bf16 bits times a power of two, exactly."""
+    f = (x.astype(np.uint32) << 16).view(np.float32) * np.float32(scale)
+    b = f.view(np.uint32)
+    assert not np.any(b & 0xFFFF), "scaling left the bf16 grid"
+    return (b >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("case", RESUME_CASES, ids=lambda c: c[0])
+def test_resume_at_another_rank_count(case):
+    """Resuming from a sharded state on a different number of ranks (the FSDP
+    tutorial page, section 3.3, loads a checkpoint at another card count).
+    Two steps run at N ranks with one micro-step each; then theta, m, v and
+    the bf16 parameters are re-sharded to N2 ranks (fs_reshard) and the third
+    step runs there with grad_acc = N / N2, micro-step j of rank k carrying
+    the original rank j*N2 + k's gradient scaled by N2 / N (the 1/grad_acc
+    that the micro-step loss holds, "Data parallelism, ZeRO and FSDP" section
+    5).  Power-of-two scaling is exact in bf16 and fp32 and the terms are
+    summed in the original rank order, so the averaged gradient and the whole
+    state equal, bit for bit, the oracle's three steps at N ranks re-laid for
+    N2 ranks by the oracle's re-shard."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    name, mode, shapes, N, N2 = case
+    A2 = N // N2
+    say("resume at another rank count", name, N, N2)
+
+    def plan(n, dt):
+        return fs.fs_plan(shapes, dt, n, False, mode).upload()
+
+    def layout(n, eb):
+        return oracle.fsdp2_layout(shapes, eb, n) if mode == "fsdp2" else oracle.fsdp1_layout(shapes, eb, n, False)
+
+    P, Pf, Q, Qf = plan(N, "bf16"), plan(N, "fp32"), plan(N2, "bf16"), plan(N2, "fp32")
+    L, Lf, M, Mf = layout(N, 2), layout(N, 4), layout(N2, 2), layout(N2, 4)
+    np.testing.assert_array_equal(L.index_map(), Lf.index_map())
+    np.testing.assert_array_equal(M.index_map(), Mf.index_map())
+    numel = [int(np.prod(s)) if len(s) else 1 for s in shapes]
+    n, n2 = P.gathered_numel, Q.gathered_numel
+
+    def grads(t, k):
+        return [synth.to_numpy_bits(synth.normal_bf16(21, _grad_stream(0, k, N, t), c, 1e-3, start=sum(numel[:i])))
+                for i, c in enumerate(numel)]
+
+    def dev(host_bits, shape):
+        return torch.from_numpy(host_bits.view(np.int16)).cuda().view(torch.bfloat16).reshape(shape)
+
+    p0 = [synth.to_numpy_bits(synth.normal_bf16(21, synth.STREAM_PARAMS, k, 0.02, start=sum(numel[:i])))
+          for i, k in enumerate(numel)]
+    g_host = oracle.pack(L, p0)
+    gathered = torch.from_numpy(g_host.view(np.int16)).cuda().view(torch.bfloat16)
+    th_host = (g_host.astype(np.uint32) << 16).view(np.float32)
+    m_host = np.zeros(n, np.float32)
+    v_host = np.zeros(n, np.float32)
+    th = torch.from_numpy(th_host.copy()).cuda()
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    grad = torch.empty(n, device="cuda")
+    gpack = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(N)]
+    adam = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+    # the oracle runs three steps at N ranks; the GPU runs the first two there
+    for t in (1, 2, 3):
+        hp = oracle.AdamWHparams(step=t, **adam)
+        grad_host = oracle.reduce_shard([oracle.pack(L, grads(t, k)) for k in range(N)], N, 1)
+        th_host, m_host, v_host, g_host = oracle.adamw_step(th_host, m_host, v_host, grad_host, hp)
+        if t < 3:
+            for k in range(N):
+                fs.fs_pack(P, [dev(x, s) for x, s in zip(grads(t, k), shapes)], gpack[k])
+            fs.fs_reduce_shard(gpack, grad, N, 1)
+            fs.fs_adamw_step(th, m, v, grad, gathered, step=t, **adam)
+
+    # re-shard the state to N2 ranks
+    rf, rb = fs.fs_reshard_plan(Pf, Qf).upload(), fs.fs_reshard_plan(P, Q).upload()
+    th2, m2, v2, grad2 = (torch.empty(n2, device="cuda") for _ in range(4))
+    gathered2 = torch.empty(n2, dtype=torch.bfloat16, device="cuda")
+    for src, dst in ((th, th2), (m, m2), (v, v2)):
+        fs.fs_reshard(rf, src, dst)
+    fs.fs_reshard(rb, gathered, gathered2)
+
+    # third step at N2 ranks, grad_acc A2
+    gpack2 = [torch.empty(n2, dtype=torch.bfloat16, device="cuda") for _ in range(N)]
+    for j in range(A2):
+        for k in range(N2):
+            gd = [dev(_scaled_bits(x, 1.0 / A2), s) for x, s in zip(grads(3, j * N2 + k), shapes)]
+            fs.fs_pack(Q, gd, gpack2[j * N2 + k])
+    fs.fs_reduce_shard(gpack2, grad2, N2, A2)
+    fs.fs_adamw_step(th2, m2, v2, grad2, gathered2, step=3, **adam)
+    torch.cuda.synchronize()
+
+    relaid = lambda x: oracle.reshard(Lf, Mf, x.view(np.uint32))
+    np.testing.assert_array_equal(bits(grad2), relaid(grad_host), err_msg=f"{name}: gradient at {N2} ranks")
+    for got, want, what in ((th2, th_host, "master"), (m2, m_host, "exp_avg"), (v2, v_host, "exp_avg_sq")):
+        np.testing.assert_array_equal(bits(got), relaid(want), err_msg=f"{name}: {what} at {N2} ranks")
+    np.testing.assert_array_equal(bits(gathered2), oracle.reshard(L, M, g_host), err_msg=f"{name}: bf16 parameters")

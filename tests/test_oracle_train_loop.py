@@ -85,3 +85,42 @@ def test_sharded_chain_equals_unsharded_adamw(case):
         pads = np.ones(th.size, bool)
         pads[imap] = False
         assert not np.any(th[pads]) and not np.any(m[pads]) and not np.any(v[pads]) and not np.any(g_bits[pads])
+
+
+@pytest.mark.parametrize("mode,N,N2", [("fsdp2", 4, 2), ("fsdp2", 8, 2), ("fsdp1", 4, 2)])
+def test_resume_at_another_rank_count(mode, N, N2):
+    """Re-sharding the state to N2 ranks and continuing there with
+    grad_acc = N / N2 (micro-step gradients scaled by N2 / N, the 1/grad_acc of
+    "Data parallelism, ZeRO and FSDP" section 5) gives exactly the state of
+    continuing at N ranks, re-laid: power-of-two scaling is exact and the
+    terms keep their order.  Pins reshard against the chain: a re-shard that
+    moves an element to another's place, or a reduce that reorders terms or
+    divides by the wrong count, breaks the equality."""
+    A2 = N // N2
+    lay = lambda n, eb: oracle.fsdp2_layout(MIXED, eb, n) if mode == "fsdp2" else oracle.fsdp1_layout(MIXED, eb, n, False)
+    L, Lf, M, Mf = lay(N, 2), lay(N, 4), lay(N2, 2), lay(N2, 4)
+    numel = [int(np.prod(s)) if len(s) else 1 for s in MIXED]
+    split = lambda x: np.split(x, np.cumsum(numel)[:-1])
+    grads = lambda t, k: split(synth.to_numpy_bits(synth.normal_bf16(37, synth.stream_grad(0, k, N) + 100 * t,
+                                                                      sum(numel), 1e-3)))
+    half = lambda x: ((((x.astype(np.uint32) << 16).view(np.float32) * np.float32(1.0 / A2)).view(np.uint32)) >> 16
+                      ).astype(np.uint16)
+    p0 = synth.to_numpy_bits(synth.normal_bf16(37, synth.STREAM_PARAMS, sum(numel), 0.02))
+    g = oracle.pack(L, split(p0))
+    th = (g.astype(np.uint32) << 16).view(np.float32).copy()
+    m, v = np.zeros_like(th), np.zeros_like(th)
+    hp = lambda t: oracle.AdamWHparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=t)
+    for t in (1, 2):
+        th, m, v, g = oracle.adamw_step(th, m, v, oracle.reduce_shard([oracle.pack(L, grads(t, k)) for k in range(N)],
+                                                                      N, 1), hp(t))
+    gA = oracle.reduce_shard([oracle.pack(L, grads(3, k)) for k in range(N)], N, 1)
+    A = oracle.adamw_step(th, m, v, gA, hp(3))
+    relaid = lambda x: oracle.reshard(Lf, Mf, x.view(np.uint32))
+    th2, m2, v2 = (relaid(x).view(np.float32) for x in (th, m, v))
+    terms = [oracle.pack(M, [half(x) for x in grads(3, j * N2 + k)]) for j in range(A2) for k in range(N2)]
+    gB = oracle.reduce_shard(terms, N2, A2)
+    B = oracle.adamw_step(th2, m2, v2, gB, hp(3))
+    np.testing.assert_array_equal(gB.view(np.uint32), relaid(gA))
+    for a, b in zip(A[:3], B[:3]):
+        np.testing.assert_array_equal(b.view(np.uint32), relaid(a))
+    np.testing.assert_array_equal(B[3], oracle.reshard(L, M, A[3]))
