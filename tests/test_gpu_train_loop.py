@@ -136,8 +136,9 @@ def _scaled_bits(x, scale):
     return (b >> 16).astype(np.uint16)
 
 
+@pytest.mark.parametrize("variant", ["two_kernels", "fused"])
 @pytest.mark.parametrize("case", RESUME_CASES, ids=lambda c: c[0])
-def test_resume_at_another_rank_count(case):
+def test_resume_at_another_rank_count(case, variant):
     """Resuming from a sharded state on a different number of ranks (the FSDP
     tutorial page, section 3.3, loads a checkpoint at another card count).
     Two steps run at N ranks with one micro-step each; then theta, m, v and
@@ -148,12 +149,13 @@ def test_resume_at_another_rank_count(case):
     5).  Power-of-two scaling is exact in bf16 and fp32 and the terms are
     summed in the original rank order, so the averaged gradient and the whole
     state equal, bit for bit, the oracle's three steps at N ranks re-laid for
-    N2 ranks by the oracle's re-shard."""
+    N2 ranks by the oracle's re-shard.  The resumed step runs as the reduce
+    and AdamW kernels, or as the fused reduce + AdamW."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     name, mode, shapes, N, N2 = case
     A2 = N // N2
-    say("resume at another rank count", name, N, N2)
+    say("resume at another rank count", name, variant, N, N2)
 
     def plan(n, dt):
         return fs.fs_plan(shapes, dt, n, False, mode).upload()
@@ -214,8 +216,11 @@ def test_resume_at_another_rank_count(case):
         for k in range(N2):
             gd = [dev(_scaled_bits(x, 1.0 / A2), s) for x, s in zip(grads(3, j * N2 + k), shapes)]
             fs.fs_pack(Q, gd, gpack2[j * N2 + k])
-    fs.fs_reduce_shard(gpack2, grad2, N2, A2)
-    fs.fs_adamw_step(th2, m2, v2, grad2, gathered2, step=3, **adam)
+    if variant == "fused":
+        fs.fs_reduce_adamw_step(gpack2, th2, m2, v2, gathered2, grad2, world=N2, grad_acc=A2, step=3, **adam)
+    else:
+        fs.fs_reduce_shard(gpack2, grad2, N2, A2)
+        fs.fs_adamw_step(th2, m2, v2, grad2, gathered2, step=3, **adam)
     torch.cuda.synchronize()
 
     relaid = lambda x: oracle.reshard(Lf, Mf, x.view(np.uint32))
