@@ -17,7 +17,7 @@
  * Conventions for every call:
  *   - Device buffers are owned by the caller.  The library allocates no
  *     device memory and never synchronizes the device, except fs_plan_upload
- *     (a set-up call that waits for its own copy).
+ *     and fs_reshard_upload (set-up calls that wait for their own copies).
  *   - Pointers named "device" point to GPU memory; pointers named "host" to
  *     CPU memory.  Every device pointer must be aligned to its element size
  *     (2 bytes for bf16, 4 for fp32); 16-byte alignment is not required but
@@ -25,7 +25,7 @@
  *   - Work is issued asynchronously on `stream` (NULL = the null stream) as
  *     kernel launches only -- no copies, allocations or waits -- so the calls
  *     can be captured into a HIP graph.  A call launches one kernel; the
- *     reduces launch one per pass of up to 32 terms.
+ *     reduces and the fused step launch one per pass of up to 32 terms.
  *   - fs_plan_info, fs_plan_param, fs_plan_segments, fs_plan_upload,
  *     fs_plan_destroy, the fs_reshard_info/upload/destroy calls and
  *     fs_last_error are infrastructure around the method's steps (reading a
@@ -58,7 +58,7 @@ typedef enum {
     FS_E_INVAL = -1,       /* bad argument: N < 1, NULL pointer, rank out of range, ... */
     FS_E_UNSUPPORTED = -2, /* a layout the method does not define (e.g. use_orig_params in FSDP2) */
     FS_E_DTYPE = -3,       /* unknown dtype */
-    FS_E_OVERFLOW = -4,    /* a size does not fit in int64 */
+    FS_E_OVERFLOW = -4,    /* a size does not fit in int64, or exceeds one launch's grid or the scratch array */
     FS_E_ALIGN = -5,       /* a pointer not aligned to its element size */
     FS_E_HIP = -6,         /* the HIP runtime reported an error */
     FS_E_NOMEM = -7        /* host memory for the plan could not be allocated */
@@ -216,7 +216,8 @@ void fs_plan_destroy(fs_plan_t plan);
  *                   Every pad element is written as zero.
  *   rank            -1, or 0 <= rank < N.
  * Errors: FS_E_INVAL (plan not uploaded, rank out of range, NULL pointers),
- * FS_E_ALIGN (out not aligned to the element size), FS_E_HIP.
+ * FS_E_ALIGN (out not aligned to the element size), FS_E_OVERFLOW (more
+ * tiles than one launch's grid holds), FS_E_HIP.
  */
 int fs_pack(fs_plan_t plan, const void *const *params, void *out, int32_t rank,
             hipStream_t stream);
@@ -260,7 +261,8 @@ int fs_reshard_upload(fs_reshard_t r, void *workspace, size_t bytes, hipStream_t
  * fs_reshard -- dst_gathered (device, dst's gathered_numel elements) <- the
  * re-sharded src_gathered (device, src's gathered_numel elements).  Pads of
  * src are not read.  Errors: FS_E_INVAL (not uploaded, NULL, overlapping
- * buffers), FS_E_ALIGN, FS_E_HIP.
+ * buffers), FS_E_ALIGN, FS_E_OVERFLOW (more tiles than one launch's grid
+ * holds), FS_E_HIP.
  */
 int fs_reshard(fs_reshard_t r, const void *src_gathered, void *dst_gathered, hipStream_t stream);
 
@@ -287,7 +289,7 @@ void fs_reshard_destroy(fs_reshard_t r);
  *                   that no piece covers (a pad) is written as zero.
  * Same kernels and tables as fs_pack with rank = r.
  * Errors: FS_E_INVAL (plan not uploaded, rank out of range, NULL pointers),
- * FS_E_ALIGN (shard not aligned to the element size), FS_E_HIP.
+ * FS_E_ALIGN (shard not aligned to the element size), FS_E_OVERFLOW, FS_E_HIP.
  */
 int fs_load_local(fs_plan_t plan, int32_t rank, const void *const *pieces, void *shard,
                   hipStream_t stream);
