@@ -643,7 +643,9 @@ def measure_70b(reps: int = 3, seed: int = 5) -> dict:
         return e
     out = {"workload": "70B Llama-style model (80 blocks, d 8192, f 28672, k/v 8192x1024, vocab 32000), "
                        "rank 0's FSDP2 1/8 shard, grad_acc 2",
-           "shard_numel": S, "groups": len(sizes), "launches_per_reduce": len(sizes),
+           "shard_numel": S, "groups": len(sizes),
+           "launches_per_reduce": sum(launches_per_call("reduce", c, N * A, N) for c in sizes),
+           "launches_per_adamw": launches_per_call("adamw", S),
            "reduce": ent(ms_r, br, round(br / (0.8 * HBM_PEAK_GBPS) / 1e6, 1)),
            "adamw": ent(ms_a, ba, round(ba / (0.8 * HBM_PEAK_GBPS) / 1e6, 1)),
            "reduce_adamw": ent(ms_r + ms_a, br + ba),
@@ -722,6 +724,25 @@ def traffic_for(kernel: str, launch_bytes_alg: float):
 # is the number of 4-element groups per lane)
 REDUCE_KERNEL = "reduce_chunk_kernel<32>"
 
+# The library runs a call over n elements as consecutive launches over
+# sub-ranges of at most this many elements (per pass of up to 32 terms); the
+# values mirror kSpan, kRsSpan and kAdamSpan in fs_kernels.hip (a CPU test
+# checks that they agree).
+LAUNCH_SPAN = {"reduce": 32 << 20, "reduce_bf16_reduce_dtype": 16 << 20, "reduce_adamw_fused": 32 << 20,
+               "adamw": 64 << 20}
+
+
+def launches_per_call(phase: str, n: int, terms: int = 32, world: int = 8) -> int:
+    """Kernel launches of one call of `phase` over n elements."""
+    spans = -(-n // LAUNCH_SPAN[phase])
+    if phase == "reduce":
+        passes = -(-terms // 32)
+    elif phase == "reduce_bf16_reduce_dtype":
+        passes = -(-(terms // world) // (32 // world))
+    else:
+        passes = 1            # AdamW; the fused step's passes before the last are reduce launches
+    return spans * passes
+
 KERNELS = {  # rocprofv3 kernel-name fragment -> bench phase
     REDUCE_KERNEL: "reduce",
     "scatter_kernel<2, (anonymous namespace)::UnpackSrc": "reshard",
@@ -774,14 +795,20 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
     copy_bytes = float(1 << 32)
     f_fetch = copy_bytes / (avg["copy_kernel"]["FETCH_SIZE"] * 1024)
     f_write = copy_bytes / (avg["copy_kernel"]["WRITE_SIZE"] * 1024)
-    # algorithmic bytes per launch of the 7B shard step
+    # algorithmic bytes per call of the 7B shard step, and the launches of one call
     S, N, A = 842301440, 8, 4
     alg = {REDUCE_KERNEL: (2 * N * A + 4) * S, "adamw_kernel": 30 * S,
            "reduce_adamw_chunk_kernel": (2 * N * A + 26) * S,
            "reduce_rs_chunk_kernel": (2 * N * A + 4) * S,
            "copy_kernel": 2 * copy_bytes}
+    nl = {REDUCE_KERNEL: launches_per_call("reduce", S, N * A, N),
+          "adamw_kernel": launches_per_call("adamw", S),
+          "reduce_adamw_chunk_kernel": launches_per_call("reduce_adamw_fused", S),
+          "reduce_rs_chunk_kernel": launches_per_call("reduce_bf16_reduce_dtype", S, N * A, N),
+          "copy_kernel": 1}
     for k in KERNELS:
         alg.setdefault(k, None)   # pack / unpack / reshard: per group, reported as means below
+        nl.setdefault(k, 1)
     rec = {"kernel_source_sha256_16": kernel_source_hash(), "fetch_scale": f_fetch, "write_scale": f_write,
            "kernels": {}}
     rows = []
@@ -791,15 +818,15 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
         fe = avg[k].get("FETCH_SIZE", 0.0) * 1024 * f_fetch
         wr = avg[k].get("WRITE_SIZE", 0.0) * 1024 * f_write
         hbm = fe + wr
-        a = alg.get(k)
-        ent = {"avg_ns": stats[k]["avg_ns"], "calls": stats[k]["calls"], "fetch_bytes_per_launch": fe,
-               "write_bytes_per_launch": wr, "hbm_bytes_per_launch": hbm}
+        a = alg.get(k) / nl[k] if alg.get(k) else None      # mean algorithmic bytes per launch
+        ent = {"avg_ns": stats[k]["avg_ns"], "calls": stats[k]["calls"], "launches_per_call": nl[k],
+               "fetch_bytes_per_launch": fe, "write_bytes_per_launch": wr, "hbm_bytes_per_launch": hbm}
         if a:
             ent["alg_bytes_per_launch"] = a
             ent["hbm_over_alg"] = hbm / a
             ent["alg_GBps_from_trace"] = a / stats[k]["avg_ns"]
         rec["kernels"][KERNELS[k]] = ent
-        rows.append((k, stats[k], fe, wr, a))
+        rows.append((k, stats[k], fe, wr, a, nl[k]))
     os.makedirs(out_dir, exist_ok=True)
     json.dump(rec, open(os.path.join(out_dir, os.path.basename(TRAFFIC_FILE)), "w"), indent=1)
     md = ["# Kernel profile: 7B rank-0 FSDP2 shard step (N=8, grad_acc=4)", "",
@@ -811,10 +838,13 @@ def summarize_rocprof(kt_dir: str, fetch_dir: str, write_dir: str, commands: lis
            "Kernel rates move by up to about 10% between allocations running the same code, with the",
            "physical placement of the buffers; compare the trace with the bench line of the same run",
            "(at the end, one allocation order), not with another run's.", "",
-           "| kernel | calls | avg duration | HBM read / launch | HBM write / launch | algorithmic / launch | HBM / alg | alg GB/s (trace) |",
-           "|---|---|---|---|---|---|---|---|"]
-    for k, st, fe, wr, a in rows:
-        md.append(f"| {k} | {st['calls']} | {st['avg_ns'] / 1e3:.1f} us | {fe / 1e9:.3f} GB | {wr / 1e9:.3f} GB | "
+           "Long calls run as several launches over sub-ranges of the shard (launches per call below);",
+           "per-launch figures are means over those launches: the call's algorithmic bytes divided by",
+           "its launches, against the mean launch duration and the mean counter values.", "",
+           "| kernel | launches | per call | avg duration | HBM read / launch | HBM write / launch | algorithmic / launch | HBM / alg | alg GB/s (trace) |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for k, st, fe, wr, a, L in rows:
+        md.append(f"| {k} | {st['calls']} | {L} | {st['avg_ns'] / 1e3:.1f} us | {fe / 1e9:.3f} GB | {wr / 1e9:.3f} GB | "
                   + (f"{a / 1e9:.3f} GB | {(fe + wr) / a:.3f} | {a / st['avg_ns']:.0f} |" if a else "per group (see below) | - | - |"))
     pk = "scatter_kernel<2, (anonymous namespace)::PackSrc"
     if pk in stats:
@@ -920,7 +950,8 @@ def main():
         kern["config5_70b"] = big
     alg = head["alg"]
     red_gbps = alg["reduce"] / (head["ms"]["reduce"] * 1e-3) / 1e9
-    traffic = traffic_for("reduce", alg["reduce"])
+    red_launches = launches_per_call("reduce", cfg["shard_numel"], cfg["world"] * cfg["grad_acc"], cfg["world"])
+    traffic = traffic_for("reduce", alg["reduce"] / red_launches)
     ra = [r["kernels"]["reduce_adamw"]["frac_hbm_peak"] for r in runs]
     out = {
         "metric": "sharded AdamW+reduce step GB/s and % HBM peak; pack/unpack GB/s (7B, N=8)",
@@ -955,7 +986,10 @@ def main():
         "tiny_mlp_step": tiny,
         "roofline": {"bound": "hbm", "kernel": REDUCE_KERNEL, "achieved": round(red_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(red_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "alg_bytes_per_launch": alg["reduce"]},
+                     "traffic": traffic, "alg_bytes_per_launch": round(alg["reduce"] / red_launches),
+                     "launches_per_call": red_launches,
+                     "note": ("per-launch bytes are means over the call's launches; achieved = the call's "
+                              "algorithmic bytes over its time on HIP events")},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -409,3 +409,24 @@ def test_planner_matches_oracle_randomized(shapes, N, eb, uo, mode):
     """Random parameter lists (scalars, empty and 1- to 3-D shapes) and N up
     to 64: the library's plan places every element where the oracle does."""
     _compare(mode, shapes, eb, N, uo and mode == "fsdp1")
+
+
+def test_bench_launch_spans_match_the_library():
+    """bench.py's launch-count arithmetic mirrors the library's span constants."""
+    import re
+    import bench
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "fsdp_sharded_state_amd", "csrc", "fs_kernels.hip")).read()
+    def span(name):
+        m = re.search(r"constexpr int64_t %s = (\d+)ll << (\d+);" % name, src)
+        assert m, name
+        return int(m.group(1)) << int(m.group(2))
+    assert bench.LAUNCH_SPAN["reduce"] == span("kSpan")
+    assert bench.LAUNCH_SPAN["reduce_adamw_fused"] == span("kSpan")
+    assert bench.LAUNCH_SPAN["reduce_bf16_reduce_dtype"] == span("kRsSpan")
+    assert bench.LAUNCH_SPAN["adamw"] == span("kAdamSpan")
+    S = 842_301_440
+    assert bench.launches_per_call("reduce", S, 32, 8) == 26
+    assert bench.launches_per_call("reduce", S, 40, 8) == 52
+    assert bench.launches_per_call("reduce_bf16_reduce_dtype", S, 32, 8) == 51
+    assert bench.launches_per_call("adamw", S) == 13

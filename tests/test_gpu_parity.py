@@ -705,3 +705,88 @@ def test_deterministic_across_runs_and_streams():
     for r in (1, 2):
         for a, b in zip(runs[0], runs[r]):
             np.testing.assert_array_equal(a, b)
+
+
+# ----------------------------------------------------- launch span boundaries --
+#
+# Calls longer than one launch's span run as consecutive launches over
+# sub-ranges (32M elements for the reduce and the fused step, 16M for the bf16
+# reduce dtype, 64M for AdamW).  Elements on both sides of every multiple of
+# 16M, the first and the ragged last ones are compared with the oracle; the
+# method is element-wise, so windows of the inputs give exact expected values.
+
+SPAN_N = 2 * (32 << 20) + 4099
+ADAM_SPAN_N = (64 << 20) + 4101
+
+
+def _windows(n, step=16 << 20, half=2048):
+    w = [(0, 2 * half)] + [(b - half, min(n, b + half)) for b in range(step, n, step)]
+    return w + [(n - 2 * half, n)]
+
+
+def _offset(t, shift):
+    """A copy of t whose data starts `shift` elements past a 16-byte boundary."""
+    raw = torch.empty(t.numel() + shift, dtype=t.dtype, device=t.device)
+    v = raw[shift:]
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("kind,shift", [("reduce", 0), ("reduce", 1), ("bf16_reduce_dtype", 0), ("fused", 0),
+                                        ("fused", 3)])
+def test_span_boundaries_reduce_family(kind, shift):
+    n, N, A = SPAN_N, 8, 5                  # 40 terms: a 32-term pass, then 8
+    say("span boundaries", kind, n, shift)
+    sl = [_offset(synth.normal_bf16(7, 100 + t, n, 1e-3, device="cuda"), shift) for t in range(N * A)]
+    W = _windows(n)
+    hsl = [[bits(s[a:b]) for s in sl] for a, b in W]
+    if kind == "fused":
+        (T, M, V), _, P = _adam_inputs(n, seed=9, step=7, grad_bf16=False)
+        st0 = [[bits(x.t[a:b]).view(np.float32) for x in (T, M, V)] for a, b in W]
+        G = Guarded(n, torch.float32)
+        fs.fs_reduce_adamw_step(sl, T.t, M.t, V.t, P.t, G.t, world=N, grad_acc=A, step=7)
+        torch.cuda.synchronize()
+        for g in (T, M, V, P, G):
+            g.check()
+        for (a, b), terms, (th0, m0, v0) in zip(W, hsl, st0):
+            ref_g = oracle.reduce_shard(terms, N, A)
+            np.testing.assert_array_equal(bits(G.t[a:b]), ref_g.view(np.uint32), err_msg=f"gradient [{a}, {b})")
+            rt, rm, rv, rp = oracle.adamw_step(th0, m0, v0, ref_g, oracle.AdamWHparams(step=7))
+            gt, gm, gv = (bits(x.t[a:b]).view(np.float32) for x in (T, M, V))
+            assert np.all(np.abs(gt - rt) <= 1e-6 * np.maximum(np.abs(rt), np.abs(th0))), (a, b)
+            assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm)), (a, b)
+            assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv)), (a, b)
+            assert np.all(np.abs(bits(P.t[a:b]).astype(np.int32) - rp.astype(np.int32)) <= 1), (a, b)
+        return
+    out = Guarded(n, torch.float32)
+    if kind == "reduce":
+        fs.fs_reduce_shard(sl, out.t, N, A)
+    else:
+        fs.fs_reduce_shard_ex(sl, out.t, N, A, reduce_dtype="bf16")
+    torch.cuda.synchronize()
+    out.check()
+    for (a, b), terms in zip(W, hsl):
+        ref = oracle.reduce_shard(terms, N, A) if kind == "reduce" else oracle.reduce_shard_bf16rs(terms, N, A)
+        np.testing.assert_array_equal(bits(out.t[a:b]), ref.view(np.uint32), err_msg=f"{kind} [{a}, {b})")
+
+
+@pytest.mark.parametrize("shift,gbf", [(0, False), (0, True), (2, False)])
+def test_span_boundaries_adamw(shift, gbf):
+    n = ADAM_SPAN_N
+    say("span boundaries adamw", n, shift, gbf)
+    (T, M, V), Gg, P = _adam_inputs(n, seed=5, step=11, grad_bf16=gbf, shift=shift)
+    W = _windows(n)
+    st0 = [[bits(x.t[a:b]).view(np.float32) for x in (T, M, V)] for a, b in W]
+    g0 = [bits(Gg.t[a:b]) for a, b in W]
+    fs.fs_adamw_step(T.t, M.t, V.t, Gg.t, P.t, step=11)
+    torch.cuda.synchronize()
+    for g in (T, M, V, P):
+        g.check()
+    for (a, b), (th0, m0, v0), gh in zip(W, st0, g0):
+        grad = gh if gbf else gh.view(np.float32)
+        rt, rm, rv, rp = oracle.adamw_step(th0, m0, v0, grad, oracle.AdamWHparams(step=11))
+        gt, gm, gv = (bits(x.t[a:b]).view(np.float32) for x in (T, M, V))
+        assert np.all(np.abs(gt - rt) <= 1e-6 * np.maximum(np.abs(rt), np.abs(th0))), (a, b)
+        assert np.all(np.abs(gm - rm) <= 1e-6 * np.abs(rm)), (a, b)
+        assert np.all(np.abs(gv - rv) <= 1e-6 * np.abs(rv)), (a, b)
+        assert np.all(np.abs(bits(P.t[a:b]).astype(np.int32) - rp.astype(np.int32)) <= 1), (a, b)
