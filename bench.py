@@ -722,7 +722,7 @@ def traffic_for(kernel: str, launch_bytes_alg: float):
 
 # the reduce's kernel for passes of more than 16 terms (its template argument
 # is the number of 4-element groups per lane)
-REDUCE_KERNEL = "reduce_chunk_kernel<32>"
+REDUCE_KERNEL = "reduce_chunk_kernel<16>"
 
 # The library runs a call over n elements as consecutive launches over
 # sub-ranges of at most this many elements (per pass of up to 32 terms); the

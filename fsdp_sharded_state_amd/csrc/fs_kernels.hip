@@ -476,10 +476,13 @@ __global__ __launch_bounds__(kThreads) void pack_cast_kernel(const Segment *__re
 // instruction covering 1 KB contiguous.  Reading each slice in long
 // contiguous runs keeps the HBM row buffers busy on one stream at a time,
 // which measured faster than interleaving all slices per element.  Passes of
-// more than 16 terms use G = 32 (64 KB per slice) with one slice in flight,
-// at one workgroup per CU: against G = 16 with two slices in flight (the
-// same 64 KB in flight, 32 KB runs) it measured 3% faster on two of three
-// placements and 1% slower on the third; G = 24 was slower on all three.
+// more than 16 terms use G = 16 (32 KB per slice) with two slices in flight,
+// at one workgroup per CU: run in the launch spans below, it measured 0.7-1.5%
+// faster than G = 32 with one slice in flight (the same 64 KB in flight) on
+// all of three placements, and faster than G = 16 at two per CU (-3 to -4%
+// for those), with three slices in flight (-0.3%) or G = 8 with four at two
+// per CU (-2 to -10%).  (In single whole-shard launches G = 32 had measured
+// 3% ahead on two of three placements.)
 // Fewer terms give each workgroup little work, and G = 4 (more, shorter
 // workgroups) measured 6-10% faster there (8 terms) and no slower at 16;
 // at G = 4 one slice in flight beat two by 1-3% at 8 terms and 1% at 16
@@ -581,11 +584,11 @@ __global__ __launch_bounds__(kThreads) void reduce_general_kernel(SliceArgs sa, 
     }
 }
 
-constexpr int kRedGroupsMany = 32;                                      // passes of > kRedFewTerms terms
+constexpr int kRedGroupsMany = 16;                                      // passes of > kRedFewTerms terms
 constexpr int kRedGroupsFew = 4;                                        // passes of <= kRedFewTerms terms
 constexpr int kRedFewTerms = 16;
 constexpr int64_t kWgRow = (int64_t)kThreads * 4;                       // elements of one group index across a workgroup
-constexpr int64_t kRedChunk = kWgRow * kRedGroupsMany;                  // 32768 elements
+constexpr int64_t kRedChunk = kWgRow * kRedGroupsMany;                  // 16384 elements
 constexpr int64_t kRedChunkFew = kWgRow * kRedGroupsFew;                // 4096 elements
 
 __device__ __forceinline__ void f4(u32x4 v, float o[4]) {
@@ -703,7 +706,7 @@ __device__ __forceinline__ void reduce_chunk(const SliceArgs &sa, int nterms, in
     const Bounds<G, TAIL> B(base, n);
     float acc[4 * G];
     if (!first_pass) load_f32_groups<G, G, TAIL>(acc, out, base, B);   // partial sums of the earlier passes
-    sum_slices<G, 1, TAIL>(sa, nterms, first_pass, acc, base, B);   // one slice in flight
+    sum_slices<G, (G >= 16 ? 2 : 1), TAIL>(sa, nterms, first_pass, acc, base, B);   // slices in flight
     if (last_pass) {
 #pragma unroll
         for (int e = 0; e < 4 * G; ++e) acc[e] = acc[e] / world;
@@ -1174,9 +1177,8 @@ AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
 // alone would let more workgroups share a CU, the extra concurrent streams
 // cost DRAM efficiency.  Measured side by side on one MI355X, same buffers,
 // three placements: the 32-term reduce on the 7B shard ran 4-8% faster at
-// one workgroup per CU than at three (with 16 groups per lane; the 32-group
-// shape kept now fills one workgroup's worth of a CU's registers, so its cap
-// of one restates that), AdamW's single-wave workgroups 4-11% faster at
+// one workgroup per CU than at three (16 groups per lane; in launch spans
+// one per CU still beats two by 3-4%), AdamW's single-wave workgroups 4-11% faster at
 // twelve per CU (registers allow 32) than 256-thread workgroups uncapped; on
 // a 70B group's shard the 16-term reduce gained 6% at three, the
 // bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4

@@ -210,7 +210,7 @@ def _slices(n, terms, seed, shift=0, sigma=1e-3, specials=False):
     return out
 
 
-RED_CHUNK = 32768     # elements per workgroup of the reduce's passes of more than 16 terms
+RED_CHUNK = 16384     # elements per workgroup of the reduce's passes of more than 16 terms
 RED_SUB = 4096        # the partial last chunk is walked in sub-chunks of this many elements
 REDUCE_CASES = [
     # (n, world, grad_acc, slice shift, out shift)
@@ -218,18 +218,18 @@ REDUCE_CASES = [
     (1000, 8, 4, 0, 0), (65536 + 3, 8, 4, 0, 0), (4099, 3, 5, 0, 0),
     (5003, 8, 5, 0, 0),          # 40 terms: two passes
     (3001, 2, 33, 0, 0),         # 66 terms: three passes
-    (40000, 8, 5, 0, 0),         # 40 terms: a 32-term pass over one whole chunk + remainder, then 8 terms
+    (40000, 8, 5, 0, 0),         # 40 terms: a 32-term pass over whole chunks + remainder, then 8 terms
     (20000 + 7, 2, 33, 0, 0),    # 66 terms, chunks + ragged remainder
-    (16384 * 3, 8, 4, 0, 0),     # one and a half chunks
+    (16384 * 7 + 1, 8, 4, 0, 0), # whole chunks and one element
     (RED_CHUNK * 3, 8, 4, 0, 0), # whole chunks only
-    (RED_CHUNK * 2 + RED_SUB * 7 + 5, 8, 4, 0, 0),   # last chunk: eight sub-chunks, 5 elements in the eighth
+    (RED_CHUNK * 2 + RED_SUB * 3 + 5, 8, 4, 0, 0),   # last chunk: four sub-chunks, 5 elements in the fourth
     (RED_CHUNK + RED_SUB - 1, 4, 8, 0, 0),           # last chunk: one sub-chunk, a straddling group of 3
     (RED_CHUNK - 1, 8, 4, 0, 0), (RED_CHUNK + 1, 8, 4, 0, 0),
     (4097, 8, 4, 1, 0), (4097, 8, 4, 3, 1), (4096, 4, 2, 0, 2),   # misaligned slices / out
     (70001, 8, 4, 1, 0),         # misaligned, large
     (30011, 5, 7, 0, 0),         # 35 terms: a 32-term pass (long chunks), then 3 terms (short chunks)
-    (16384 * 2 + 4096 * 3 + 5, 8, 4, 0, 0),   # last chunk cut into four sub-chunks, the fourth holding 5 elements
-    (16384 + 4095, 4, 8, 0, 0),  # a single partial chunk: five sub-chunks, a straddling group of 3 elements
+    (16384 * 5 + 4096 * 2 + 4093, 8, 4, 0, 0),   # last chunk: three sub-chunks, a straddling group of 1
+    (16384 * 2 - 4096 + 3, 4, 8, 0, 0),          # last chunk: four sub-chunks, 3 elements in the fourth
     (4096 * 5 + 1027, 8, 1, 0, 0),   # few terms: last chunk of 1027 elements
     (1025, 8, 1, 0, 0), (4095, 16, 1, 0, 0), (4097, 17, 1, 0, 0),   # 16 / 17 terms: the chunk switch
     (25_297_920, 8, 1, 0, 0),    # one Llama-7B block shard, 8-buffer average
