@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
     L.fs_plan_upload.argtypes = [vp, vp, sz, vp]
     L.fs_plan_destroy.argtypes = [vp]
     L.fs_plan_destroy.restype = None
+    L.fs_plan_twin.argtypes = [vp, i32, ctypes.POINTER(vp)]
     L.fs_pack.argtypes = [vp, vp, vp, i32, vp]
     L.fs_unpack.argtypes = [vp, vp, vp, vp]
     L.fs_reduce_shard.argtypes = [i64, i32, i32, vp, vp, vp]
@@ -108,7 +109,7 @@ def lib() -> ctypes.CDLL:
     L.fs_stream_fill.argtypes = [vp, i64, ctypes.c_uint32, vp]
     L.fs_last_error.argtypes = []
     L.fs_last_error.restype = ctypes.c_char_p
-    for name in ("fs_plan", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
+    for name in ("fs_plan", "fs_plan_twin", "fs_plan_info", "fs_plan_param", "fs_plan_segments", "fs_plan_upload",
                  "fs_pack", "fs_unpack", "fs_reduce_shard", "fs_adamw_step", "fs_reduce_adamw_step",
                  "fs_reduce_shard_ex", "fs_pack_cast", "fs_reshard_plan", "fs_reshard_info",
                  "fs_reshard_upload", "fs_reshard", "fs_load_local", "fs_reduce_adamw_step_noalloc",
@@ -213,6 +214,16 @@ class Plan:
                     raise RuntimeError(f"parameter {p} has two runs on rank {rank}")
                 out[p] = (dst - r * c, src, ln)
         return out
+
+    def twin(self, dtype) -> "Plan":
+        """The plan of `dtype` elements at this plan's element positions
+        (fs_plan_twin): lays out the fp32 master, m and v of this plan's bf16
+        parameters element for element (not uploaded)."""
+        h = ctypes.c_void_p()
+        _check(lib().fs_plan_twin(self._h, _dtype_code(dtype), ctypes.byref(h)))
+        t = Plan(h.value)
+        t.shapes = self.shapes
+        return t
 
     def local_views(self, shard: torch.Tensor, rank: int) -> List[torch.Tensor]:
         """The sharded state dict of `rank`, zero-copy: for each parameter,

@@ -118,6 +118,98 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
+// The tables that depend on the element size: the unpack view (parameters
+// end to end on 16-byte boundaries), the tile grids, the workspace layout
+// and the size-dependent summary fields.  p->params, p->pack_segs and the
+// position fields of p->info are set; bad_alloc propagates to the caller.
+static void finalize_plan(fs_plan_s *p, fs_dtype dtype) {
+    const int64_t eb = dtype == FS_BF16 ? 2 : 4;
+    const int vec = (int)(16 / eb);
+    p->vec = vec;
+    const int32_t n_params = p->info.n_params, world = p->info.world;
+    const int64_t shard = p->info.shard_numel, gathered = p->info.gathered_numel;
+    const std::vector<Segment> &ps = p->pack_segs;
+    p->bufinfo.clear();
+    p->unpack_segs.clear();
+    p->pack_tiles_all.clear();
+    p->pack_tiles_rank.clear();
+    p->rank_tile_off.clear();
+    p->unpack_tiles.clear();
+    p->ws = fsi::WorkspaceLayout{};
+    // ---- unpack view: parameters laid end to end on 16-byte boundaries
+    p->bufinfo.resize(n_params);
+    int64_t vb = 0;
+    for (int32_t i = 0; i < n_params; ++i) {
+        p->bufinfo[i].vbase = vb;
+        p->bufinfo[i].numel = p->params[i].numel;
+        vb += align_up(p->params[i].numel, vec);
+    }
+    p->unpack_segs.reserve(ps.size());
+    for (const Segment &s : ps)
+        p->unpack_segs.push_back(Segment{p->bufinfo[s.buf].vbase + s.src_off, s.vx, s.len, s.buf, s.rank});
+    std::sort(p->unpack_segs.begin(), p->unpack_segs.end(),
+              [](const Segment &a, const Segment &b) { return a.vx < b.vx; });
+
+    // ---- tiles
+    // Per-rank grids (anchored at each shard's start).  When every shard
+    // starts on a 16-byte block of the gathered buffer, their concatenation
+    // is also a grid anchored at 0 and serves the all-ranks pack: one table.
+    p->rank_tile_off.push_back(0);
+    p->pack_tiles_rank.reserve((size_t)world * (size_t)(ceil_div(ceil_div(shard, vec), fsi::kCopyTileBlocks) + 1));
+    for (int32_t r = 0; r < world; ++r) {
+        fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, fsi::kCopyTileBlocks,
+                         p->pack_tiles_rank);
+        p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
+    }
+    const bool shared_grid = world == 1 || shard % vec == 0;
+    if (!shared_grid) {
+        p->pack_tiles_all.reserve((size_t)(ceil_div(ceil_div(gathered, vec), fsi::kCopyTileBlocks) + 1));
+        fsi::build_tiles(ps, 0, gathered, vec, fsi::kCopyTileBlocks, p->pack_tiles_all);
+    }
+    p->unpack_tiles.reserve((size_t)(ceil_div(ceil_div(vb, vec), fsi::kCopyTileBlocks) + 1));
+    fsi::build_tiles(p->unpack_segs, 0, vb, vec, fsi::kCopyTileBlocks, p->unpack_tiles);
+    for (Tile &t : p->unpack_tiles)
+        if (t.run_buf >= 0) t.run_dst = t.x_begin - p->bufinfo[t.run_buf].vbase;
+
+    // ---- workspace layout (each table on a 256-byte boundary)
+    fsi::WorkspaceLayout &w = p->ws;
+    int64_t off = 0;
+    auto place = [&](int64_t count, int64_t elem, int64_t *o, int64_t *n) {
+        *o = off;
+        *n = count;
+        off = align_up(off + count * elem, 256);
+    };
+    place((int64_t)ps.size(), sizeof(Segment), &w.pack_segs, &w.n_pack_segs);
+    place((int64_t)p->unpack_segs.size(), sizeof(Segment), &w.unpack_segs, &w.n_unpack_segs);
+    place((int64_t)p->pack_tiles_all.size(), sizeof(Tile), &w.pack_tiles_all, &w.n_pack_tiles_all);
+    place((int64_t)p->pack_tiles_rank.size(), sizeof(Tile), &w.pack_tiles_rank, &w.n_pack_tiles_rank);
+    if (shared_grid) {   // the all-ranks launch reads the per-rank table
+        w.pack_tiles_all = w.pack_tiles_rank;
+        w.n_pack_tiles_all = w.n_pack_tiles_rank;
+    }
+    place((int64_t)p->unpack_tiles.size(), sizeof(Tile), &w.unpack_tiles, &w.n_unpack_tiles);
+    place((int64_t)p->bufinfo.size(), sizeof(fsi::BufInfo), &w.bufinfo, &w.n_bufinfo);
+    place((int64_t)p->local_first.size(), sizeof(int64_t), &w.local_first, &w.n_local_first);
+    w.total_bytes = std::max<int64_t>(off, 256);
+
+    // ---- summary: element type, workspace and ledger
+    fs_plan_info_t &I = p->info;
+    I.dtype = dtype;
+    I.elem_bytes = (int32_t)eb;
+    I.workspace_bytes = w.total_bytes;
+    const double b = (double)eb, bopt = (double)I.bopt, Pd = (double)I.total_numel, Nd = (double)world;
+    const double acc = I.grad_acc > 1 ? 4.0 : 0.0;   // fp32 gradient accumulator
+    const double per_param = 2.0 * b + bopt + acc;
+    I.ledger_ideal_bytes = Pd * per_param / Nd;
+    I.ledger_padded_bytes = (double)shard * per_param;
+    I.ledger_ddp_bytes = Pd * (2.0 * b + bopt) + acc * Pd;
+    I.ledger_zero1_bytes = 2.0 * Pd * b + Pd * bopt / Nd + acc * Pd;
+    I.ledger_zero2_bytes = Pd * b + Pd * (b + bopt) / Nd + acc * Pd / Nd;
+    I.peak_full_shard_bytes = I.ledger_ideal_bytes + Pd * b;
+    I.comm_full_shard_bytes = 3.0 * Pd * (Nd - 1.0) / Nd * b;
+    I.comm_shard_grad_op_bytes = 2.0 * Pd * (Nd - 1.0) / Nd * b;
+}
+
 extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dims,
                        fs_dtype dtype, int32_t world, int32_t use_orig_params,
                        fs_mode mode, int32_t grad_acc, fs_plan_t *out) {
@@ -254,71 +346,13 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
         p->local_first.assign((size_t)world * (size_t)n_params, 0);
         for (const Segment &sg : ps) p->local_first[(size_t)sg.rank * (size_t)n_params + (size_t)sg.buf] = sg.src_off;
 
-        // ---- unpack view: parameters laid end to end on 16-byte boundaries
-        p->bufinfo.resize(n_params);
-        int64_t vb = 0;
-        for (int32_t i = 0; i < n_params; ++i) {
-            p->bufinfo[i].vbase = vb;
-            p->bufinfo[i].numel = p->params[i].numel;
-            vb += align_up(p->params[i].numel, vec);
-        }
-        p->unpack_segs.reserve(ps.size());
-        for (const Segment &s : ps)
-            p->unpack_segs.push_back(Segment{p->bufinfo[s.buf].vbase + s.src_off, s.vx, s.len, s.buf, s.rank});
-        std::sort(p->unpack_segs.begin(), p->unpack_segs.end(),
-                  [](const Segment &a, const Segment &b) { return a.vx < b.vx; });
-
-        // ---- tiles
-        // Per-rank grids (anchored at each shard's start).  When every shard
-        // starts on a 16-byte block of the gathered buffer, their concatenation
-        // is also a grid anchored at 0 and serves the all-ranks pack: one table.
-        p->rank_tile_off.push_back(0);
-        p->pack_tiles_rank.reserve((size_t)world * (size_t)(ceil_div(ceil_div(shard, vec), fsi::kCopyTileBlocks) + 1));
-        for (int32_t r = 0; r < world; ++r) {
-            fsi::build_tiles(ps, (int64_t)r * shard, (int64_t)(r + 1) * shard, vec, fsi::kCopyTileBlocks,
-                             p->pack_tiles_rank);
-            p->rank_tile_off.push_back((int64_t)p->pack_tiles_rank.size());
-        }
-        const bool shared_grid = world == 1 || shard % vec == 0;
-        if (!shared_grid) {
-            p->pack_tiles_all.reserve((size_t)(ceil_div(ceil_div(gathered, vec), fsi::kCopyTileBlocks) + 1));
-            fsi::build_tiles(ps, 0, gathered, vec, fsi::kCopyTileBlocks, p->pack_tiles_all);
-        }
-        p->unpack_tiles.reserve((size_t)(ceil_div(ceil_div(vb, vec), fsi::kCopyTileBlocks) + 1));
-        fsi::build_tiles(p->unpack_segs, 0, vb, vec, fsi::kCopyTileBlocks, p->unpack_tiles);
-        for (Tile &t : p->unpack_tiles)
-            if (t.run_buf >= 0) t.run_dst = t.x_begin - p->bufinfo[t.run_buf].vbase;
-
-        // ---- workspace layout (each table on a 256-byte boundary)
-        fsi::WorkspaceLayout &w = p->ws;
-        int64_t off = 0;
-        auto place = [&](int64_t count, int64_t elem, int64_t *o, int64_t *n) {
-            *o = off;
-            *n = count;
-            off = align_up(off + count * elem, 256);
-        };
-        place((int64_t)ps.size(), sizeof(Segment), &w.pack_segs, &w.n_pack_segs);
-        place((int64_t)p->unpack_segs.size(), sizeof(Segment), &w.unpack_segs, &w.n_unpack_segs);
-        place((int64_t)p->pack_tiles_all.size(), sizeof(Tile), &w.pack_tiles_all, &w.n_pack_tiles_all);
-        place((int64_t)p->pack_tiles_rank.size(), sizeof(Tile), &w.pack_tiles_rank, &w.n_pack_tiles_rank);
-        if (shared_grid) {   // the all-ranks launch reads the per-rank table
-            w.pack_tiles_all = w.pack_tiles_rank;
-            w.n_pack_tiles_all = w.n_pack_tiles_rank;
-        }
-        place((int64_t)p->unpack_tiles.size(), sizeof(Tile), &w.unpack_tiles, &w.n_unpack_tiles);
-        place((int64_t)p->bufinfo.size(), sizeof(fsi::BufInfo), &w.bufinfo, &w.n_bufinfo);
-        place((int64_t)p->local_first.size(), sizeof(int64_t), &w.local_first, &w.n_local_first);
-        w.total_bytes = std::max<int64_t>(off, 256);
-
-        // ---- summary and ledger
+        // ---- summary (positions), then the element-size-dependent tables
         fs_plan_info_t &I = p->info;
         I.mode = mode;
-        I.dtype = dtype;
         I.world = world;
         I.use_orig_params = use_orig_params;
         I.grad_acc = grad_acc;
         I.n_params = n_params;
-        I.elem_bytes = (int32_t)eb;
         I.bopt = 12;
         I.total_numel = total;
         I.flat_numel = mode == FS_FSDP1_FLAT ? flat : 0;
@@ -327,18 +361,7 @@ extern "C" int fs_plan(int32_t n_params, const int32_t *ndim, const int64_t *dim
         I.align_pad = align_pad;
         I.tail_pad = mode == FS_FSDP1_FLAT ? gathered - flat : gathered - total;
         I.n_segments = (int64_t)ps.size();
-        I.workspace_bytes = w.total_bytes;
-        const double b = (double)eb, bopt = (double)I.bopt, Pd = (double)total, Nd = (double)world;
-        const double acc = grad_acc > 1 ? 4.0 : 0.0;   // fp32 gradient accumulator
-        const double per_param = 2.0 * b + bopt + acc;
-        I.ledger_ideal_bytes = Pd * per_param / Nd;
-        I.ledger_padded_bytes = (double)shard * per_param;
-        I.ledger_ddp_bytes = Pd * (2.0 * b + bopt) + acc * Pd;
-        I.ledger_zero1_bytes = 2.0 * Pd * b + Pd * bopt / Nd + acc * Pd;
-        I.ledger_zero2_bytes = Pd * b + Pd * (b + bopt) / Nd + acc * Pd / Nd;
-        I.peak_full_shard_bytes = I.ledger_ideal_bytes + Pd * b;
-        I.comm_full_shard_bytes = 3.0 * Pd * (Nd - 1.0) / Nd * b;
-        I.comm_shard_grad_op_bytes = 2.0 * Pd * (Nd - 1.0) / Nd * b;
+        finalize_plan(p, dtype);
     } catch (const std::bad_alloc &) {
         delete p;
         return fsi::fail(FS_E_NOMEM, "fs_plan: out of host memory");
@@ -377,6 +400,32 @@ extern "C" int fs_plan_segments(fs_plan_t plan, fs_segment_t *out, int64_t cap, 
 }
 
 extern "C" void fs_plan_destroy(fs_plan_t plan) { delete plan; }
+
+// The same element positions with another element type: the parameter list,
+// segments and per-rank pieces are copied, the element-size tables rebuilt.
+extern "C" int fs_plan_twin(fs_plan_t plan, fs_dtype dtype, fs_plan_t *out) {
+    fsi::clear_error();
+    if (!plan || !out) return fsi::fail(FS_E_INVAL, "fs_plan_twin: NULL argument");
+    *out = nullptr;
+    if (dtype != FS_BF16 && dtype != FS_FP32) return fsi::fail(FS_E_DTYPE, "fs_plan_twin: unknown dtype %d", (int)dtype);
+    int64_t bytes;
+    if (!mul_ok(plan->info.gathered_numel, dtype == FS_BF16 ? 2 : 4, &bytes))
+        return fsi::fail(FS_E_OVERFLOW, "fs_plan_twin: gathered size overflows int64");
+    fs_plan_s *p = new (std::nothrow) fs_plan_s();
+    if (!p) return fsi::fail(FS_E_NOMEM, "fs_plan_twin: out of host memory");
+    try {
+        p->info = plan->info;
+        p->params = plan->params;
+        p->pack_segs = plan->pack_segs;
+        p->local_first = plan->local_first;
+        finalize_plan(p, dtype);
+    } catch (const std::bad_alloc &) {
+        delete p;
+        return fsi::fail(FS_E_NOMEM, "fs_plan_twin: out of host memory");
+    }
+    *out = p;
+    return FS_OK;
+}
 
 // ---------------------------------------------------------------- reshard --
 //

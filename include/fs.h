@@ -208,6 +208,28 @@ int fs_plan_upload(fs_plan_t plan, void *workspace, size_t bytes, hipStream_t st
 void fs_plan_destroy(fs_plan_t plan);
 
 /*
+ * fs_plan_twin -- a plan with the same element positions as `plan` and
+ * elements of `dtype` (host only, not uploaded): every element of the twin's
+ * gathered buffer and shards holds the same parameter element as in plan's.
+ * It lays out state kept beside the parameters, element for element: the
+ * fp32 master, m and v of a group's bf16 parameters [DPZ sections 1 and 9.1:
+ * each rank updates its own slice of them].  FSDP1's use_orig_params
+ * alignment follows the parameter dtype [FvF section 03], so a plan made
+ * directly with FS_FP32 places those elements differently; the twin's pack,
+ * unpack, re-shard and fs_load_local move the state where the bf16 plan's
+ * elements are.  For FSDP2, and FSDP1 without use_orig_params, the twin
+ * equals the plan made with `dtype`.
+ *
+ *   plan           any plan.
+ *   dtype          FS_BF16 or FS_FP32: the twin's element type.
+ *   out   (host)   receives the twin; release it with fs_plan_destroy.
+ * info of the twin: the plan's, with dtype, elem_bytes, workspace_bytes and
+ * the ledger fields (computed with the twin's element size) replaced.
+ * Errors: FS_E_INVAL (NULL), FS_E_DTYPE, FS_E_OVERFLOW, FS_E_NOMEM.
+ */
+int fs_plan_twin(fs_plan_t plan, fs_dtype dtype, fs_plan_t *out);
+
+/*
  * fs_pack -- the all-gather copy-in [FvF section 03: FSDP2 copies each
  * parameter's shard into the group's concatenated all-gather input; FSDP1's
  * flat is chunked].
@@ -279,7 +301,7 @@ void fs_reshard_destroy(fs_reshard_t r);
  * sharded state dict, saved and loaded per rank without communication; the
  * FSDP tutorial page (m.xxqk.cn), section 3.3: sharded checkpoints are
  * loaded rank by rank].  The inverse of viewing a shard's local pieces: with
- * the plan's fp32 twin the same call restores master, m or v.
+ * the plan's fp32 twin (fs_plan_twin) the same call restores master, m or v.
  *
  *   rank            0 <= rank < N.
  *   pieces (device) array of n_params device pointers; entry i points to the

@@ -23,7 +23,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import List, Optional, Sequence
 
 import numpy as np
@@ -163,6 +163,14 @@ class Layout:
         return _CLayout(self.mode, self.n_params, self.world, self.elem_bytes,
                         self.shard, _ptr(k[0]), _ptr(k[1]), _ptr(k[2]),
                         _ptr(k[3]), _ptr(k[4]))
+
+    def with_elem_bytes(self, elem_bytes: int) -> "Layout":
+        """The same element positions holding elements of `elem_bytes` bytes:
+        the layout of state kept element for element beside the parameters
+        (the fp32 master, m and v of bf16 parameters, "Data parallelism, ZeRO
+        and FSDP" sections 1 and 9.1).  Only the copies change."""
+        assert elem_bytes in (2, 4)
+        return replace(self, elem_bytes=elem_bytes)
 
     def index_map(self) -> np.ndarray:
         """Gathered index of every parameter element, parameters in order."""

@@ -3,9 +3,9 @@
 // of the oracle (oracle/fs_oracle.c).  Test infrastructure: it links both only
 // to compare them.  It runs the integer code that decides every index the
 // kernels use -- layouts, segment lowering, tile building, the re-shard piece
-// intersection -- over exhaustive tiny parameter lists, the workload shapes
-// and the documented error paths, and checks the planner's element map
-// against the oracle's.  Exit status 0 and a final "ok" line mean clean.
+// intersection, the twin of the other element size -- over exhaustive tiny
+// parameter lists, the workload shapes and the documented error paths, and
+// checks the planner's element map against the oracle's.  Exit status 0 and a final "ok" line mean clean.
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -132,6 +132,16 @@ static void check_case(const Shapes &sh, fs_dtype dt, int32_t world, int32_t uo,
         oracle_index_map(&L, want.data());
         for (size_t k = 0; k < got.size(); ++k) EXPECT(got[k] == want[k], "element %zu: %lld vs %lld", k,
                                                        (long long)got[k], (long long)want[k]);
+    }
+    // the twin of the other element size places every element where p does
+    fs_plan_t t = nullptr;
+    rc = fs_plan_twin(p, dt == FS_BF16 ? FS_FP32 : FS_BF16, &t);
+    EXPECT(rc == FS_OK, "fs_plan_twin rc %d: %s", rc, fs_last_error());
+    if (rc == FS_OK) {
+        fs_plan_info_t TI;
+        fs_plan_info(t, &TI);
+        EXPECT(TI.gathered_numel == I.gathered_numel && plan_map(t, TI) == got, "the twin moves elements");
+        fs_plan_destroy(t);
     }
     ++g_checked;
     if (keep) *keep = p;

@@ -430,3 +430,35 @@ def test_bench_launch_spans_match_the_library():
     assert bench.launches_per_call("reduce", S, 40, 8) == 52
     assert bench.launches_per_call("reduce_bf16_reduce_dtype", S, 32, 8) == 51
     assert bench.launches_per_call("adamw", S) == 13
+
+
+@pytest.mark.parametrize("kind,uo", [("fsdp1", True), ("fsdp1", False), ("fsdp2", False)])
+def test_plan_twin_keeps_element_positions(kind, uo):
+    """fs_plan_twin: the twin places every element where the plan does (equal to
+    the oracle's layout of the plan's dtype), with the other element size; for
+    FSDP2 and FSDP1 without use_orig_params it equals the plan made directly
+    with that dtype, and with use_orig_params it does not (the alignment
+    follows the parameter dtype)."""
+    shapes = [(6, 3), (9,), (1, 1), (13, 5), (0, 2), (33, 16), (7,)]
+    for N in (1, 3, 4, 8):
+        P = fs.fs_plan(shapes, "bf16", N, uo, kind, 2)
+        T = P.twin("fp32")
+        assert T.info.elem_bytes == 4 and T.info.dtype == fs.FS_FP32
+        for f in ("mode", "world", "use_orig_params", "grad_acc", "n_params", "total_numel", "flat_numel",
+                  "shard_numel", "gathered_numel", "align_pad", "tail_pad", "n_segments"):
+            assert getattr(T.info, f) == getattr(P.info, f), f
+        assert T.segments() == P.segments()
+        L = _oracle_layout(kind, shapes, 2, N, uo)
+        np.testing.assert_array_equal(_plan_index_map(T), L.with_elem_bytes(4).index_map())
+        D = fs.fs_plan(shapes, "fp32", N, uo, kind, 2)
+        if kind == "fsdp1" and uo:
+            assert D.segments() != T.segments()
+        else:
+            assert D.segments() == T.segments()
+            assert D.info.workspace_bytes == T.info.workspace_bytes
+            assert abs(D.info.ledger_ideal_bytes - T.info.ledger_ideal_bytes) < 1e-6
+        back = T.twin("bf16")
+        assert back.segments() == P.segments() and back.info.workspace_bytes == P.info.workspace_bytes
+    L = fs.lib()
+    assert L.fs_plan_twin(None, fs.FS_FP32, ctypes.byref(ctypes.c_void_p())) == fs.FS_E_INVAL
+    assert L.fs_plan_twin(P._h, 7, ctypes.byref(ctypes.c_void_p())) == fs.FS_E_DTYPE

@@ -120,11 +120,12 @@ def test_training_steps_match_oracle(case, variant):
 
 
 RESUME_CASES = [
-    # (name, mode, shapes, N, N2): FSDP2 and the FSDP1 flat parameter without alignment, whose
-    # element positions are the same for bf16 parameters and fp32 state
-    ("fsdp2_mixed_4_to_2", "fsdp2", MIXED, 4, 2),
-    ("fsdp2_llama_block_d256_8_to_2", "fsdp2", synth.llama_block_shapes(256, 688), 8, 2),
-    ("fsdp1_flat_mixed_4_to_2", "fsdp1", MIXED, 4, 2),
+    # (name, mode, use_orig_params, shapes, N, N2); the fp32 state is laid out by the bf16
+    # plans' fp32 twins (fs_plan_twin), at the bf16 elements' positions
+    ("fsdp2_mixed_4_to_2", "fsdp2", False, MIXED, 4, 2),
+    ("fsdp2_llama_block_d256_8_to_2", "fsdp2", False, synth.llama_block_shapes(256, 688), 8, 2),
+    ("fsdp1_flat_mixed_4_to_2", "fsdp1", False, MIXED, 4, 2),
+    ("fsdp1_orig_params_mixed_4_to_2", "fsdp1", True, MIXED, 4, 2),
 ]
 
 
@@ -153,20 +154,19 @@ def test_resume_at_another_rank_count(case, variant):
     and AdamW kernels, or as the fused reduce + AdamW."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    name, mode, shapes, N, N2 = case
+    name, mode, uo, shapes, N, N2 = case
     A2 = N // N2
     say("resume at another rank count", name, variant, N, N2)
 
-    def plan(n, dt):
-        return fs.fs_plan(shapes, dt, n, False, mode).upload()
+    def layout(n):
+        return oracle.fsdp2_layout(shapes, 2, n) if mode == "fsdp2" else oracle.fsdp1_layout(shapes, 2, n, uo)
 
-    def layout(n, eb):
-        return oracle.fsdp2_layout(shapes, eb, n) if mode == "fsdp2" else oracle.fsdp1_layout(shapes, eb, n, False)
-
-    P, Pf, Q, Qf = plan(N, "bf16"), plan(N, "fp32"), plan(N2, "bf16"), plan(N2, "fp32")
-    L, Lf, M, Mf = layout(N, 2), layout(N, 4), layout(N2, 2), layout(N2, 4)
-    np.testing.assert_array_equal(L.index_map(), Lf.index_map())
-    np.testing.assert_array_equal(M.index_map(), Mf.index_map())
+    P, Q = (fs.fs_plan(shapes, "bf16", n, uo, mode) for n in (N, N2))
+    Pf, Qf = P.twin("fp32").upload(), Q.twin("fp32").upload()
+    P.upload()
+    Q.upload()
+    L, M = layout(N), layout(N2)
+    Lf, Mf = L.with_elem_bytes(4), M.with_elem_bytes(4)
     numel = [int(np.prod(s)) if len(s) else 1 for s in shapes]
     n, n2 = P.gathered_numel, Q.gathered_numel
 

@@ -214,3 +214,35 @@ def test_reshard_is_unpack_then_pack():
             np.testing.assert_array_equal(oracle.reshard(Ls, Ls, g), g)
             for Ld in layouts:
                 np.testing.assert_array_equal(oracle.reshard(Ls, Ld, g), oracle.pack(Ld, oracle.unpack(Ls, g)))
+
+
+def test_layout_with_other_element_size():
+    """Layout.with_elem_bytes keeps every element's gathered index and copies
+    elements of the new size: for FSDP2 and FSDP1 without use_orig_params it
+    is the layout built with that size; with use_orig_params (alignment by the
+    parameter dtype) the 4-byte layout built directly places elements
+    elsewhere, the derived one where the 2-byte layout does.  Pack and unpack
+    round-trip 4-byte elements at those positions with zero pads."""
+    shapes = [(6, 3), (9,), (1, 1), (13, 5), (0, 2), (33, 16), (7,)]
+    rng = np.random.default_rng(4)
+    for N in (1, 3, 8):
+        for build, uo in ((lambda eb: oracle.fsdp2_layout(shapes, eb, N), False),
+                          (lambda eb: oracle.fsdp1_layout(shapes, eb, N, False), False),
+                          (lambda eb: oracle.fsdp1_layout(shapes, eb, N, True), True)):
+            L2, L4 = build(2), build(4)
+            T = L2.with_elem_bytes(4)
+            np.testing.assert_array_equal(T.index_map(), L2.index_map())
+            assert T.gathered_numel == L2.gathered_numel and T.elem_bytes == 4
+            if uo:
+                assert not np.array_equal(L4.index_map(), T.index_map())
+            else:
+                np.testing.assert_array_equal(L4.index_map(), T.index_map())
+            params = [rng.integers(1, 1 << 32, size=int(n), dtype=np.uint64).astype(np.uint32) for n in T.numel]
+            g = oracle.pack(T, params)
+            assert g.dtype == np.uint32
+            pads = np.ones(g.size, bool)
+            pads[T.index_map()] = False
+            assert not g[pads].any()
+            np.testing.assert_array_equal(g[T.index_map()], np.concatenate(params))
+            for a, b in zip(oracle.unpack(T, g), params):
+                np.testing.assert_array_equal(a, b)

@@ -87,18 +87,22 @@ def test_sharded_chain_equals_unsharded_adamw(case):
         assert not np.any(th[pads]) and not np.any(m[pads]) and not np.any(v[pads]) and not np.any(g_bits[pads])
 
 
-@pytest.mark.parametrize("mode,N,N2", [("fsdp2", 4, 2), ("fsdp2", 8, 2), ("fsdp1", 4, 2)])
-def test_resume_at_another_rank_count(mode, N, N2):
+@pytest.mark.parametrize("mode,uo,N,N2", [("fsdp2", False, 4, 2), ("fsdp2", False, 8, 2), ("fsdp1", False, 4, 2),
+                                          ("fsdp1", True, 4, 2), ("fsdp1", True, 8, 2)])
+def test_resume_at_another_rank_count(mode, uo, N, N2):
     """Re-sharding the state to N2 ranks and continuing there with
     grad_acc = N / N2 (micro-step gradients scaled by N2 / N, the 1/grad_acc of
     "Data parallelism, ZeRO and FSDP" section 5) gives exactly the state of
     continuing at N ranks, re-laid: power-of-two scaling is exact and the
     terms keep their order.  Pins reshard against the chain: a re-shard that
     moves an element to another's place, or a reduce that reorders terms or
-    divides by the wrong count, breaks the equality."""
+    divides by the wrong count, breaks the equality.  The fp32 state sits at
+    the bf16 elements' positions (Layout.with_elem_bytes), which FSDP1's
+    use_orig_params alignment makes differ from a 4-byte layout's."""
     A2 = N // N2
-    lay = lambda n, eb: oracle.fsdp2_layout(MIXED, eb, n) if mode == "fsdp2" else oracle.fsdp1_layout(MIXED, eb, n, False)
-    L, Lf, M, Mf = lay(N, 2), lay(N, 4), lay(N2, 2), lay(N2, 4)
+    lay = lambda n: oracle.fsdp2_layout(MIXED, 2, n) if mode == "fsdp2" else oracle.fsdp1_layout(MIXED, 2, n, uo)
+    L, M = lay(N), lay(N2)
+    Lf, Mf = L.with_elem_bytes(4), M.with_elem_bytes(4)
     numel = [int(np.prod(s)) if len(s) else 1 for s in MIXED]
     split = lambda x: np.split(x, np.cumsum(numel)[:-1])
     grads = lambda t, k: split(synth.to_numpy_bits(synth.normal_bf16(37, synth.stream_grad(0, k, N) + 100 * t,

@@ -207,3 +207,51 @@ def test_gpu_load_local_misaligned_pieces_and_errors():
         plan.load_local(shard, N, pieces)
     with pytest.raises(ValueError):
         plan.load_local(shard, r, pieces[:-1])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,N2", [(4, 2), (3, 5)])
+def test_gpu_twin_state_pack_unpack_import_reshard(N, N2):
+    """fp32 state kept at the element positions of a bf16 FSDP1 FlatParameter
+    with use_orig_params (alignment by the parameter dtype, "FSDP1 vs FSDP2"
+    section 03): the bf16 plan's fp32 twin packs, unpacks, imports a rank's
+    local pieces and re-shards it to N2 ranks, each bit for bit against the
+    oracle's bf16 layout carrying 4-byte elements; pads stay zero."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gpu_util import Guarded, bits, say
+    say("fp32 twin of an FSDP1 use_orig_params plan", N, N2)
+    shapes = [(1,), (7,), (0,), (3, 3), (2,), (17,), (5, 5)]
+    T = fs.fs_plan(shapes, "bf16", N, True, "fsdp1").twin("fp32").upload()
+    T2 = fs.fs_plan(shapes, "bf16", N2, True, "fsdp1").twin("fp32").upload()
+    L = oracle.fsdp1_layout(shapes, 2, N, True).with_elem_bytes(4)
+    L2 = oracle.fsdp1_layout(shapes, 2, N2, True).with_elem_bytes(4)
+    assert fs.fs_plan(shapes, "fp32", N, True, "fsdp1").segments() != T.segments()   # the case the twin is for
+    params = _params(shapes, "fp32", seed=43)
+    host = [p.reshape(-1).numpy().view(np.uint32) for p in params]
+    dev = [p.reshape(-1).view(torch.float32).cuda() for p in params]
+    G = Guarded(T.gathered_numel, torch.float32)
+    fs.fs_pack(T, dev, G.t)
+    outs = [Guarded(p.numel(), torch.float32, shift=i % 3) for i, p in enumerate(params)]
+    fs.fs_unpack(T, G.t, [o.t for o in outs])
+    torch.cuda.synchronize()
+    G.check()
+    want = oracle.pack(L, host)
+    np.testing.assert_array_equal(bits(G.t), want)
+    for o, h in zip(outs, host):
+        o.check()
+        np.testing.assert_array_equal(bits(o.t), h)
+    for r in range(N):
+        views = T.local_views(G.t[r * T.shard_numel:(r + 1) * T.shard_numel], r)
+        shard = Guarded(T.shard_numel, torch.float32, fill=None)
+        shard.t.view(torch.int32).fill_(0x5A5A5A5A)
+        T.load_local(shard.t, r, [v.contiguous() for v in views])
+        torch.cuda.synchronize()
+        shard.check()
+        np.testing.assert_array_equal(bits(shard.t), oracle.pack(L, host, rank=r), err_msg=f"rank {r}")
+    R = fs.fs_reshard_plan(T, T2).upload()
+    D = Guarded(T2.gathered_numel, torch.float32)
+    fs.fs_reshard(R, G.t, D.t)
+    torch.cuda.synchronize()
+    D.check()
+    np.testing.assert_array_equal(bits(D.t), oracle.reshard(L, L2, want))
