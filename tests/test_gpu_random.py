@@ -6,7 +6,8 @@ equal the oracle bit for bit.  The reduce family (fp32 and bf16 reduce
 dtype, fused reduce + AdamW) runs on random sizes, N, grad_acc and
 per-slice misalignment: reduces bit-exact, fused bit-identical to the two
 kernels, AdamW within its tolerance of the oracle.  Every buffer sits in a
-canary guard band.
+canary guard band.  fp32 state at random bf16 plans' element positions (the
+plans' fp32 twins) packs, unpacks and re-shards bit for bit as well.
 """
 import numpy as np
 import pytest
@@ -114,6 +115,49 @@ def test_random_layout_pack_unpack_reshard(seed):
     torch.cuda.synchronize()
     D.check()
     src.check()
+    np.testing.assert_array_equal(bits(D.t), oracle.reshard(L, L2, junk))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_twin_state(seed):
+    """fp32 state at a bf16 plan's element positions (fs_plan_twin): pack,
+    unpack and re-shard to another random plan's twin, against the oracle's
+    bf16 layouts carrying 4-byte elements, with random misalignment."""
+    shapes, _, mode, N, uo, mode2, N2, uo2, shifts = _random_case(100 + seed)
+    if mode == "fsdp1":
+        uo = True        # the case the twin is for: alignment by the bf16 parameter dtype
+    say("random twin", seed, mode, N, uo, "->", mode2, N2, uo2, len(shapes), "params")
+    T = fs.fs_plan(shapes, "bf16", N, uo, mode).twin("fp32").upload()
+    T2 = fs.fs_plan(shapes, "bf16", N2, uo2, mode2).twin("fp32").upload()
+    L = _olayout(mode, shapes, "bf16", N, uo).with_elem_bytes(4)
+    L2 = _olayout(mode2, shapes, "bf16", N2, uo2).with_elem_bytes(4)
+    params, off = [], 0
+    for s, sh in zip(shapes, shifts):
+        n = int(np.prod(s)) if len(s) else 1
+        params.append(Guarded(n, torch.float32, shift=sh,
+                              fill=synth.bits32(seed, synth.STREAM_MASTER, n, device="cuda", start=off).view(torch.float32)))
+        off += n
+    host = [bits(p.t) for p in params]
+    ref = oracle.pack(L, host)
+    G = Guarded(T.gathered_numel, torch.float32, shift=shifts[-1])
+    fs.fs_pack(T, [p.t for p in params], G.t)
+    torch.cuda.synchronize()
+    G.check()
+    np.testing.assert_array_equal(bits(G.t), ref)
+    junk = ref.copy()
+    mask = np.ones(junk.size, bool)
+    mask[L.index_map()] = False
+    junk[mask] = 0x7FFFFFFF
+    src = Guarded(T.gathered_numel, torch.float32, shift=shifts[-3], fill=from_bits(junk, torch.float32))
+    outs = [Guarded(p.n, torch.float32, shift=sh) for p, sh in zip(params, reversed(shifts))]
+    fs.fs_unpack(T, src.t, [o.t for o in outs])
+    D = Guarded(T2.gathered_numel, torch.float32, shift=shifts[0])
+    fs.fs_reshard(fs.fs_reshard_plan(T, T2).upload(), src.t, D.t)
+    torch.cuda.synchronize()
+    for o, h in zip(outs, host):
+        o.check()
+        np.testing.assert_array_equal(bits(o.t), h)
+    D.check()
     np.testing.assert_array_equal(bits(D.t), oracle.reshard(L, L2, junk))
 
 
