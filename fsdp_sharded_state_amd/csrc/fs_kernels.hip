@@ -1321,9 +1321,10 @@ void launch_fused(int64_t n, hipStream_t stream, const SliceArgs &sa, int cnt, i
     });
 }
 
-// One pass of the fp32 reduce over terms [t0, t0 + cnt): chunked when every
-// pointer is 16-byte aligned (one launch, the last chunk partial), else the
-// general kernel.
+// One pass of the fp32 reduce over terms [t0, t0 + cnt) and the sub-range
+// [off, off + len) of a call over n elements: chunked when every pointer is
+// 16-byte aligned (one launch, its last chunk partial; the residency cap is
+// decided on n), else the general kernel.
 void launch_reduce_pass(int64_t n, int64_t off, int64_t len, hipStream_t stream, const uint16_t *const *slices,
                         int t0, int cnt, int first, int last, float world, bool aligned, float *out) {
     SliceArgs sa;
