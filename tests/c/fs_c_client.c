@@ -6,8 +6,11 @@
  *   fs_c_client host   plan the worked example of "FSDP1 vs FSDP2" (Table 3:
  *                      two parameters of 3 and 5 elements, N = 4, bf16) under
  *                      FSDP1 (use_orig_params false / true) and FSDP2, and
- *                      the documented error returns; print one JSON line.
- *                      Makes no GPU call.
+ *                      the documented error returns; the fp32 twin of the
+ *                      use_orig_params plan beside the plan made directly
+ *                      with FS_FP32 (the twin keeps the bf16 alignment, the
+ *                      direct plan aligns fp32 elements); print one JSON
+ *                      line.  Makes no GPU call.
  *   fs_c_client gpu    on device 0: plan the tiny 2-layer MLP group (FSDP1,
  *                      use_orig_params, N = 4, grad_acc = 2), pack every
  *                      shard, unpack, reduce 8 constant gradient slices and
@@ -66,6 +69,18 @@ static int run_host(void) {
     print_plan("fsdp1_use_orig_params_true", f1t);
     printf(", ");
     print_plan("fsdp2", f2);
+    fs_plan_t twin = NULL, f1t32 = NULL;
+    int rc_twin = fs_plan_twin(f1t, FS_FP32, &twin);
+    int rc_f32 = fs_plan(2, ndim, dims, FS_FP32, 4, 1, FS_FSDP1_FLAT, 1, &f1t32);
+    fs_plan_info_t It;
+    int eb_twin = (rc_twin == FS_OK && fs_plan_info(twin, &It) == FS_OK) ? It.elem_bytes : 0;
+    printf(", \"twin_rc\": [%d, %d], \"twin_elem_bytes\": %d, ", rc_twin, rc_f32, eb_twin);
+    print_plan("fsdp1_use_orig_params_true_fp32_twin", twin);
+    printf(", ");
+    print_plan("fsdp1_use_orig_params_true_fp32_direct", f1t32);
+    fs_plan_t none = NULL;
+    int e_twin_dtype = fs_plan_twin(f1t, (fs_dtype)7, &none);
+    int e_twin_null = fs_plan_twin(NULL, FS_FP32, &none);
     int e_world = plan_shapes(2, ndim, dims, 0, 0, FS_FSDP1_FLAT, 1, &bad);
     int e_uo = plan_shapes(2, ndim, dims, 4, 1, FS_FSDP2_PER_PARAM, 1, &bad);
     const int64_t neg[2] = {3, -5};
@@ -73,11 +88,13 @@ static int run_host(void) {
     int e_acc = plan_shapes(2, ndim, dims, 4, 0, FS_FSDP1_FLAT, 0, &bad);
     const char *msg = fs_last_error();
     printf(", \"errors\": {\"world_0\": %d, \"use_orig_params_fsdp2\": %d, \"negative_dim\": %d, "
-           "\"grad_acc_0\": %d, \"last_error_nonempty\": %d}}\n",
-           e_world, e_uo, e_dim, e_acc, msg != NULL && msg[0] != '\0');
+           "\"grad_acc_0\": %d, \"twin_bad_dtype\": %d, \"twin_null\": %d, \"last_error_nonempty\": %d}}\n",
+           e_world, e_uo, e_dim, e_acc, e_twin_dtype, e_twin_null, msg != NULL && msg[0] != '\0');
     fs_plan_destroy(f1f);
     fs_plan_destroy(f1t);
     fs_plan_destroy(f2);
+    fs_plan_destroy(twin);
+    fs_plan_destroy(f1t32);
     return 0;
 }
 

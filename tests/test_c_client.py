@@ -25,7 +25,7 @@ sys.path.insert(0, os.path.join(HERE, "c"))
 import build_client  # noqa: E402
 
 GOLDEN = json.load(open(os.path.join(HERE, "golden", "worked_example.json")))
-FS_E_INVAL, FS_E_UNSUPPORTED = -1, -2
+FS_E_INVAL, FS_E_UNSUPPORTED, FS_E_DTYPE = -1, -2, -3
 
 
 @pytest.fixture(scope="module")
@@ -62,7 +62,28 @@ def test_c_client_host_worked_example(client):
     rank0 = [s for s in rec["fsdp2"]["segments"] if s[4] == 0]
     assert [s[2] for s in sorted(rank0, key=lambda s: s[3])] == GOLDEN["fsdp2_per_param_chunk_elements"]
     assert rec["errors"] == {"world_0": FS_E_INVAL, "use_orig_params_fsdp2": FS_E_UNSUPPORTED,
-                             "negative_dim": FS_E_INVAL, "grad_acc_0": FS_E_INVAL, "last_error_nonempty": 1}
+                             "negative_dim": FS_E_INVAL, "grad_acc_0": FS_E_INVAL,
+                             "twin_bad_dtype": FS_E_DTYPE, "twin_null": FS_E_INVAL, "last_error_nonempty": 1}
+
+
+def test_c_client_host_fp32_twin(client):
+    """From C, the fp32 twin of the worked example's use_orig_params plan
+    keeps the bf16 plan's positions (the 16-byte alignment counted in 2-byte
+    elements: 5 pad elements before the second parameter, 4 elements per
+    rank), while the plan made directly with FS_FP32 aligns 4-byte elements
+    (1 pad element, 3 per rank): "FSDP1 vs FSDP2", section 03."""
+    rec = json.loads(subprocess.run([client, "host"], capture_output=True, text=True, timeout=60,
+                                    check=True).stdout)
+    assert rec["twin_rc"] == [0, 0] and rec["twin_elem_bytes"] == 4
+    shapes, N = [tuple(s) for s in GOLDEN["shapes"]], GOLDEN["world"]
+    bf, tw, d32 = (rec["fsdp1_use_orig_params_true" + k] for k in ("", "_fp32_twin", "_fp32_direct"))
+    for k in ("shard_numel", "gathered_numel", "align_pad", "tail_pad", "segments"):
+        assert tw[k] == bf[k]
+    L = oracle.fsdp1_layout(shapes, 2, N, True)
+    _check_segments(tw, L.with_elem_bytes(4), tw["shard_numel"])
+    D = oracle.fsdp1_layout(shapes, 4, N, True)
+    assert d32["shard_numel"] == 3 and d32["gathered_numel"] == 12 and d32["align_pad"] == 1
+    _check_segments(d32, D, 3)
 
 
 @pytest.mark.gpu
