@@ -368,9 +368,13 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const Segment *__restr
 // to nearest even.  Same tiles and segments as the bit-copy pack (they are in
 // destination elements); a 16-byte destination block of 8 bf16 needs 32
 // source bytes: up to three aligned 16-byte loads and two funnel shifts.
-// Single-run tiles with a 16-byte-aligned source (the usual case) issue all
-// their lane's loads before converting and storing: 4% faster than one block
-// at a time.
+// Single-run tiles with a 16-byte-aligned source (the usual case) go by
+// half-blocks instead: a lane loads 16 contiguous source bytes (the wave's
+// loads cover 1 KB without gaps) and stores their 8 destination bytes, all of
+// the lane's loads issued before any conversion.  With the launch capped at
+// six workgroups per CU this measured 3% faster on the 7B groups than whole
+// blocks per lane (two 16-byte loads 32 bytes apart, one 16-byte store)
+// uncapped, which had been 4% faster than one block at a time.
 
 __device__ __forceinline__ uint16_t bf16_rne_bits(uint32_t u) {
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
@@ -411,21 +415,23 @@ __global__ __launch_bounds__(kThreads) void pack_cast_kernel(const Segment *__re
                           (reinterpret_cast<uintptr_t>(dst0) & 15) == 0;
     if (dst_full && t.run_buf >= 0) {   // one contiguous run: 32 source bytes per block
         const intptr_t src = reinterpret_cast<intptr_t>(params[t.run_buf]) + t.run_src * 4;
-        if ((src & 15) == 0) {   // aligned source: all loads in flight, then convert and store
-            constexpr int U = fsi::kBlocksPerThread;
-            u32x4 lo[U], hi[U];
+        if ((src & 15) == 0) {   // aligned source: half-blocks, all loads in flight, then convert and store
+            constexpr int U = 2 * fsi::kBlocksPerThread;
+            const int nh = 2 * t.nblk;   // half-block h: source bytes [16h, 16h+16), destination [8h, 8h+8)
+            u32x4 x[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int b = u * kThreads + threadIdx.x;
-                if (b < t.nblk) {
-                    lo[u] = ld16(reinterpret_cast<const char *>(src + 32 * (intptr_t)b));
-                    hi[u] = ld16(reinterpret_cast<const char *>(src + 32 * (intptr_t)b + 16));
-                }
+                const int h = u * kThreads + threadIdx.x;
+                if (h < nh) x[u] = ld16(reinterpret_cast<const char *>(src + 16 * (intptr_t)h));
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int b = u * kThreads + threadIdx.x;
-                if (b < t.nblk) st16(dst0 + 16 * (int64_t)b, cvt8_bf16(lo[u], hi[u]));
+                const int h = u * kThreads + threadIdx.x;
+                if (h < nh) {
+                    const u32x2 w = {(uint32_t)bf16_rne_bits(x[u].x) | ((uint32_t)bf16_rne_bits(x[u].y) << 16),
+                                     (uint32_t)bf16_rne_bits(x[u].z) | ((uint32_t)bf16_rne_bits(x[u].w) << 16)};
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(dst0 + 8 * (int64_t)h));
+                }
             }
             return;
         }
@@ -1184,8 +1190,10 @@ AdamConsts adam_consts(const fs_adamw_hparams_t &hp) {
 // bf16-reduce-dtype kernels 3% at two (8 groups per lane) and three (4
 // groups).  Of the copy kernels the unpack and the re-shard, whose loads do
 // not wait for a pointer-table read, run capped at six per CU (1.6% and 2.6%
-// faster); the pack and the cast pack, which read the parameter pointer
-// table before their loads, measured slower capped.  A cap of k is set
+// faster); the pack, which reads the parameter pointer table before its
+// loads, measured slower capped; the cast pack, whose loads are twice its
+// stores, runs capped at six (3% faster with its half-block loads; five and
+// seven 1% slower than six, four 7%).  A cap of k is set
 // by reserving dynamic LDS that the kernel never touches: with L bytes of
 // LDS per CU, L / (k + 1) + 1 bytes per workgroup let k workgroups fit but
 // not k + 1.  Grids shorter than kCapMinRounds rounds of resident
@@ -1199,6 +1207,7 @@ constexpr int kRsFewWgsPerCu = 3;      // reduce_rs_chunk_kernel<kRsGroupsFew>
 constexpr int kAdamWgsPerCu = 12;      // adamw_kernel (one wave per workgroup)
 constexpr int kUnpackWgsPerCu = 6;     // unpack_kernel (registers allow 7-8)
 constexpr int kReshardWgsPerCu = 6;    // scatter_kernel<W, UnpackSrc> (registers allow 8)
+constexpr int kCastWgsPerCu = 6;       // pack_cast_kernel (registers allow 8)
 constexpr int64_t kCapMinRounds = 16;
 
 // Long calls run as consecutive launches over sub-ranges of at most kSpan
@@ -1702,7 +1711,8 @@ extern "C" int fs_pack_cast(fs_plan_t plan, const void *const *params, fs_dtype 
     if (ntiles == 0) return FS_OK;
     if (ntiles > INT32_MAX) return fsi::fail(FS_E_OVERFLOW, "fs_pack_cast: too many tiles for one launch");
     (void)hipGetLastError();
-    hipLaunchKernelGGL(pack_cast_kernel, dim3((uint32_t)ntiles), dim3(kThreads), 0, stream, segs, tiles, params,
+    const uint32_t lds = lds_cap(kCastWgsPerCu, ntiles, (int64_t)sizeof(TileLds));
+    hipLaunchKernelGGL(pack_cast_kernel, dim3((uint32_t)ntiles), dim3(kThreads), lds, stream, segs, tiles, params,
                        static_cast<char *>(out), lo, hi);
     return check_launch("fs_pack_cast");
 }

@@ -2,7 +2,8 @@
 memory) against fs_reduce_adamw_step with a caller-supplied grad_out, bit for
 bit, on two calls in a row, the second smaller; more than 32 terms, so the
 partial sums go through the library's scratch array.  Also: an aligned and a
-misaligned case, the 32-term path that needs no scratch, and the size limit."""
+misaligned case, the 32-term path that needs no scratch, the largest size the
+scratch holds, and the size limit."""
 import numpy as np
 import pytest
 import torch
@@ -50,6 +51,11 @@ def test_noalloc_matches_fused_with_grad_out_two_calls():
 def test_noalloc_misaligned_and_single_pass():
     _run_pair(30_011, 5, 7, seed=13, shift=1)    # 35 terms, misaligned buffers: the general kernels
     _run_pair(65_539, 8, 4, seed=14)             # 32 terms: one pass, no scratch needed
+
+
+def test_noalloc_at_the_scratch_capacity():
+    # the largest n the scratch array holds, 40 terms: every partial sum it can keep is written and read
+    _run_pair(fs.NOALLOC_MAX_NUMEL, 8, 5, seed=15)
 
 
 def test_noalloc_rejects_sizes_beyond_the_scratch():
