@@ -3,8 +3,8 @@ grad_acc = 4, S = 842,301,440), in the launch configuration the benchmark
 times (one fs_reduce_shard over 32 separate bf16 slices, one fs_adamw_step
 with an fp32 gradient and a bf16 copy, fs_pack with rank -1 and fs_unpack
 per group), plus the bf16 reduce dtype and the fused reduce + AdamW over the
-same slices; at these sizes the reduce and AdamW launches cap their
-resident workgroups.
+same slices, and per group the re-shard, the cast pack and the state-dict
+import; at these sizes the launches cap their resident workgroups.
 
 The oracle cannot run the whole shard here, so it computes sampled outputs
 one by one from inputs it regenerates itself (synth is counter-based: element
@@ -118,7 +118,11 @@ def test_fullsize_reduce_and_adamw(plans):
 def test_fullsize_pack_unpack_groups(plans, which):
     """Pack (all ranks), unpack and re-shard (N -> N/2) of a full-size group;
     sampled elements of the gathered buffers and of the unpacked parameters
-    against the oracle's layouts, and every pad element zero."""
+    against the oracle's layouts, and every pad element zero.  Also the
+    fp32 -> bf16 cast pack of fp32 parameters (sampled, against the oracle's
+    rounding of the regenerated values) and the state-dict import of ranks 0
+    and N-1 from their local pieces of the parameters (whole shard, equal to
+    that rank's shard of the packed buffer)."""
     groups, ps = plans
     gi = {"block0": 0, "block31": 31, "root": 32}[which]
     shapes, plan = groups[gi], ps[gi]
@@ -140,7 +144,23 @@ def test_fullsize_pack_unpack_groups(plans, which):
     rs = fs.fs_reshard_plan(plan, half).upload()
     regathered = torch.empty(half.gathered_numel, dtype=torch.bfloat16, device="cuda")
     fs.fs_reshard(rs, gathered, regathered)
+    # cast pack of fp32 parameters, all ranks
+    p32 = [synth.normal_f32(SEED, synth.STREAM_MASTER, math.prod(s), 0.02, device="cuda", start=st)
+           for s, st in zip(shapes, starts)]
+    gcast = torch.empty(plan.gathered_numel, dtype=torch.bfloat16, device="cuda")
+    fs.fs_pack_cast(plan, p32, gcast)
+    # state-dict import: each rank's local pieces of the parameters into a fresh shard
+    imported = {}
+    for r in (0, N - 1):
+        pieces = [params[i].view(-1)[pc[1]:pc[1] + pc[2]] if pc else params[i].view(-1)[:0]
+                  for i, pc in enumerate(plan.local_pieces(r))]
+        imported[r] = torch.full((plan.shard_numel,), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        plan.load_local(imported[r], r, pieces)
     torch.cuda.synchronize()
+    for r, sh in imported.items():
+        c = plan.shard_numel
+        assert torch.equal(sh.view(torch.int16), gathered.view(torch.int16)[r * c:(r + 1) * c])
+    del p32, imported
 
     L = oracle.fsdp2_layout(shapes, 2, N)
     Lh = oracle.fsdp2_layout(shapes, 2, N // 2)
@@ -154,6 +174,8 @@ def test_fullsize_pack_unpack_groups(plans, which):
         np.testing.assert_array_equal(got, expect)
         xh = Lh.index_at(np.full(e.size, i, np.int32), e)
         np.testing.assert_array_equal(bits(regathered.view(torch.int16)[torch.from_numpy(xh).cuda()]), expect)
+        x32 = synth.normal_f32_at(SEED, synth.STREAM_MASTER, torch.from_numpy(e + st), 0.02).numpy()
+        np.testing.assert_array_equal(bits(gcast.view(torch.int16)[torch.from_numpy(x).cuda()]), oracle.bf16_round(x32))
         got_u = bits(outs[i].view(-1).view(torch.int16)[torch.from_numpy(e).cuda()])
         np.testing.assert_array_equal(got_u, expect)
         assert torch.equal(outs[i].view(torch.int16), params[i].view(torch.int16))
