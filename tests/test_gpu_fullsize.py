@@ -4,7 +4,8 @@ times (one fs_reduce_shard over 32 separate bf16 slices, one fs_adamw_step
 with an fp32 gradient and a bf16 copy, fs_pack with rank -1 and fs_unpack
 per group), plus the bf16 reduce dtype and the fused reduce + AdamW over the
 same slices, and per group the re-shard, the cast pack and the state-dict
-import; at these sizes the launches cap their resident workgroups.
+import; at these sizes the reduce, AdamW, unpack, re-shard and cast pack
+launches cap their resident workgroups.
 
 The oracle cannot run the whole shard here, so it computes sampled outputs
 one by one from inputs it regenerates itself (synth is counter-based: element
