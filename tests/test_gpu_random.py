@@ -7,7 +7,8 @@ dtype, fused reduce + AdamW) runs on random sizes, N, grad_acc and
 per-slice misalignment: reduces bit-exact, fused bit-identical to the two
 kernels, AdamW within its tolerance of the oracle.  Every buffer sits in a
 canary guard band.  fp32 state at random bf16 plans' element positions (the
-plans' fp32 twins) packs, unpacks and re-shards bit for bit as well.
+plans' fp32 twins) packs, unpacks and re-shards bit for bit as well, and the
+cast pack and the state-dict import match the oracle on the same lists.
 """
 import numpy as np
 import pytest
@@ -116,6 +117,51 @@ def test_random_layout_pack_unpack_reshard(seed):
     D.check()
     src.check()
     np.testing.assert_array_equal(bits(D.t), oracle.reshard(L, L2, junk))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_cast_pack_and_import(seed):
+    """On the same random parameter lists (bf16 plans): the fp32 -> bf16 cast
+    pack of misaligned fp32 parameters, all ranks and one rank, and the
+    state-dict import of one rank from its local pieces held as separate
+    misaligned tensors, against the oracle bit for bit."""
+    shapes, _, mode, N, uo, _, _, _, shifts = _random_case(seed)
+    say("random cast pack / import", seed, mode, N, uo, len(shapes), "params")
+    plan = fs.fs_plan(shapes, "bf16", N, uo, mode).upload()
+    L = _olayout(mode, shapes, "bf16", N, uo)
+    p32, p16, off = [], [], 0
+    for s, sh in zip(shapes, shifts):
+        n = int(np.prod(s)) if len(s) else 1
+        vals = synth.normal_f32(seed, synth.STREAM_MASTER, n, 0.02, device="cuda", start=off)
+        if n >= 4:   # a NaN, an infinity, a bf16 tie and a denormal among the values
+            vals[:4] = torch.tensor([float("nan"), -float("inf"), 1.0 + 2.0 ** -8, 1e-40], device="cuda")
+        p32.append(Guarded(n, torch.float32, shift=sh, fill=vals))
+        p16.append(Guarded(n, torch.bfloat16, shift=7 - sh,
+                           fill=synth.bits16(seed, synth.STREAM_PARAMS, n, device="cuda", start=off).view(torch.bfloat16)))
+        off += n
+    ref_cast = oracle.pack_cast(L, [p.t.cpu().numpy() for p in p32])
+    G = Guarded(plan.gathered_numel, torch.bfloat16, shift=shifts[-1])
+    fs.fs_pack_cast(plan, [p.t for p in p32], G.t)
+    r = int(seed % N)
+    c = plan.shard_numel
+    S = Guarded(c, torch.bfloat16, shift=shifts[-2])
+    fs.fs_pack_cast(plan, [p.t for p in p32], S.t, rank=r)
+    # import rank r's pieces of the bf16 parameters, each a separate misaligned tensor
+    host16 = [bits(p.t) for p in p16]
+    ref = oracle.pack(L, host16, rank=r)
+    pieces = []
+    for k, (pc, h) in enumerate(zip(plan.local_pieces(r), host16)):
+        lo, cnt = (pc[1], pc[2]) if pc else (0, 0)
+        pieces.append(Guarded(cnt, torch.bfloat16, shift=shifts[k % len(shifts)],
+                              fill=from_bits(h[lo:lo + cnt], torch.bfloat16) if cnt else None))
+    I = Guarded(c, torch.bfloat16, shift=shifts[-3], fill=torch.full((c,), -1, dtype=torch.int16).view(torch.bfloat16))
+    plan.load_local(I.t, r, [q.t for q in pieces])
+    torch.cuda.synchronize()
+    for g in [G, S, I] + p32 + p16 + pieces:
+        g.check()
+    np.testing.assert_array_equal(bits(G.t), ref_cast)
+    np.testing.assert_array_equal(bits(S.t), ref_cast[r * c:(r + 1) * c])
+    np.testing.assert_array_equal(bits(I.t), ref)
 
 
 @pytest.mark.parametrize("seed", range(8))
