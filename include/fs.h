@@ -35,8 +35,8 @@
  *     fs_last_error are infrastructure around the method's steps (reading a
  *     plan back, placing its tables in device memory, reporting errors); no
  *     passage of the pages defines them.
- *   - Long launches of the reduces, AdamW, the unpack and the re-shard
- *     reserve LDS they never use, to limit how many of their workgroups share
+ *   - Long launches of the reduces, AdamW, the unpack, the re-shard and the
+ *     cast pack reserve LDS they never use, to limit how many of their workgroups share
  *     a CU (fewer concurrent HBM streams run faster); a kernel that another
  *     stream runs at the same time finds correspondingly less LDS on those
  *     CUs.
